@@ -1,0 +1,189 @@
+"""Python binding of libditq (the fused low-bit DiT linear layer on MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of libditq.so.
+The functions named ``dit_*`` mirror the C ABI in include/ditq.h one to one and
+take raw device pointers (ints); the helpers below them take torch tensors and
+use torch only for device memory and the current stream.
+
+The library must have been built (``python bit_gemm_dit_amd/build.py``); import
+fails loudly otherwise.  There is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "FMT_FP4", "FMT_FP8", "EPI_IDENTITY", "EPI_GATED_SILU", "EPI_QK_RMSNORM", "DitError", "RmsNormParams",
+    "dit_packed_weight_bytes", "dit_act_code_bytes", "dit_act_scale_bytes", "dit_pack_weights",
+    "dit_quantize_act", "dit_gemm_q4_epilogue", "dit_gemm_q8_epilogue", "dit_status_str", "dit_last_error",
+    "pack_weights", "quantize_act", "gemm", "linear", "library_path", "EXPORTED",
+]
+
+FMT_FP4 = 1
+FMT_FP8 = 2
+EPI_IDENTITY = 0
+EPI_GATED_SILU = 1
+EPI_QK_RMSNORM = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libditq.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(
+        f"{library_path} is missing: build it with `python bit_gemm_dit_amd/build.py` "
+        "(there is no CPU fallback)")
+
+# torch ships its own HIP runtime (soname libamdhip64.so.7, loaded by file name).
+# Loading torch first makes the dynamic linker bind libditq.so to that same copy;
+# loading libditq.so first would map a second runtime from /opt/rocm, and two
+# runtimes in one process do not share the device.
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(library_path)
+
+
+class RmsNormParams(ctypes.Structure):
+    """dit_rmsnorm_params: head_dim, n_heads, gamma_q / gamma_k (device pointers), eps."""
+    _fields_ = [("head_dim", ctypes.c_int), ("n_heads", ctypes.c_int), ("gamma_q", ctypes.c_void_p),
+                ("gamma_k", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
+_i, _p, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+_SIGS = {
+    "dit_packed_weight_bytes": (_sz, [_i, _i, _i, _i]),
+    "dit_act_code_bytes": (_sz, [_i, _i, _i]),
+    "dit_act_scale_bytes": (_sz, [_i, _i, _i]),
+    "dit_pack_weights": (_i, [_i, _i, _p, _i, _i, _i, _p, _p]),
+    "dit_quantize_act": (_i, [_i, _p, _i, _i, _i, _p, _p, _p]),
+    "dit_gemm_q4_epilogue": (_i, [_p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams), _p, _i, _p]),
+    "dit_gemm_q8_epilogue": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _i, _p]),
+    "dit_status_str": (ctypes.c_char_p, [_i]),
+    "dit_last_error": (ctypes.c_char_p, []),
+}
+EXPORTED = tuple(_SIGS)
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class DitError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = dit_last_error() if status == 4 else ""
+        super().__init__(f"{where}: {dit_status_str(status)} (status {status})" + (f" [{detail}]" if detail else ""))
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise DitError(status, where)
+
+
+# ---------------------------------------------------------------- C ABI mirrors
+def dit_status_str(status: int) -> str:
+    return _lib.dit_status_str(status).decode()
+
+
+def dit_last_error() -> str:
+    return _lib.dit_last_error().decode()
+
+
+def dit_packed_weight_bytes(fmt: int, epi: int, N: int, K: int) -> int:
+    return _lib.dit_packed_weight_bytes(fmt, epi, N, K)
+
+
+def dit_act_code_bytes(fmt: int, M: int, K: int) -> int:
+    return _lib.dit_act_code_bytes(fmt, M, K)
+
+
+def dit_act_scale_bytes(fmt: int, M: int, K: int) -> int:
+    return _lib.dit_act_scale_bytes(fmt, M, K)
+
+
+def dit_pack_weights(fmt, epi, w_ptr, N, K, ldw, packed_ptr, stream=None) -> None:
+    _check(_lib.dit_pack_weights(fmt, epi, w_ptr, N, K, ldw, packed_ptr, stream), "dit_pack_weights")
+
+
+def dit_quantize_act(fmt, x_ptr, M, K, ldx, codes_ptr, scales_ptr, stream=None) -> None:
+    _check(_lib.dit_quantize_act(fmt, x_ptr, M, K, ldx, codes_ptr, scales_ptr, stream), "dit_quantize_act")
+
+
+def dit_gemm_q4_epilogue(a_codes, a_scales, w_packed, M, N, K, epi, rms, out, ldo, stream=None) -> None:
+    rp = ctypes.byref(rms) if rms is not None else None
+    _check(_lib.dit_gemm_q4_epilogue(a_codes, a_scales, w_packed, M, N, K, epi, rp, out, ldo, stream),
+           "dit_gemm_q4_epilogue")
+
+
+def dit_gemm_q8_epilogue(a_codes, a_scales, w_packed, M, N, K, epi, out, ldo, stream=None) -> None:
+    _check(_lib.dit_gemm_q8_epilogue(a_codes, a_scales, w_packed, M, N, K, epi, out, ldo, stream),
+           "dit_gemm_q8_epilogue")
+
+
+# ---------------------------------------------------------------- torch helpers
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ld(t) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit stride along the last dimension")
+    return t.stride(0)
+
+
+def pack_weights(w, fmt: int, epi: int):
+    """bf16 weights [N, K] (torch Linear layout) -> packed blob (uint8 device tensor)."""
+    import torch
+    N, K = w.shape
+    nbytes = dit_packed_weight_bytes(fmt, epi, N, K)
+    if nbytes == 0:
+        raise DitError(2, "dit_packed_weight_bytes")
+    blob = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    dit_pack_weights(fmt, epi, w.data_ptr(), N, K, _ld(w), blob.data_ptr(), _stream())
+    return blob
+
+
+def quantize_act(x, fmt: int):
+    """bf16 activations [M, K] -> (codes, scales) device tensors."""
+    import torch
+    M, K = x.shape
+    cb, sb = dit_act_code_bytes(fmt, M, K), dit_act_scale_bytes(fmt, M, K)
+    if cb == 0:
+        raise DitError(2, "dit_act_code_bytes")
+    if fmt == FMT_FP4:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    else:
+        codes = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    assert codes.numel() * codes.element_size() == cb and scales.numel() * scales.element_size() == sb
+    dit_quantize_act(fmt, x.data_ptr(), M, K, _ld(x), codes.data_ptr(), scales.data_ptr(), _stream())
+    return codes, scales
+
+
+def gemm(codes, scales, blob, N: int, K: int, fmt: int, epi: int, rms: RmsNormParams | None = None, out=None):
+    """Fused GEMM + epilogue on quantized activations; returns the bf16 output [M, N or N/2]."""
+    import torch
+    M = codes.shape[0]
+    width = N // 2 if epi == EPI_GATED_SILU else N
+    if out is None:
+        out = torch.empty((M, width), dtype=torch.bfloat16, device=codes.device)
+    if fmt == FMT_FP4:
+        dit_gemm_q4_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi, rms,
+                             out.data_ptr(), _ld(out), _stream())
+    else:
+        dit_gemm_q8_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi,
+                             out.data_ptr(), _ld(out), _stream())
+    return out
+
+
+def linear(x, blob, N: int, fmt: int, epi: int, rms: RmsNormParams | None = None, out=None):
+    """The whole layer: quantize x on the fly, then the fused GEMM + epilogue."""
+    codes, scales = quantize_act(x, fmt)
+    return gemm(codes, scales, blob, N, x.shape[1], fmt, epi, rms=rms, out=out)
+
+
+def rmsnorm_params(gamma_q, gamma_k, n_heads: int, eps: float) -> RmsNormParams:
+    """Build the RMSNorm parameter struct from fp32 device tensors (kept alive by the caller)."""
+    return RmsNormParams(gamma_q.numel(), n_heads, gamma_q.data_ptr(), gamma_k.data_ptr(), eps)

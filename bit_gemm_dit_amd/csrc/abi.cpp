@@ -1,0 +1,181 @@
+// C ABI of the fused low-bit linear layer: argument validation and dispatch.
+//
+// Every check runs on the host before any HIP call (so the error paths can be
+// exercised without a device); the kernels themselves live in quant.hip,
+// pack.hip and gemm.hip.  The entry points and their contracts are declared and
+// documented in include/ditq.h.
+#include "ditq.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <cstdio>
+
+#include "common.hpp"
+
+namespace {
+
+using ditq::FMT_FP4;
+using ditq::FMT_FP8;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool valid_fmt(int f) { return f == DIT_FMT_FP4_E2M1_MX32 || f == DIT_FMT_FP8_E4M3_ROWCOL; }
+bool valid_epi(int e) { return e == DIT_EPI_IDENTITY || e == DIT_EPI_GATED_SILU || e == DIT_EPI_QK_RMSNORM; }
+
+// Shapes the kernels implement.  K: whole 256-element k-steps (FP4 scale groups);
+// N: whole 64-row weight groups (128 for gated-SiLU so each 64-row packed group
+// holds 32 gate/up pairs).  Byte counts stay below 2^32 so that 32-bit buffer
+// offsets cover every tensor (plus one tile of ragged rows).
+bool shape_ok(int fmt, int epi, int N, int K) {
+  if (K % 256 != 0 || N % 64 != 0) return false;
+  if (epi == DIT_EPI_GATED_SILU && N % 128 != 0) return false;
+  const size_t Np = (size_t)ditq::padded_rows(N);
+  const size_t code_bytes = fmt == FMT_FP4 ? Np * K / 2 : Np * K;
+  return code_bytes < (1ull << 31);
+}
+bool rows_ok(int fmt, int M, int K) {
+  const size_t row = fmt == FMT_FP4 ? (size_t)K / 2 : (size_t)K;
+  return ((size_t)M + 256) * row < (1ull << 31);
+}
+
+// Detail of the most recent DIT_EDEVICE on this thread (see dit_last_error).
+thread_local char g_last_error[256] = "";
+
+dit_status device_error(const char* what, hipError_t e) {
+  std::snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  return DIT_EDEVICE;
+}
+
+// DIT_OK if the current device is a gfx950, DIT_EDEVICE otherwise.  Cached per device id.
+dit_status check_device() {
+  static std::atomic<int> ok_dev{-1};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return device_error("hipGetDevice", e);
+  if (ok_dev.load(std::memory_order_relaxed) == dev) return DIT_OK;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return device_error("hipGetDeviceProperties", e);
+  const char* arch = prop.gcnArchName;
+  if (!(arch[0] == 'g' && arch[1] == 'f' && arch[2] == 'x' && arch[3] == '9' && arch[4] == '5' && arch[5] == '0')) {
+    std::snprintf(g_last_error, sizeof g_last_error, "device %d is %s, not gfx950", dev, arch);
+    return DIT_EDEVICE;
+  }
+  ok_dev.store(dev, std::memory_order_relaxed);
+  // A failed query made by other code earlier on this thread stays pending in
+  // hipGetLastError; drop it so that the check after our launch sees only ours.
+  (void)hipGetLastError();
+  return DIT_OK;
+}
+
+dit_status launched(hipError_t e) { return e == hipSuccess ? DIT_OK : device_error("kernel launch", e); }
+
+}  // namespace
+
+extern "C" {
+
+size_t dit_packed_weight_bytes(dit_fmt fmt, dit_epi epi, int N, int K) {
+  if (!valid_fmt(fmt) || !valid_epi(epi) || N <= 0 || K <= 0) return 0;
+  if (!shape_ok(fmt, epi, N, K)) return 0;
+  if (fmt == DIT_FMT_FP8_E4M3_ROWCOL && epi == DIT_EPI_QK_RMSNORM) return 0;
+  return ditq::blob_total_bytes(fmt, ditq::padded_rows(N), K);
+}
+
+size_t dit_act_code_bytes(dit_fmt fmt, int M, int K) {
+  if (!valid_fmt(fmt) || M <= 0 || K <= 0 || K % 256 != 0) return 0;
+  return fmt == DIT_FMT_FP4_E2M1_MX32 ? (size_t)M * K / 2 : (size_t)M * K;
+}
+
+size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K) {
+  if (!valid_fmt(fmt) || M <= 0 || K <= 0 || K % 256 != 0) return 0;
+  return fmt == DIT_FMT_FP4_E2M1_MX32 ? (size_t)M * K / 32 : (size_t)M * 4;
+}
+
+dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N, int K, int ldw, void* packed,
+                            void* stream) {
+  if (!valid_fmt(fmt) || !valid_epi(epi) || !w_bf16 || !packed || N <= 0 || K <= 0) return DIT_EINVAL;
+  if (!shape_ok(fmt, epi, N, K)) return DIT_EUNSUPPORTED;
+  if (fmt == DIT_FMT_FP8_E4M3_ROWCOL && epi == DIT_EPI_QK_RMSNORM) return DIT_EUNSUPPORTED;
+  if (!aligned16(w_bf16) || !aligned16(packed) || ldw < K || ldw % 8 != 0) return DIT_EALIGN;
+  if (dit_status s = check_device()) return s;
+  (void)hipGetLastError();
+  return launched(ditq::launch_pack(fmt, epi, static_cast<const uint16_t*>(w_bf16), N, K, ldw,
+                                    static_cast<uint8_t*>(packed), static_cast<hipStream_t>(stream)));
+}
+
+dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int ldx, void* codes, void* scales,
+                            void* stream) {
+  if (!valid_fmt(fmt) || !x_bf16 || !codes || !scales || M <= 0 || K <= 0) return DIT_EINVAL;
+  if (K % 256 != 0 || !rows_ok(fmt, M, K)) return DIT_EUNSUPPORTED;
+  if (!aligned16(x_bf16) || !aligned16(codes) || ldx < K || ldx % 8 != 0) return DIT_EALIGN;
+  if (fmt == DIT_FMT_FP8_E4M3_ROWCOL && !aligned(scales, 4)) return DIT_EALIGN;
+  if (dit_status s = check_device()) return s;
+  (void)hipGetLastError();
+  const auto x = static_cast<const uint16_t*>(x_bf16);
+  const auto st = static_cast<hipStream_t>(stream);
+  if (fmt == DIT_FMT_FP4_E2M1_MX32)
+    return launched(ditq::launch_quant_fp4(x, M, K, ldx, static_cast<uint8_t*>(codes),
+                                           static_cast<uint8_t*>(scales), st));
+  return launched(
+      ditq::launch_quant_fp8(x, M, K, ldx, static_cast<uint8_t*>(codes), static_cast<float*>(scales), st));
+}
+
+dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const void* w_packed, int M, int N,
+                                int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
+                                void* stream) {
+  if (!a_codes || !a_scales || !w_packed || !out_bf16 || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi))
+    return DIT_EINVAL;
+  if ((epi == DIT_EPI_QK_RMSNORM) != (rms != nullptr)) return DIT_EINVAL;
+  if (rms) {
+    if (!rms->gamma_q || !rms->gamma_k || rms->n_heads <= 0 || !(rms->eps > 0.0f)) return DIT_EINVAL;
+    if ((long long)N != 3LL * rms->n_heads * rms->head_dim) return DIT_EINVAL;
+    if (rms->head_dim != 128 && rms->head_dim != 256) return DIT_EUNSUPPORTED;
+  }
+  if (!shape_ok(FMT_FP4, epi, N, K) || !rows_ok(FMT_FP4, M, K)) return DIT_EUNSUPPORTED;
+  const int width = epi == DIT_EPI_GATED_SILU ? N / 2 : N;
+  if (!aligned16(a_codes) || !aligned(a_scales, 8) || !aligned16(w_packed) || !aligned16(out_bf16) ||
+      ldo < width || ldo % 8 != 0)
+    return DIT_EALIGN;
+  if (rms && (!aligned16(rms->gamma_q) || !aligned16(rms->gamma_k))) return DIT_EALIGN;
+  if (dit_status s = check_device()) return s;
+  (void)hipGetLastError();
+  ditq::RmsArgs r{};
+  if (rms) r = ditq::RmsArgs{rms->head_dim, rms->n_heads, rms->gamma_q, rms->gamma_k, rms->eps};
+  return launched(ditq::launch_gemm_fp4(static_cast<const uint8_t*>(a_codes), static_cast<const uint8_t*>(a_scales),
+                                        static_cast<const uint8_t*>(w_packed), M, N, K, epi, rms ? &r : nullptr,
+                                        static_cast<uint16_t*>(out_bf16), ldo, static_cast<hipStream_t>(stream)));
+}
+
+dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, const void* w_packed, int M, int N,
+                                int K, dit_epi epi, void* out_bf16, int ldo, void* stream) {
+  if (!a_codes || !a_scales || !w_packed || !out_bf16 || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi))
+    return DIT_EINVAL;
+  if (epi == DIT_EPI_QK_RMSNORM) return DIT_EUNSUPPORTED;
+  if (!shape_ok(FMT_FP8, epi, N, K) || !rows_ok(FMT_FP8, M, K)) return DIT_EUNSUPPORTED;
+  const int width = epi == DIT_EPI_GATED_SILU ? N / 2 : N;
+  if (!aligned16(a_codes) || !aligned(a_scales, 4) || !aligned16(w_packed) || !aligned16(out_bf16) ||
+      ldo < width || ldo % 8 != 0)
+    return DIT_EALIGN;
+  if (dit_status s = check_device()) return s;
+  (void)hipGetLastError();
+  return launched(ditq::launch_gemm_fp8(static_cast<const uint8_t*>(a_codes), a_scales,
+                                        static_cast<const uint8_t*>(w_packed), M, N, K, epi,
+                                        static_cast<uint16_t*>(out_bf16), ldo, static_cast<hipStream_t>(stream)));
+}
+
+const char* dit_last_error(void) { return g_last_error; }
+
+const char* dit_status_str(dit_status status) {
+  switch (status) {
+    case DIT_OK: return "ok";
+    case DIT_EINVAL: return "invalid argument";
+    case DIT_EUNSUPPORTED: return "unsupported shape or combination";
+    case DIT_EALIGN: return "misaligned pointer or leading dimension";
+    case DIT_EDEVICE: return "no usable gfx950 device or launch failure";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+// Shared device/host definitions of the fused low-bit linear layer (gfx950).
+//
+// Blob layout constants, vector types and the FP4 / FP8 element encoders used by
+// both the activation quantizer and the weight packer.  The encoders follow the
+// quantization rule documented in include/ditq.h (per 32-element block: E8M0
+// scale = 2^(floor(log2 amax) - 2); element = RNE_E2M1(x / scale); FP8: RNE_E4M3
+// of x / s with s = amax / 448), the formats of page "How fal made Ideogram V4 6x
+// faster" (paragraph 2, a 4-bit float format) and page "WaveSpeedAI X DataCrunch"
+// (engine list, FP8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ditq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+enum { FMT_FP4 = 1, FMT_FP8 = 2 };
+enum { EPI_IDENTITY = 0, EPI_GATED_SILU = 1, EPI_QK_RMSNORM = 2 };
+
+// ---------------------------------------------------------------- blob layout
+constexpr uint32_t kBlobMagic = 0x51544944u;   // "DITQ"
+constexpr uint32_t kBlobVersion = 1;
+constexpr int kHeaderBytes = 256;
+constexpr int kRowPad = 256;                   // packed rows are padded to a multiple of this
+
+__host__ __device__ inline int padded_rows(int N) { return (N + kRowPad - 1) / kRowPad * kRowPad; }
+__host__ __device__ inline size_t blob_code_bytes(int fmt, int Np, int K) {
+  return fmt == FMT_FP4 ? (size_t)Np * K / 2 : (size_t)Np * K;
+}
+__host__ __device__ inline size_t blob_scale_bytes(int fmt, int Np, int K) {
+  return fmt == FMT_FP4 ? (size_t)Np * K / 32 : (size_t)Np * 4;
+}
+__host__ __device__ inline size_t blob_scales_offset(int fmt, int Np, int K) {
+  return kHeaderBytes + blob_code_bytes(fmt, Np, K);
+}
+__host__ __device__ inline size_t blob_total_bytes(int fmt, int Np, int K) {
+  return blob_scales_offset(fmt, Np, K) + blob_scale_bytes(fmt, Np, K);
+}
+// Logical weight row stored at packed row p, or -1 for padding.  For gated-SiLU
+// each 64-row group holds 32 gate rows followed by their 32 up rows.
+__host__ __device__ inline int packed_row_source(int epi, int N, int p) {
+  if (p >= N) return -1;
+  if (epi != EPI_GATED_SILU) return p;
+  const int P = p >> 6, i = p & 63;
+  return i < 32 ? 32 * P + i : N / 2 + 32 * P + (i - 32);
+}
+
+// ---------------------------------------------------------------- FP4 encoding
+// E8M0 scale byte from the largest bf16 magnitude of a block (bit pattern with
+// the sign cleared).  Magnitude order equals integer order for finite bf16, and
+// floor(log2 amax) - 2 + 127 clamped at 0 reduces to max(exponent field - 2, 0):
+// subnormal maxima have exponent field 0 and clamp to 0 as well.
+__device__ inline uint32_t fp4_scale_byte(uint32_t amax_bits) {
+  const uint32_t ex = amax_bits >> 7;
+  return ex > 2 ? ex - 2 : 0;
+}
+
+// Double a bf16 magnitude/sign pattern exactly (only used on blocks whose maximum
+// has an exponent field <= 2, so no overflow): subnormals shift left, which also
+// carries correctly into the smallest normal binade; normals add one to the exponent.
+__device__ inline uint32_t bf16_double_bits(uint32_t b) {
+  const uint32_t s = b & 0x8000u, m = b & 0x7FFFu;
+  return s | ((m >> 7) == 0 ? (m << 1) : (m + 0x80u));
+}
+__device__ inline uint32_t bf16x2_double(uint32_t w) {
+  return bf16_double_bits(w & 0xFFFFu) | (bf16_double_bits(w >> 16) << 16);
+}
+
+// 8 bf16 values (one uint4) -> 8 E2M1 codes (one dword, element 2j in the low
+// nibble of byte j) for scale byte `byte`.  The hardware conversion computes
+// RNE_E2M1(x / scale) with saturation at 6 and the sign kept; it takes the scale
+// as an fp32 power of two.  Byte 0 would need the subnormal float 2^-127, so
+// there the values are doubled exactly and divided by 2^-126 instead.
+__device__ inline uint32_t fp4_encode8(v4i v, uint32_t byte) {
+  uint32_t w0 = (uint32_t)v.x, w1 = (uint32_t)v.y, w2 = (uint32_t)v.z, w3 = (uint32_t)v.w;
+  uint32_t sbits = byte << 23;
+  if (byte == 0) {
+    w0 = bf16x2_double(w0); w1 = bf16x2_double(w1); w2 = bf16x2_double(w2); w3 = bf16x2_double(w3);
+    sbits = 1u << 23;
+  }
+  const float scale = __uint_as_float(sbits);
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w0), scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w1), scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w2), scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w3), scale, 3);
+  return r;
+}
+
+__device__ inline uint32_t bf16x2_absmax(uint32_t w) {
+  const uint32_t a = w & 0x7FFFu, b = (w >> 16) & 0x7FFFu;
+  return a > b ? a : b;
+}
+__device__ inline uint32_t absmax8(v4i v) {
+  uint32_t m = bf16x2_absmax((uint32_t)v.x);
+  m = max(m, bf16x2_absmax((uint32_t)v.y));
+  m = max(m, bf16x2_absmax((uint32_t)v.z));
+  m = max(m, bf16x2_absmax((uint32_t)v.w));
+  return m;
+}
+
+// ---------------------------------------------------------------- FP8 encoding
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Row scale s = fl32(amax / 448) (IEEE division), 1 for an all-zero row.
+__device__ inline float fp8_row_scale(uint32_t amax_bits) {
+  const float amax = __uint_as_float(amax_bits << 16);
+  return amax_bits == 0 ? 1.0f : amax / 448.0f;
+}
+
+// Four bf16 values -> four E4M3 codes (byte i = element i): q = RNE_E4M3(fl32(x / s)).
+// |x / s| <= 448 * (1 + 2^-23) by construction; the clamp keeps values in the
+// hardware conversion's saturating range without changing any rounding.
+__device__ inline uint32_t fp8_encode4(uint32_t w0, uint32_t w1, float s) {
+  float a = bf16_lo(w0) / s, b = bf16_hi(w0) / s, c = bf16_lo(w1) / s, d = bf16_hi(w1) / s;
+  a = fmaxf(fminf(a, 448.0f), -448.0f);
+  b = fmaxf(fminf(b, 448.0f), -448.0f);
+  c = fmaxf(fminf(c, 448.0f), -448.0f);
+  d = fmaxf(fminf(d, 448.0f), -448.0f);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+// ---------------------------------------------------------------- buffer resources
+// Raw buffer descriptors: loads past num_records bytes return zeros, which
+// clips ragged tiles without branches.
+constexpr int kBufferFlags = 0x00020000;
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+
+// ---------------------------------------------------------------- launchers (host)
+struct RmsArgs {
+  int head_dim;
+  int n_heads;
+  const float* gamma_q;
+  const float* gamma_k;
+  float eps;
+};
+
+hipError_t launch_quant_fp4(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream);
+hipError_t launch_quant_fp8(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, float* scales,
+                            hipStream_t stream);
+hipError_t launch_pack(int fmt, int epi, const uint16_t* w, int N, int K, int ldw, uint8_t* blob,
+                       hipStream_t stream);
+hipError_t launch_gemm_fp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* blob, int M,
+                           int N, int K, int epi, const RmsArgs* rms, uint16_t* out, int ldo,
+                           hipStream_t stream);
+hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scales, const uint8_t* blob, int M,
+                           int N, int K, int epi, uint16_t* out, int ldo, hipStream_t stream);
+
+}  // namespace ditq

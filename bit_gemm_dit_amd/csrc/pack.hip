@@ -1,0 +1,128 @@
+// Weight packer (gfx950): bf16 W [N, K] -> packed blob (layout in include/ditq.h).
+//
+// The codes are pre-shuffled into the MFMA operand layout: one 1 KB (FP4) or 2 KB
+// (FP8) fragment holds, lane by lane, exactly the registers of one 32x32x64 MFMA
+// operand, so the GEMM copies tiles to LDS and reads fragments with contiguous,
+// conflict-free 16-byte accesses.  For gated-SiLU the rows are permuted so that
+// gate row j and up row j + N/2 sit in the same lane of adjacent 32-row groups:
+// "the columns of B are permuted at packing time so that each pair sits together"
+// (page "How fal made Ideogram V4 6x faster", paragraph 4).  Runs once per weight.
+#include "common.hpp"
+
+namespace ditq {
+namespace {
+
+__device__ void write_header(uint8_t* blob, int fmt, int epi, int N, int K, int Np) {
+  uint32_t* h = reinterpret_cast<uint32_t*>(blob);
+  for (int i = 0; i < kHeaderBytes / 4; ++i) h[i] = 0;
+  h[0] = kBlobMagic;
+  h[1] = kBlobVersion;
+  h[2] = (uint32_t)fmt;
+  h[3] = (uint32_t)epi;
+  h[4] = (uint32_t)N;
+  h[5] = (uint32_t)K;
+  h[6] = (uint32_t)Np;
+  uint64_t* h64 = reinterpret_cast<uint64_t*>(blob + 32);
+  h64[0] = kHeaderBytes;
+  h64[1] = blob_scales_offset(fmt, Np, K);
+  h64[2] = blob_total_bytes(fmt, Np, K);
+}
+
+// FP4: one thread per (fragment, lane): that lane's 32 K elements are exactly one
+// E8M0 block of one weight row, so the thread computes the block scale and the 16
+// code bytes on its own.
+__global__ __launch_bounds__(256) void pack_fp4_kernel(const uint16_t* __restrict__ w, int N, int K,
+                                                       int ldw, int epi, int Np,
+                                                       uint8_t* __restrict__ blob) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t kc = (uint32_t)K / 64;
+  const uint32_t total = (uint32_t)Np / 32 * kc * 64;
+  if (t == 0) write_header(blob, FMT_FP4, epi, N, K, Np);
+  if (t >= total) return;
+  const uint32_t L = t & 63, frag = t >> 6;
+  const uint32_t c = frag % kc, g = frag / kc;
+  const int p = (int)(32 * g + (L & 31));
+  const int src = packed_row_source(epi, N, p);
+  v4i out = {0, 0, 0, 0};
+  uint32_t byte = 0;
+  if (src >= 0) {
+    const v4i* wp = reinterpret_cast<const v4i*>(w + (size_t)src * ldw + 64 * c + 32 * (L >> 5));
+    const v4i v0 = wp[0], v1 = wp[1], v2 = wp[2], v3 = wp[3];
+    const uint32_t m = max(max(absmax8(v0), absmax8(v1)), max(absmax8(v2), absmax8(v3)));
+    byte = fp4_scale_byte(m);
+    out.x = (int)fp4_encode8(v0, byte);
+    out.y = (int)fp4_encode8(v1, byte);
+    out.z = (int)fp4_encode8(v2, byte);
+    out.w = (int)fp4_encode8(v3, byte);
+  }
+  *reinterpret_cast<v4i*>(blob + kHeaderBytes + (size_t)frag * 1024 + 16 * L) = out;
+  // scale group (g, s = c / 4), byte 4L + j with j = c % 4: block 8s + 2j + L/32 == 2c + L/32
+  uint8_t* sc = blob + blob_scales_offset(FMT_FP4, Np, K);
+  sc[((size_t)g * (K / 256) + c / 4) * 256 + 4 * L + (c & 3)] = (uint8_t)byte;
+}
+
+// FP8: one wave per packed row.  Pass 1 finds the row's amax (-> s_w), pass 2
+// encodes 32-element pieces; piece q of the row lands in fragment (g, q/2), lane
+// p%32 + 32*(q%2).
+__global__ __launch_bounds__(256) void pack_fp8_kernel(const uint16_t* __restrict__ w, int N, int K,
+                                                       int ldw, int epi, int Np,
+                                                       uint8_t* __restrict__ blob) {
+  const int lane = threadIdx.x & 63;
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blockIdx.x == 0 && threadIdx.x == 0) write_header(blob, FMT_FP8, epi, N, K, Np);
+  if (p >= Np) return;
+  const int src = packed_row_source(epi, N, p);
+  float* sw = reinterpret_cast<float*>(blob + blob_scales_offset(FMT_FP8, Np, K));
+  const int g = p / 32, kc = K / 64;
+  const int lane_in_frag = p & 31;
+  if (src < 0) {
+    for (int q = lane; q < K / 32; q += 64) {
+      uint8_t* d = blob + kHeaderBytes + ((size_t)g * kc + q / 2) * 2048 + 32 * (lane_in_frag + 32 * (q & 1));
+      *reinterpret_cast<v4i*>(d) = v4i{0, 0, 0, 0};
+      *reinterpret_cast<v4i*>(d + 16) = v4i{0, 0, 0, 0};
+    }
+    if (lane == 0) sw[p] = 0.0f;
+    return;
+  }
+  const uint16_t* wr = w + (size_t)src * ldw;
+  uint32_t m = 0;
+  for (int k = lane * 8; k < K; k += 512) m = max(m, absmax8(*reinterpret_cast<const v4i*>(wr + k)));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  const float s = fp8_row_scale(m);
+  if (lane == 0) sw[p] = s;
+  for (int q = lane; q < K / 32; q += 64) {
+    const v4i* wp = reinterpret_cast<const v4i*>(wr + 32 * q);
+    v4i lo, hi;
+    const v4i a = wp[0], b = wp[1], c = wp[2], d = wp[3];
+    lo.x = (int)fp8_encode4((uint32_t)a.x, (uint32_t)a.y, s);
+    lo.y = (int)fp8_encode4((uint32_t)a.z, (uint32_t)a.w, s);
+    lo.z = (int)fp8_encode4((uint32_t)b.x, (uint32_t)b.y, s);
+    lo.w = (int)fp8_encode4((uint32_t)b.z, (uint32_t)b.w, s);
+    hi.x = (int)fp8_encode4((uint32_t)c.x, (uint32_t)c.y, s);
+    hi.y = (int)fp8_encode4((uint32_t)c.z, (uint32_t)c.w, s);
+    hi.z = (int)fp8_encode4((uint32_t)d.x, (uint32_t)d.y, s);
+    hi.w = (int)fp8_encode4((uint32_t)d.z, (uint32_t)d.w, s);
+    uint8_t* dst = blob + kHeaderBytes + ((size_t)g * kc + q / 2) * 2048 + 32 * (lane_in_frag + 32 * (q & 1));
+    *reinterpret_cast<v4i*>(dst) = lo;
+    *reinterpret_cast<v4i*>(dst + 16) = hi;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack(int fmt, int epi, const uint16_t* w, int N, int K, int ldw, uint8_t* blob,
+                       hipStream_t stream) {
+  const int Np = padded_rows(N);
+  if (fmt == FMT_FP4) {
+    const uint32_t total = (uint32_t)Np / 32 * ((uint32_t)K / 64) * 64;
+    hipLaunchKernelGGL(pack_fp4_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, w, N, K, ldw, epi,
+                       Np, blob);
+  } else {
+    hipLaunchKernelGGL(pack_fp8_kernel, dim3((Np + 3) / 4), dim3(256), 0, stream, w, N, K, ldw, epi, Np,
+                       blob);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ditq

@@ -1,0 +1,130 @@
+// On-the-fly activation quantizers (gfx950).
+//
+// FP4: bf16 [M, K] -> E2M1 codes [M][K/2] + E8M0 scales [M][K/32].  Activation
+// statistics change from one diffusion iteration to the next, so the scales are
+// computed from the data on every call rather than calibrated once (page
+// "Versnellende diffusiemodellen met TheStage AI", section on acceleration and
+// compression); the 4-bit float format is that of page "How fal made Ideogram V4
+// 6x faster", paragraph 2.
+// FP8: bf16 [M, K] -> E4M3 codes [M][K] + fp32 row scales [M] (page "WaveSpeedAI
+// X DataCrunch", engine list: FP8 mixed precision).
+//
+// Both kernels are HBM-bound streams: 2 bytes read per element, 0.5 + 1/32 (FP4)
+// or 1 (FP8) byte written.  Every wave instruction touches contiguous memory.
+#include "common.hpp"
+
+namespace ditq {
+namespace {
+
+// DPP quad permutations: xor 1 = [1,0,3,2], xor 2 = [2,3,0,1].
+constexpr int kQuadXor1 = 0xB1;
+constexpr int kQuadXor2 = 0x4E;
+
+// One thread per 8 consecutive elements (16 bytes of bf16); the four threads of a
+// DPP quad cover one 32-element block and agree on its scale.  Grid-stride over
+// all chunks; the chunk count and the stride are multiples of 4, so quads are
+// always fully active together.
+__global__ __launch_bounds__(256) void quant_fp4_kernel(const uint16_t* __restrict__ x, int ldx,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales, uint32_t total,
+                                                        uint32_t per_row) {
+  const uint32_t stride = gridDim.x * 256u;
+  for (uint32_t c = blockIdx.x * 256u + threadIdx.x; c < total; c += stride) {
+    const uint32_t row = c / per_row, col = c - row * per_row;
+    const v4i v = *reinterpret_cast<const v4i*>(x + (size_t)row * ldx + (size_t)col * 8);
+    uint32_t m = absmax8(v);
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kQuadXor1, 0xF, 0xF, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kQuadXor2, 0xF, 0xF, false));
+    const uint32_t byte = fp4_scale_byte(m);
+    reinterpret_cast<uint32_t*>(codes)[c] = fp4_encode8(v, byte);   // codes are dense: chunk c -> bytes 4c..4c+3
+    if ((threadIdx.x & 3) == 0) scales[c >> 2] = (uint8_t)byte;
+  }
+}
+
+// One wave per row.  Rows up to kMaxCached*512 elements stay in registers between
+// the amax pass and the encode pass; longer rows are read twice.
+constexpr int kMaxCached = 16;
+
+template <bool CACHED>
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                        int ldx, uint8_t* __restrict__ codes,
+                                                        float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;                                   // uniform per wave
+  const uint16_t* xr = x + (size_t)row * ldx;
+  uint8_t* cr = codes + (size_t)row * K;
+  const int nch = (K + 511) / 512;
+  uint32_t m = 0;
+  v4i cache[CACHED ? kMaxCached : 1];
+  if (CACHED) {
+#pragma unroll
+    for (int i = 0; i < kMaxCached; ++i) {
+      const int k = i * 512 + lane * 8;
+      if (i < nch && k < K) {
+        cache[i] = *reinterpret_cast<const v4i*>(xr + k);
+        m = max(m, absmax8(cache[i]));
+      }
+    }
+  } else {
+    for (int i = 0; i < nch; ++i) {
+      const int k = i * 512 + lane * 8;
+      if (k < K) m = max(m, absmax8(*reinterpret_cast<const v4i*>(xr + k)));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  const float s = fp8_row_scale(m);
+  if (lane == 0) scales[row] = s;
+  if (CACHED) {
+#pragma unroll
+    for (int i = 0; i < kMaxCached; ++i) {
+      const int k = i * 512 + lane * 8;
+      if (i < nch && k < K) {
+        const v4i v = cache[i];
+        uint2 q;
+        q.x = fp8_encode4((uint32_t)v.x, (uint32_t)v.y, s);
+        q.y = fp8_encode4((uint32_t)v.z, (uint32_t)v.w, s);
+        *reinterpret_cast<uint2*>(cr + k) = q;
+      }
+    }
+  } else {
+    for (int i = 0; i < nch; ++i) {
+      const int k = i * 512 + lane * 8;
+      if (k < K) {
+        const v4i v = *reinterpret_cast<const v4i*>(xr + k);
+        uint2 q;
+        q.x = fp8_encode4((uint32_t)v.x, (uint32_t)v.y, s);
+        q.y = fp8_encode4((uint32_t)v.z, (uint32_t)v.w, s);
+        *reinterpret_cast<uint2*>(cr + k) = q;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_fp4(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream) {
+  const uint32_t per_row = (uint32_t)K / 8;
+  const uint32_t total = (uint32_t)M * per_row;
+  // enough threads for one chunk each up to ~8 resident waves per SIMD; grid-stride beyond
+  uint32_t blocks = (total + 255) / 256;
+  const uint32_t cap = 256u * 32u;                        // 256 CUs x 32 blocks of 4 waves
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(quant_fp4_kernel, dim3(blocks), dim3(256), 0, stream, x, ldx, codes, scales, total,
+                     per_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, float* scales,
+                            hipStream_t stream) {
+  const dim3 grid((M + 3) / 4);
+  if (K <= kMaxCached * 512)
+    hipLaunchKernelGGL(quant_fp8_kernel<true>, grid, dim3(256), 0, stream, x, M, K, ldx, codes, scales);
+  else
+    hipLaunchKernelGGL(quant_fp8_kernel<false>, grid, dim3(256), 0, stream, x, M, K, ldx, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace ditq

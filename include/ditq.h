@@ -1,0 +1,190 @@
+/*
+ * ditq.h -- C ABI of the fused low-bit linear layer for diffusion transformers
+ * on AMD MI355X (gfx950).
+ *
+ * The layer: bf16 activations are quantized on the fly to a 4-bit float (FP4
+ * E2M1, one E8M0 scale per 32 consecutive K elements) or to FP8 E4M3 (one fp32
+ * scale per row); they are multiplied with pre-packed low-bit weights on the
+ * scaled MFMA units; the small op that follows the GEMM (identity, gated-SiLU,
+ * per-head QK-RMSNorm) is applied to the fp32 accumulator before the single bf16
+ * store.  Sources: page "How fal made Ideogram V4 6x faster" (news.ditty.ir),
+ * paragraph 2 (4-bit float matmuls), paragraph 3 (epilogue fusion, per-head
+ * RMSNorm, the head_dim 256 revisit schedule), paragraph 4 (gated-SiLU and the
+ * packing-time column interleave of B); page "WaveSpeedAI X DataCrunch: FLUX
+ * real-time image inference on B200", engine list (BF16/FP8 mixed precision).
+ *
+ * General rules for every entry point
+ * -----------------------------------
+ * - Tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *   allocates, frees or synchronises; each call only enqueues kernels on
+ *   `stream` (a hipStream_t passed as void*, NULL = the default stream) and
+ *   returns.  Asynchronous faults surface at the caller's next synchronisation.
+ * - All argument checks run on the host before any HIP call, in this order:
+ *     DIT_EINVAL       null pointer, M/N/K <= 0, unknown fmt/epi, missing or
+ *                      inconsistent RMSNorm parameters
+ *     DIT_EUNSUPPORTED a shape or combination the kernels do not implement
+ *     DIT_EALIGN       a pointer not 16-byte aligned, or a leading dimension
+ *                      smaller than the row width or not a multiple of 8 elements
+ *     DIT_EDEVICE      no usable gfx950 device, or a launch error
+ * - Outputs must not alias inputs.  Results are bitwise deterministic (no atomics,
+ *   no split-K).  Calls on different streams may run concurrently.
+ * - Matrices are row-major.  bf16 tensors are given as raw 16-bit patterns.
+ */
+#ifndef DITQ_H
+#define DITQ_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DIT_OK = 0,
+  DIT_EINVAL = 1,
+  DIT_EUNSUPPORTED = 2,
+  DIT_EALIGN = 3,
+  DIT_EDEVICE = 4
+} dit_status;
+
+typedef enum {
+  DIT_FMT_FP4_E2M1_MX32 = 1,   /* E2M1 codes + one E8M0 scale per 32 K elements */
+  DIT_FMT_FP8_E4M3_ROWCOL = 2  /* OCP E4M3 codes + fp32 per-row / per-column scales */
+} dit_fmt;
+
+typedef enum {
+  DIT_EPI_IDENTITY = 0,        /* out = bf16(C) */
+  DIT_EPI_GATED_SILU = 1,      /* out[:, j] = bf16(SiLU(C[:, j]) * C[:, j + N/2]), j < N/2 */
+  DIT_EPI_QK_RMSNORM = 2       /* per-head RMSNorm on the Q and K heads of C = [Q | K | V] */
+} dit_epi;
+
+/* Parameters of DIT_EPI_QK_RMSNORM (page "How fal made Ideogram V4 6x faster",
+ * paragraph 3).  The GEMM output C has N = 3 * n_heads * head_dim columns laid
+ * out [Q | K | V], each part head-major.  For every token row and every Q head h
+ * (columns h*D .. h*D+D-1) and K head h (columns H*D + h*D ..):
+ *     y[d] = x[d] / sqrt(mean_d(x^2) + eps) * gamma[d]
+ * with gamma_q for the Q heads and gamma_k for the K heads (fp32 device
+ * arrays of head_dim elements, shared by all heads).  V columns pass through.
+ * head_dim 256 uses the two-half revisit schedule: the first 128 columns of a
+ * head stay in registers with their partial sum of squares until the second
+ * half's sum arrives, then both halves are normalised and stored. */
+typedef struct {
+  int head_dim;          /* 128 or 256 */
+  int n_heads;           /* H, per Q / K / V */
+  const float* gamma_q;  /* device, [head_dim] */
+  const float* gamma_k;  /* device, [head_dim] */
+  float eps;             /* > 0, e.g. 1e-6 */
+} dit_rmsnorm_params;
+
+/* ---------------------------------------------------------------- size queries
+ * Pure arithmetic, no device access; 0 means "unsupported arguments". */
+
+/* Bytes of the packed weight blob written by dit_pack_weights.  Rows are padded
+ * to Np = ceil(N / 256) * 256.  FP4: 256 + Np*K/2 + Np*K/32.  FP8: 256 + Np*K + 4*Np. */
+size_t dit_packed_weight_bytes(dit_fmt fmt, dit_epi epi, int N, int K);
+
+/* Bytes of the activation codes / scales written by dit_quantize_act.
+ * FP4: codes M*K/2, scales M*K/32.  FP8: codes M*K, scales 4*M. */
+size_t dit_act_code_bytes(dit_fmt fmt, int M, int K);
+size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
+
+/* ---------------------------------------------------------------- weight packer
+ * Quantizes W (bf16 [N, K], row stride ldw elements; torch Linear layout, so
+ * row n is output column n) and writes the packed blob (`packed`, at least
+ * dit_packed_weight_bytes bytes, 256-byte aligned recommended).  Run once per
+ * weight, offline.  `epi` selects the row order: DIT_EPI_GATED_SILU interleaves
+ * the gate rows (0 .. N/2-1) with the up rows (N/2 .. N-1); the GEMM must then be
+ * called with DIT_EPI_GATED_SILU too.  Blobs packed for IDENTITY and QK_RMSNORM
+ * are identical and interchangeable.
+ *
+ * Quantization rule, per weight row: FP4 -- the same rule as dit_quantize_act
+ * along K; FP8 -- s_w[n] = fl32(amax_n / 448) (1 if the row is zero), codes
+ * RNE_E4M3(fl32(w / s_w[n])).
+ *
+ * Blob layout (little-endian; the GEMM relies on it, tests decode it):
+ *   header, 256 bytes: u32 magic 0x51544944 ("DITQ"), u32 layout version 1,
+ *     u32 fmt, u32 epi, u32 N, u32 K, u32 Np, u32 0, u64 codes offset (256),
+ *     u64 scales offset, u64 total bytes, then zeros.
+ *   packed row p (0 <= p < Np) holds logical weight row perm(p): identity for
+ *     IDENTITY / QK_RMSNORM; for GATED_SILU, with P = p / 64 and i = p % 64,
+ *     perm(p) = 32P + i if i < 32 (gate) else N/2 + 32P + i - 32 (up), so a gate
+ *     row and its up row land in the same lane of two adjacent 32-row groups of
+ *     the MFMA output.  Rows p >= N are zero.
+ *   FP4 codes: 1024-byte fragments (the B-operand registers of one
+ *     32x32x64 MFMA); fragment (g, c), g < Np/32, c < K/64, at
+ *     256 + (g*K/64 + c)*1024; its byte 16*L + b (lane L < 64, b < 16) holds
+ *     the codes of packed row 32g + L%32 at k = 64c + 32*(L/32) + 2b (low
+ *     nibble) and k + 1 (high nibble).
+ *   FP4 scales: 256-byte groups (g, s), s < K/256, at
+ *     scales offset + (g*K/256 + s)*256; byte 4*L + j is the E8M0 scale of
+ *     packed row 32g + L%32 for the 32-element K block 8s + 2j + L/32 (so the
+ *     dword of lane L serves its four 64-K MFMA steps through the op_sel byte
+ *     select).
+ *   FP8 codes: 2048-byte fragments (g, c) at 256 + (g*K/64 + c)*2048; byte
+ *     32*L + b holds the E4M3 code of packed row 32g + L%32 at
+ *     k = 64c + 32*(L/32) + b.
+ *   FP8 scales: fp32 [Np] at the scales offset, in packed row order.
+ *
+ * Supported: K % 256 == 0; N % 64 == 0 (GATED_SILU: N % 128 == 0); ldw >= K,
+ * ldw % 8 == 0; w_bf16 and packed 16-byte aligned.  W must be finite. */
+dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N, int K,
+                            int ldw, void* packed, void* stream);
+
+/* ---------------------------------------------------------------- activation quantizer
+ * Quantizes x (bf16 [M, K], row stride ldx elements) on the fly; a bit-exact
+ * kernel (round to nearest, ties to even).
+ *
+ * FP4 (activation statistics change every diffusion iteration, so scales are
+ * computed per call from the data -- page "Versnellende diffusiemodellen met
+ * TheStage AI", section on acceleration and compression):
+ *   per row and per 32-element K block: amax = max |x|;
+ *   scale byte = clamp(floor(log2 amax) - 2 + 127, 0, 254), 0 if amax == 0;
+ *   code = sign(x) | RNE_E2M1(min(|x| / 2^(byte-127), 6)), the sign bit copied
+ *   from x even when the magnitude rounds to 0.
+ *   codes: u8 [M][K/2], even k in the low nibble; scales: u8 E8M0 [M][K/32].
+ * FP8:
+ *   per row: s = fl32(amax / 448) (1 if the row is zero); code =
+ *   RNE_E4M3(fl32(x / s)), both divisions IEEE fp32; codes u8 [M][K]; scales fp32 [M].
+ *
+ * Supported: K % 256 == 0, ldx >= K, ldx % 8 == 0, pointers 16-byte aligned
+ * (FP4 scales: any alignment).  x must be finite. */
+dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int ldx,
+                            void* codes, void* scales, void* stream);
+
+/* ---------------------------------------------------------------- fused GEMM + epilogue, FP4
+ * out = epi(A W^T) with A the FP4 activations from dit_quantize_act
+ * (a_codes [M][K/2], a_scales [M][K/32]) and W the blob from dit_pack_weights
+ * (FP4, packed for the same epi family).  The fp32 accumulator goes through the
+ * epilogue and is stored once as bf16 (round to nearest even) into out_bf16
+ * [M][ldo]; the output width is N/2 for GATED_SILU and N otherwise.
+ * `rms` must be non-NULL exactly when epi == DIT_EPI_QK_RMSNORM (host pointer to
+ * the struct; the gammas inside are device pointers), with
+ * N == 3 * n_heads * head_dim and head_dim in {128, 256}.
+ * Supported: M >= 1 (any), K % 256 == 0, N % 64 == 0 (GATED_SILU: N % 128 == 0),
+ * ldo >= output width, ldo % 8 == 0, pointers 16-byte aligned (a_scales: 8). */
+dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const void* w_packed,
+                                int M, int N, int K, dit_epi epi, const dit_rmsnorm_params* rms,
+                                void* out_bf16, int ldo, void* stream);
+
+/* ---------------------------------------------------------------- fused GEMM + epilogue, FP8
+ * out = epi((A W^T) * s_a[m] * s_w[n]) with A the E4M3 codes [M][K] and fp32
+ * row scales [M] from dit_quantize_act, W an FP8 blob.  epi is IDENTITY or
+ * GATED_SILU (QK_RMSNORM returns DIT_EUNSUPPORTED).  Same shape rules as the FP4
+ * entry point (a_scales 4-byte aligned). */
+dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, const void* w_packed,
+                                int M, int N, int K, dit_epi epi,
+                                void* out_bf16, int ldo, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* dit_status_str(dit_status status);
+
+/* Detail of the most recent DIT_EDEVICE returned on the calling thread (the
+ * failing HIP call and its error string); "" if there was none.  The pointer
+ * stays valid until the thread's next failing call. */
+const char* dit_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DITQ_H */

@@ -1,0 +1,106 @@
+"""The C ABI on the CPU: the library loads, exports every function include/ditq.h
+declares, its size queries are right, and every validation path returns its
+status before any HIP call (fake pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ditq.h")
+
+ditq = pytest.importorskip("bit_gemm_dit_amd", reason="libditq.so not built")
+
+OK, EINVAL, EUNSUP, EALIGN, EDEVICE = 0, 1, 2, 3, 4
+A = 0x10000          # fake, 16-byte aligned "device" addresses: never dereferenced
+B = 0x20000
+C = 0x30000
+D = 0x40000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dit_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared()
+    assert names == sorted(ditq.EXPORTED)
+    lib = ctypes.CDLL(ditq.library_path)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_size_queries():
+    assert ditq.dit_act_code_bytes(1, 4608, 3072) == 4608 * 1536
+    assert ditq.dit_act_scale_bytes(1, 4608, 3072) == 4608 * 96
+    assert ditq.dit_act_code_bytes(2, 9216, 3072) == 9216 * 3072
+    assert ditq.dit_act_scale_bytes(2, 9216, 3072) == 9216 * 4
+    assert ditq.dit_packed_weight_bytes(1, 1, 16384, 3072) == 256 + 16384 * 1536 + 16384 * 96
+    assert ditq.dit_packed_weight_bytes(1, 0, 320, 256) == 256 + 512 * 128 + 512 * 8     # rows padded to 512
+    assert ditq.dit_packed_weight_bytes(2, 0, 12288, 3072) == 256 + 12288 * 3072 + 12288 * 4
+    assert ditq.dit_packed_weight_bytes(1, 0, 64, 128) == 0          # K % 256
+    assert ditq.dit_packed_weight_bytes(1, 1, 64, 256) == 0          # gated needs N % 128
+    assert ditq.dit_packed_weight_bytes(2, 2, 384, 256) == 0         # FP8 has no RMSNorm epilogue
+    assert ditq.dit_packed_weight_bytes(3, 0, 64, 256) == 0
+    assert ditq.dit_act_code_bytes(1, 0, 256) == 0
+
+
+def test_status_strings():
+    for s in range(5):
+        assert ditq.dit_status_str(s)
+    assert ditq.dit_status_str(99) == "unknown status"
+
+
+def _q4(a=A, s=B, w=C, M=64, N=512, K=256, epi=1, rms=None, out=D, ldo=256):
+    return ditq._lib.dit_gemm_q4_epilogue(a, s, w, M, N, K, epi, ctypes.byref(rms) if rms else None, out, ldo, None)
+
+
+def test_gemm_q4_validation():
+    assert _q4(a=None) == EINVAL
+    assert _q4(M=0) == EINVAL
+    assert _q4(epi=7) == EINVAL
+    assert _q4(epi=2) == EINVAL                                      # RMSNorm without params
+    r = ditq.RmsNormParams(128, 1, A, B, 1e-6)
+    assert _q4(epi=1, rms=r) == EINVAL                               # params without RMSNorm
+    assert _q4(epi=2, rms=r, N=512) == EINVAL                        # N != 3 H D
+    assert _q4(epi=2, rms=ditq.RmsNormParams(128, 1, A, B, 0.0), N=384, ldo=384) == EINVAL   # eps <= 0
+    assert _q4(epi=2, rms=ditq.RmsNormParams(64, 2, A, B, 1e-6), N=384, ldo=384) == EUNSUP   # head_dim 64
+    assert _q4(K=128) == EUNSUP
+    assert _q4(N=576) == EUNSUP                                      # gated needs N % 128
+    assert _q4(out=D + 8) == EALIGN
+    assert _q4(ldo=255) == EALIGN                                    # < output width 256
+    assert _q4(ldo=260) == EALIGN                                    # not a multiple of 8
+    assert _q4(epi=0, ldo=256) == EALIGN                             # identity width is 512
+    assert _q4(s=B + 4) == EALIGN
+    # every argument valid: the first HIP call reports that no gfx950 device is usable
+    if not _has_gpu():
+        assert _q4() == EDEVICE
+
+
+def test_other_entry_points_validation():
+    lib = ditq._lib
+    assert lib.dit_quantize_act(1, None, 4, 256, 256, B, C, None) == EINVAL
+    assert lib.dit_quantize_act(3, A, 4, 256, 256, B, C, None) == EINVAL
+    assert lib.dit_quantize_act(1, A, 4, 300, 304, B, C, None) == EUNSUP
+    assert lib.dit_quantize_act(1, A, 4, 256, 250, B, C, None) == EALIGN
+    assert lib.dit_quantize_act(1, A + 2, 4, 256, 256, B, C, None) == EALIGN
+    assert lib.dit_quantize_act(2, A, 4, 256, 256, B, C + 2, None) == EALIGN
+    assert lib.dit_pack_weights(1, 0, A, 64, 256, 256, None, None) == EINVAL
+    assert lib.dit_pack_weights(1, 1, A, 64, 256, 256, B, None) == EUNSUP
+    assert lib.dit_pack_weights(2, 2, A, 384, 256, 256, B, None) == EUNSUP
+    assert lib.dit_pack_weights(1, 0, A, 64, 256, 264, B + 1, None) == EALIGN
+    assert lib.dit_gemm_q8_epilogue(A, B, C, 4, 512, 256, 2, D, 512, None) == EUNSUP
+    assert lib.dit_gemm_q8_epilogue(A, B + 2, C, 4, 512, 256, 0, D, 512, None) == EALIGN
+    assert lib.dit_gemm_q8_epilogue(A, None, C, 4, 512, 256, 0, D, 512, None) == EINVAL
+    if not _has_gpu():
+        assert lib.dit_quantize_act(1, A, 4, 256, 256, B, C, None) == EDEVICE
+        assert lib.dit_pack_weights(2, 1, A, 128, 256, 256, B, None) == EDEVICE
+        assert lib.dit_gemm_q8_epilogue(A, B, C, 4, 512, 256, 1, D, 256, None) == EDEVICE
+
+
+def _has_gpu():
+    import torch
+    return torch.cuda.device_count() > 0

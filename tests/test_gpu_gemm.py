@@ -1,0 +1,139 @@
+"""GPU parity of the fused GEMM + epilogue against the float64 oracle.
+
+Small problems (several tiles, a ragged M tail, M = 1) are compared element by
+element; the full-size workloads run in the launch configuration the benchmark
+times and are compared on sampled token rows (every column of each sampled row),
+which the oracle computes one row at a time.  Tolerance: per element
+|gpu - oracle| <= 8e-3 * row-RMS(oracle) + half a bf16 ulp of the oracle value.
+"""
+import numpy as np
+import pytest
+
+from oracle import layer
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+FMT = {"fp4": 1, "fp8": 2}
+EPI = {"identity": 0, "gated_silu": 1, "qk_rmsnorm": 2}
+
+
+@pytest.fixture(scope="module")
+def ditq():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_gemm_dit_amd
+    return bit_gemm_dit_amd
+
+
+def run_layer(ditq, d, fmt, epi, ldo=None, stream=None, guard=0):
+    """Pack W, quantize x, run the fused GEMM through the C ABI; returns bf16 bits [M, width]."""
+    import torch
+    from tests.gpu_util import to_dev_bf16, to_host_bits
+    M, K = d["x"].shape
+    N = d["w"].shape[0]
+    f, e = FMT[fmt], EPI[epi]
+    width = N // 2 if e == 1 else N
+    ldo = ldo or width
+    x = to_dev_bf16(d["x"])
+    w = to_dev_bf16(d["w"])
+    st = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    blob = torch.empty(ditq.dit_packed_weight_bytes(f, e, N, K), dtype=torch.uint8, device="cuda")
+    ditq.dit_pack_weights(f, e, w.data_ptr(), N, K, K, blob.data_ptr(), st)
+    codes = torch.empty(ditq.dit_act_code_bytes(f, M, K), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(ditq.dit_act_scale_bytes(f, M, K), dtype=torch.uint8, device="cuda")
+    ditq.dit_quantize_act(f, x.data_ptr(), M, K, K, codes.data_ptr(), scales.data_ptr(), st)
+    # output with guard elements before and after, and a poisoned padding region
+    total = guard + M * ldo + guard
+    out = torch.full((total,), -12345, dtype=torch.int16, device="cuda")
+    optr = out.data_ptr() + 2 * guard
+    rms = None
+    keep = []
+    if e == 2:
+        gq = torch.from_numpy(d["gamma_q"]).cuda()
+        gk = torch.from_numpy(d["gamma_k"]).cuda()
+        keep = [gq, gk]
+        rms = ditq.RmsNormParams(d["head_dim"], d["n_heads"], gq.data_ptr(), gk.data_ptr(), d["eps"])
+    if f == 1:
+        ditq.dit_gemm_q4_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, e, rms, optr, ldo, st)
+    else:
+        ditq.dit_gemm_q8_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, e, optr, ldo, st)
+    torch.cuda.synchronize()
+    del keep
+    o = out.cpu().numpy().view(np.uint16)
+    assert np.all(o[:guard] == np.uint16(-12345 & 0xFFFF)) and np.all(o[guard + M * ldo:] == np.uint16(-12345 & 0xFFFF))
+    body = o[guard:guard + M * ldo].reshape(M, ldo)
+    assert np.all(body[:, width:] == np.uint16(-12345 & 0xFFFF)), "write past the output width"
+    return body[:, :width].copy()
+
+
+def oracle_rows(d, fmt, epi, rows=None):
+    kw = {}
+    if epi == "qk_rmsnorm":
+        kw = dict(n_heads=d["n_heads"], head_dim=d["head_dim"], gamma_q=d["gamma_q"], gamma_k=d["gamma_k"], eps=d["eps"])
+    return layer.forward(d["x"], d["w"], fmt, epi, rows=rows, **kw)
+
+
+SMALL = [
+    # workload kind, fmt, epi, M, N, K, n_heads
+    ("tiny_gated_silu", "fp4", "gated_silu", 64, 512, 256, None),
+    ("mlp_gated_silu", "fp4", "gated_silu", 300, 1024, 512, None),
+    ("mlp_gated_silu", "fp4", "gated_silu", 1, 640, 768, None),
+    ("mlp_gated_silu", "fp4", "identity", 257, 832, 512, None),
+    ("mlp_gated_silu", "fp4", "identity", 63, 256, 256, None),
+    ("qkv_rmsnorm_hd128", "fp4", "qk_rmsnorm", 300, None, 512, 2),
+    ("qkv_rmsnorm_hd128", "fp4", "qk_rmsnorm", 5, None, 256, 1),
+    ("qkv_rmsnorm_hd256", "fp4", "qk_rmsnorm", 130, None, 512, 1),
+    ("qkv_rmsnorm_hd256", "fp4", "qk_rmsnorm", 70, None, 768, 3),
+    ("fp8_cfg_pair", "fp8", "identity", 300, 768, 512, None),
+    ("fp8_cfg_pair", "fp8", "gated_silu", 129, 1024, 768, None),
+    ("fp8_cfg_pair", "fp8", "identity", 1, 320, 256, None),
+]
+
+
+@pytest.mark.parametrize("kind,fmt,epi,M,N,K,H", SMALL, ids=[f"{s[1]}-{s[2]}-M{s[3]}-K{s[5]}" for s in SMALL])
+def test_small_all_elements(ditq, kind, fmt, epi, M, N, K, H):
+    from tests.gpu_util import compare_bf16
+    d = make_inputs(kind, seed=M + K, M=M, N=N, K=K, n_heads=H)
+    print(f"case {kind} {fmt} {epi} M={M} N={d['w'].shape[0]} K={K}", flush=True)
+    g = run_layer(ditq, d, fmt, epi, guard=64)
+    y = oracle_rows(d, fmt, epi)
+    compare_bf16(g, y, f"{kind}/{epi}")
+
+
+def test_tiny_workload_exact_config(ditq):
+    from tests.gpu_util import compare_bf16
+    d = make_inputs("tiny_gated_silu", seed=0)
+    g = run_layer(ditq, d, "fp4", "gated_silu")
+    rep = compare_bf16(g, oracle_rows(d, "fp4", "gated_silu"), "tiny")
+    print("tiny literal max err / row-RMS:", rep["literal_max_err_over_rowrms"])
+
+
+def test_ldo_stream_and_determinism(ditq):
+    import torch
+    from tests.gpu_util import compare_bf16
+    d = make_inputs("mlp_gated_silu", seed=5, M=200, N=1024, K=512)
+    s = torch.cuda.Stream()
+    g1 = run_layer(ditq, d, "fp4", "gated_silu", ldo=520, stream=s, guard=16)
+    g2 = run_layer(ditq, d, "fp4", "gated_silu", ldo=512)
+    np.testing.assert_array_equal(g1, g2)
+    compare_bf16(g1, oracle_rows(d, "fp4", "gated_silu"), "ldo")
+
+
+FULL = [("qkv_rmsnorm_hd128", "qk_rmsnorm"), ("mlp_gated_silu", "gated_silu"),
+        ("qkv_rmsnorm_hd256", "qk_rmsnorm"), ("fp8_cfg_pair", "identity"), ("fp8_cfg_pair", "gated_silu")]
+
+
+@pytest.mark.parametrize("name,epi", FULL, ids=[f"{a}-{b}" for a, b in FULL])
+def test_full_size_sampled_rows(ditq, name, epi):
+    from tests.gpu_util import compare_bf16
+    wl = WORKLOADS[name]
+    d = make_inputs(name, seed=0)
+    print(f"case full {name} {epi}", flush=True)
+    g = run_layer(ditq, d, wl.fmt, epi)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 255, 256, wl.M - 1], rng.choice(wl.M, 40, replace=False)]))
+    y = oracle_rows(d, wl.fmt, epi, rows=rows)
+    rep = compare_bf16(g[rows], y, f"{name}/{epi}")
+    print(f"{name}/{epi}: literal max err / row-RMS = {rep['literal_max_err_over_rowrms']:.4g}")

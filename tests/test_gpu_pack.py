@@ -1,0 +1,73 @@
+"""GPU parity of the weight packer: the blob, decoded from its documented layout
+by the oracle's reader, holds exactly the oracle's codes and scales."""
+import numpy as np
+import pytest
+
+from oracle import packed, quant
+from workloads import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ditq():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_gemm_dit_amd
+    return bit_gemm_dit_amd
+
+
+def _pack(ditq, bits, fmt, epi, ldw=None):
+    import torch
+    from tests.gpu_util import to_dev_bf16
+    N, K = bits.shape
+    ldw = ldw or K
+    buf = np.zeros((N, ldw), dtype=np.uint16)
+    buf[:, :K] = bits
+    w = to_dev_bf16(buf)
+    nbytes = ditq.dit_packed_weight_bytes(fmt, epi, N, K)
+    blob = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")      # poison: padding must be written
+    ditq.dit_pack_weights(fmt, epi, w.data_ptr(), N, K, ldw, blob.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return blob.cpu().numpy()
+
+
+@pytest.mark.parametrize("N,K,epi,ldw", [(512, 256, 1, 256), (320, 256, 0, 264), (128, 768, 2, 768),
+                                         (1024, 512, 1, 512)])
+def test_fp4_pack_bitexact(ditq, N, K, epi, ldw):
+    d = make_inputs("qkv_rmsnorm_hd128", seed=N, M=1, N=N, K=K)
+    blob = _pack(ditq, d["w"], 1, epi, ldw)
+    hdr = packed.read_header(blob)
+    assert (hdr["magic"], hdr["version"], hdr["fmt"], hdr["epi"], hdr["N"], hdr["K"]) == (packed.MAGIC, 1, 1, epi, N, K)
+    assert hdr["total"] == blob.size
+    c, s, pad = packed.decode(blob, 1, epi, N, K)
+    rc, rs = quant.quantize_fp4(d["w"])
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
+    assert not pad["codes"].any() and not pad["scales"].any()
+
+
+@pytest.mark.parametrize("name,epi", [("mlp_gated_silu", 1), ("qkv_rmsnorm_hd256", 2)])
+def test_fp4_pack_full_size(ditq, name, epi):
+    d = make_inputs(name, seed=0, M=1)
+    N, K = d["w"].shape
+    blob = _pack(ditq, d["w"], 1, epi)
+    c, s, _ = packed.decode(blob, 1, epi, N, K)
+    rc, rs = quant.quantize_fp4(d["w"])
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
+
+
+@pytest.mark.parametrize("N,K,epi", [(320, 256, 0), (256, 512, 1), (12288, 3072, 1)])
+def test_fp8_pack_bitexact(ditq, N, K, epi):
+    d = make_inputs("fp8_cfg_pair", seed=N, M=1, N=N, K=K)
+    d["w"][3, :] = 0                                                   # an all-zero row
+    blob = _pack(ditq, d["w"], 2, epi)
+    hdr = packed.read_header(blob)
+    assert (hdr["magic"], hdr["fmt"], hdr["epi"], hdr["N"], hdr["K"]) == (packed.MAGIC, 2, epi, N, K)
+    c, s, pad = packed.decode(blob, 2, epi, N, K)
+    rc, rs = quant.quantize_fp8(d["w"])
+    np.testing.assert_array_equal(s.view(np.uint32), rs.view(np.uint32))
+    np.testing.assert_array_equal(c, rc)
+    assert not pad["codes"].any()
