@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused low-bit DiT linear layer on one MI355X.
+
+One step = the whole hot path on one batch of synthetic activations that are
+already resident in HBM: the on-the-fly FP4 activation quantizer followed by the
+fused FP4 GEMM + epilogue, for the DiT MLP up-projection workload (M=4608 tokens,
+K=3072, N=2x8192 gate/up pairs, gated-SiLU epilogue, bf16 output 4608x8192).
+Weights are packed once before timing (an offline step).  Input/output sets
+rotate over more than the 256 MB Infinity Cache, so every step reads its
+operands from HBM rather than from a warm cache.
+
+Prints one JSON line:
+  value        = 2*M*N*K / (quantize + GEMM time per step), TFLOP/s
+  roofline     = the GEMM kernel alone: 2*M*N*K / its average duration (HIP events
+                 around each launch in the timed region) against the MI355X dense
+                 FP4 MFMA peak; traffic = HBM bytes per launch from rocprofv3
+                 counters recorded under profiles/ (null if the kernel source has
+                 changed since)
+  cpu_baseline = the CPU oracle (float64) on a bounded row sample of the same
+                 workload, timed on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused FP4 GEMM+epilogue TFLOP/s and % of MI355X FP4 MFMA peak, M=4608 K=3072"
+PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0}        # MI355X dense MFMA peaks
+HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_fp4_mlp_gated_silu.txt")
+GEMM_SRC = os.path.join(ROOT, "bit_gemm_dit_amd", "csrc", "gemm.hip")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in (GEMM_SRC, os.path.join(ROOT, "bit_gemm_dit_amd", "csrc", "common.hpp")):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic() -> float | None:
+    """HBM bytes per GEMM launch from the committed counter summary, if it still
+    describes the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split("=", 1) for line in f.read().splitlines() if "=" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_hash", "").strip() != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def build_sets(ditq, torch, wl, n_sets: int, epi: int):
+    from workloads import make_inputs
+    d = make_inputs(wl.name, seed=0)
+    x0 = torch.from_numpy(d["x"].view("int16")).cuda().view(torch.bfloat16)
+    w = torch.from_numpy(d["w"].view("int16")).cuda().view(torch.bfloat16)
+    blob0 = ditq.pack_weights(w, ditq.FMT_FP4, epi)
+    del w
+    sets = []
+    for i in range(n_sets):
+        x = x0 if i == 0 else x0.clone()
+        blob = blob0 if i == 0 else blob0.clone()
+        codes = torch.empty((wl.M, wl.K // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((wl.M, wl.K // 32), dtype=torch.uint8, device="cuda")
+        out = torch.empty((wl.M, wl.N // 2), dtype=torch.bfloat16, device="cuda")
+        sets.append((x, blob, codes, scales, out))
+    return d, sets
+
+
+def run_gpu(args):
+    import torch
+    import bit_gemm_dit_amd as ditq
+    from workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    epi = ditq.EPI_GATED_SILU
+    d, sets = build_sets(ditq, torch, wl, args.rotate, epi)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    M, N, K = wl.M, wl.N, wl.K
+
+    def step(i, ev=None):
+        x, blob, codes, scales, out = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        ditq.dit_quantize_act(ditq.FMT_FP4, x.data_ptr(), M, K, K, codes.data_ptr(), scales.data_ptr(), sptr)
+        if ev is not None:
+            ev[1].record(stream)
+        ditq.dit_gemm_q4_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi, None,
+                                  out.data_ptr(), N // 2, sptr)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = [e[0].elapsed_time(e[1]) for e in events]
+    g_ms = [e[1].elapsed_time(e[2]) for e in events]
+    flops = wl.flops
+    ms_per_step = wall * 1e3 / args.steps
+    gemm_ms = sum(g_ms) / len(g_ms)
+    quant_ms = sum(q_ms) / len(q_ms)
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    quant_bytes = M * K * 2 + M * K // 2 + M * K // 32
+    traffic = read_traffic()
+    res = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": M, "N": N, "K": K, "epilogue": "gated_silu",
+                   "format": "fp4_e2m1_e8m0_block32", "output": f"bf16 {M}x{N // 2}",
+                   "rotating_sets": len(sets)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["fp4"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["fp4"], 4), "traffic": traffic},
+        "kernels": {
+            "gemm_fp4_gated_silu_us": round(gemm_ms * 1e3, 2),
+            "quant_fp4_us": round(quant_ms * 1e3, 2),
+            "quant_fp4_GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+            "quant_fp4_hbm_frac": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / HBM_GBPS, 4),
+        },
+    }
+    if args.all_configs:
+        res["other_configs"] = time_other_configs(ditq, torch, args)
+    return res, d
+
+
+def time_other_configs(ditq, torch, args):
+    """GEMM-only and quantizer timings of the other full-size workloads (informational)."""
+    from workloads import WORKLOADS, make_inputs
+    out = {}
+    plans = [("qkv_rmsnorm_hd128", "qk_rmsnorm"), ("qkv_rmsnorm_hd256", "qk_rmsnorm"),
+             ("fp8_cfg_pair", "identity"), ("fp8_cfg_pair", "gated_silu")]
+    epis = {"identity": 0, "gated_silu": 1, "qk_rmsnorm": 2}
+    for name, epi_name in plans:
+        wl = WORKLOADS[name]
+        d = make_inputs(name, seed=0)
+        fmt = ditq.FMT_FP4 if wl.fmt == "fp4" else ditq.FMT_FP8
+        epi = epis[epi_name]
+        x = torch.from_numpy(d["x"].view("int16")).cuda().view(torch.bfloat16)
+        w = torch.from_numpy(d["w"].view("int16")).cuda().view(torch.bfloat16)
+        blob = ditq.pack_weights(w, fmt, epi)
+        del w
+        rms = None
+        keep = []
+        if epi == 2:
+            gq = torch.from_numpy(d["gamma_q"]).cuda()
+            gk = torch.from_numpy(d["gamma_k"]).cuda()
+            keep = [gq, gk]
+            rms = ditq.rmsnorm_params(gq, gk, wl.n_heads, wl.eps)
+        codes, scales = ditq.quantize_act(x, fmt)
+        o = ditq.gemm(codes, scales, blob, wl.N, wl.K, fmt, epi, rms=rms)
+        # flush the Infinity Cache between launches by touching a 512 MB buffer
+        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        times_g, times_q = [], []
+        for _ in range(max(3, args.steps // 2)):
+            flush.zero_()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            ditq.dit_quantize_act(fmt, x.data_ptr(), wl.M, wl.K, wl.K, codes.data_ptr(), scales.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream)
+            e[1].record()
+            ditq.gemm(codes, scales, blob, wl.N, wl.K, fmt, epi, rms=rms, out=o)
+            e[2].record()
+            torch.cuda.synchronize()
+            times_q.append(e[0].elapsed_time(e[1]))
+            times_g.append(e[1].elapsed_time(e[2]))
+        times_g.sort()
+        times_q.sort()
+        g = times_g[len(times_g) // 2]
+        q = times_q[len(times_q) // 2]
+        qbytes = wl.M * wl.K * 2 + (wl.M * wl.K // 2 + wl.M * wl.K // 32 if fmt == 1 else wl.M * wl.K + 4 * wl.M)
+        out[f"{name}/{epi_name}"] = {
+            "gemm_us": round(g * 1e3, 2),
+            "tflops": round(wl.flops / (g * 1e-3) / 1e12, 1),
+            "frac_of_peak": round(wl.flops / (g * 1e-3) / 1e12 / PEAK_TFLOPS[wl.fmt], 4),
+            "quant_us": round(q * 1e3, 2),
+            "quant_GBps": round(qbytes / (q * 1e-3) / 1e9, 1),
+        }
+        del keep, flush, blob, x, codes, scales, o
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(d, budget_s: float):
+    """Time the CPU oracle (quantize the activation rows, decode, float64 GEMM,
+    gated-SiLU) on a row sample sized to about `budget_s` seconds; weights are
+    quantized and decoded once beforehand, as packing is offline."""
+    import numpy as np
+    from oracle import epilogue, quant
+    cores = len(os.sched_getaffinity(0))
+    M, K = d["x"].shape
+    N = d["w"].shape[0]
+    wc, ws = quant.quantize_fp4(d["w"])
+    Wd = quant.dequantize_fp4(wc, ws)
+    WdT = np.ascontiguousarray(Wd.T)
+    del Wd
+
+    def run(rows):
+        ac, as_ = quant.quantize_fp4(d["x"][:rows])
+        acc = quant.dequantize_fp4(ac, as_) @ WdT
+        return epilogue.gated_silu(acc)
+
+    rows = 64
+    t = time.perf_counter()
+    run(rows)
+    dt = time.perf_counter() - t
+    rows = int(min(M, max(64, rows * budget_s / max(dt, 1e-3))))
+    rows = max(64, rows // 64 * 64)
+    t = time.perf_counter()
+    run(rows)
+    dt = time.perf_counter() - t
+    flops = 2.0 * rows * N * K
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows} of {M} token rows of the same workload (activation quantize + decode + float64 "
+                      f"GEMM + gated-SiLU; weights quantized beforehand), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mlp_gated_silu")
+    ap.add_argument("--rotate", type=int, default=4, help="input/output sets cycled through (> cache size)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-configs", action="store_true", help="also time the other workloads' kernels")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this layer runs on one GPU; multi-GPU runs are not part of this benchmark "
+                                   "(the path would shard over token rows with replicated weights)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if args.workload != "mlp_gated_silu":
+        raise SystemExit("the headline step is the mlp_gated_silu workload; use --all-configs for the others")
+    res, d = run_gpu(args)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
