@@ -47,6 +47,12 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # A kernel whose host-side stub was dropped leaves an undefined symbol that only
+    # shows up when the library is loaded; refuse such a library here instead.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "ditq" in ln]
+    if nm.returncode != 0 or missing:
+        raise RuntimeError(f"libditq.so has undefined library symbols: {missing or nm.stderr}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -130,21 +130,27 @@ __device__ inline float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Operand fragments of one 64-K MFMA step: TN weight fragments, TM token fragments.
+template <class T>
+struct Frags {
+  v8i w[T::TN];
+  v8i a[T::TM];
+};
+
 template <class T, int J>
-__device__ __forceinline__ void mfma_step(v16f (&acc)[T::TN][T::TM], const uint8_t* wb, const uint8_t* ab,
-                                          int wn, int wm, int lane, const uint32_t* wsc, const uint32_t* asc) {
+__device__ __forceinline__ void load_frags(Frags<T>& f, const uint8_t* wb, const uint8_t* ab, int wn, int wm,
+                                           int lane) {
   const int h = lane >> 5, l32 = lane & 31;
-  v8i wf[T::TN], af[T::TM];
 #pragma unroll
   for (int tn = 0; tn < T::TN; ++tn) {
-    const uint8_t* f = wb + ((wn * T::TN + tn) * T::CH + J) * T::FRAG;
+    const uint8_t* fp = wb + ((wn * T::TN + tn) * T::CH + J) * T::FRAG;
     if constexpr (T::FMT == FMT_FP4) {
-      const v4i x = *reinterpret_cast<const v4i*>(f + 16 * lane);
-      wf[tn] = __builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1);
+      const v4i x = *reinterpret_cast<const v4i*>(fp + 16 * lane);
+      f.w[tn] = __builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1);
     } else {
-      const v4i x0 = *reinterpret_cast<const v4i*>(f + 32 * lane);
-      const v4i x1 = *reinterpret_cast<const v4i*>(f + 32 * lane + 16);
-      wf[tn] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const v4i x0 = *reinterpret_cast<const v4i*>(fp + 32 * lane);
+      const v4i x1 = *reinterpret_cast<const v4i*>(fp + 32 * lane + 16);
+      f.w[tn] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   }
 #pragma unroll
@@ -154,37 +160,82 @@ __device__ __forceinline__ void mfma_step(v16f (&acc)[T::TN][T::TM], const uint8
     if constexpr (T::FMT == FMT_FP4) {
       const int c = 2 * J + h;
       const v4i x = *reinterpret_cast<const v4i*>(row + 16 * (c ^ swz(r)));
-      af[tm] = __builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1);
+      f.a[tm] = __builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1);
     } else {
       const int c = 4 * J + 2 * h;
       const v4i x0 = *reinterpret_cast<const v4i*>(row + 16 * (c ^ swz(r)));
       const v4i x1 = *reinterpret_cast<const v4i*>(row + 16 * ((c + 1) ^ swz(r)));
-      af[tm] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+      f.a[tm] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   }
+}
+
+template <class T, int J>
+__device__ __forceinline__ void mfma_frags(v16f (&acc)[T::TN][T::TM], const Frags<T>& f, const uint32_t* wsc,
+                                           const uint32_t* asc) {
 #pragma unroll
   for (int tn = 0; tn < T::TN; ++tn)
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) {
       if constexpr (T::FMT == FMT_FP4)
-        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[tn], af[tm], acc[tn][tm], 4, 4, J,
+        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[tn], f.a[tm], acc[tn][tm], 4, 4, J,
                                                                       (int)wsc[tn], J, (int)asc[tm]);
       else
-        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[tn], af[tm], acc[tn][tm], 0, 0, 0,
+        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[tn], f.a[tm], acc[tn][tm], 0, 0, 0,
                                                                       0x7F7F7F7F, 0, 0x7F7F7F7F);
     }
 }
 
+// sched_group_barrier masks
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Issue order for one 64-K step: the LDS reads of the next step's fragments are
+// spread between this step's MFMAs, so their latency hides behind MFMA work.
+template <class T>
+__device__ __forceinline__ void interleave_hint(bool next_loads) {
+  constexpr int NMFMA = T::TN * T::TM;
+  constexpr int NDS = (T::TN + T::TM) * (T::FMT == FMT_FP4 ? 1 : 2);
+  if (next_loads) {
+#pragma unroll
+    for (int i = 0; i < NDS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    if constexpr (NMFMA > NDS) __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - NDS, 0);
+  } else {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA, 0);
+  }
+}
+
+// One k-step: fragments of 64-K step j+1 are read from LDS while the MFMAs of step
+// j run (two register sets, f0 / f1).
 template <class T>
 __device__ __forceinline__ void compute_stage(v16f (&acc)[T::TN][T::TM], const uint8_t* stage, int wn, int wm,
                                               int lane, const uint32_t* wsc, const uint32_t* asc) {
   const uint8_t* wb = stage;
   const uint8_t* ab = stage + T::W_BYTES;
-  mfma_step<T, 0>(acc, wb, ab, wn, wm, lane, wsc, asc);
-  mfma_step<T, 1>(acc, wb, ab, wn, wm, lane, wsc, asc);
+  Frags<T> f0, f1;
+  load_frags<T, 0>(f0, wb, ab, wn, wm, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags<T, 1>(f1, wb, ab, wn, wm, lane);
+  mfma_frags<T, 0>(acc, f0, wsc, asc);
+  interleave_hint<T>(true);
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (T::CH == 4) {
-    mfma_step<T, 2>(acc, wb, ab, wn, wm, lane, wsc, asc);
-    mfma_step<T, 3>(acc, wb, ab, wn, wm, lane, wsc, asc);
+    load_frags<T, 2>(f0, wb, ab, wn, wm, lane);
+    mfma_frags<T, 1>(acc, f1, wsc, asc);
+    interleave_hint<T>(true);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags<T, 3>(f1, wb, ab, wn, wm, lane);
+    mfma_frags<T, 2>(acc, f0, wsc, asc);
+    interleave_hint<T>(true);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_frags<T, 3>(acc, f1, wsc, asc);
+    interleave_hint<T>(false);
+  } else {
+    mfma_frags<T, 1>(acc, f1, wsc, asc);
+    interleave_hint<T>(false);
   }
 }
 
@@ -302,9 +353,44 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
 }
 
 // ---------------------------------------------------------------- kernel
+// An empty volatile asm that reads every accumulator: the MFMAs of a k-step must
+// then be issued before it, and it stays ordered with the wait and the barrier that
+// follow (MFMAs touch no memory, so without it they may be sunk below the barrier).
+// The asm exists only in the device pass: on the host pass "a" would name an x86
+// register, and the failed constraint would silently drop the kernel's host stub.
+template <class T>
+__device__ __forceinline__ void pin_accumulators(v16f (&acc)[T::TN][T::TM]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int tn = 0; tn < T::TN; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm) asm volatile("" ::"a"(acc[tn][tm]));
+#endif
+}
+
+// N direct-to-LDS copies of 1 KB each: lane L of copy i fetches 16 bytes at
+// voff[i] + soff and the hardware writes them to dst + 1024 i + 16 L.
+// (A plain device function: inside a lambda the builtin would also be compiled
+// for the host, where it fails and takes the kernel's host stub with it.)
+template <int N>
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, const uint32_t* voff, int soff,
+                                            uint8_t* dst) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16,
+                                             voff[i], soff, 0, 0);
+}
+
+// waitcnt immediates (gfx9 encoding: vmcnt[3:0]|expcnt[6:4]|lgkmcnt[11:8]|vmcnt_hi[15:14])
+constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0), others unconstrained
+
 template <class T>
 __global__ void __launch_bounds__(T::NT) gemm_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * T::STAGE];
+  constexpr int NW = T::NT / 64;
+  constexpr int WCK = T::W_BYTES / 1024 / NW;    // 1 KB LDS chunks per wave per k-step
+  constexpr int ACK = T::A_BYTES / 1024 / NW;
+  static_assert(T::W_BYTES % (1024 * NW) == 0 && T::A_BYTES % (1024 * NW) == 0, "chunks per wave");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % T::WAVES_N, wm = wave / T::WAVES_N;
   const int l32 = lane & 31;
@@ -318,24 +404,29 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(Params p) {
   const auto a_rsrc = make_rsrc(p.a_codes, p.a_bytes);
   const auto w_rsrc = make_rsrc(p.w_codes, p.w_bytes);
 
-  uint32_t w_off[T::WCH], a_off[T::ACH], a_dst[T::ACH];
+  // Direct-to-LDS copies: each wave instruction writes 1 KB of LDS, lane L at +16L.
+  // Weight chunk q = 1 KB of row group q/4 (copied verbatim: the blob is in lane
+  // order already).  Activation chunk q = 8 rows of 128 bytes; lane L fetches the
+  // logical 16-byte chunk that the swizzle places at slot L%8 of row 8q + L/8.
+  uint32_t w_off[WCK], a_off[ACK];
 #pragma unroll
-  for (int i = 0; i < T::WCH; ++i) {
-    const int q = tid + i * T::NT;
-    w_off[i] = (uint32_t)(n0 / 32 + q / 256) * wgroup + 16u * (q % 256);
+  for (int i = 0; i < WCK; ++i) {
+    const int q = wave * WCK + i;
+    w_off[i] = (uint32_t)(n0 / 32 + (q >> 2)) * wgroup + 1024u * (q & 3) + 16u * lane;
   }
 #pragma unroll
-  for (int i = 0; i < T::ACH; ++i) {
-    const int q = tid + i * T::NT;
-    const int r = q >> 3, c = q & 7;
+  for (int i = 0; i < ACK; ++i) {
+    const int q = wave * ACK + i;
+    const int r = 8 * q + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
     a_off[i] = (uint32_t)(m0 + r) * arow + 16u * c;     // rows >= M lie past the buffer and read as 0
-    a_dst[i] = T::W_BYTES + r * kRowBytes + 16 * (c ^ swz(r));
   }
 
   // E8M0 scales (FP4): one dword per weight row tile, 8 bytes per token row.
   [[maybe_unused]] __amdgpu_buffer_rsrc_t ws_rsrc, as_rsrc;
   uint32_t ws_off[T::TN], as_off[T::TM];
-  uint32_t wsc[T::TN], asc[T::TM];
+  uint32_t wsc[T::TN], asc[T::TM], wsc_n[T::TN];
+  uint32_t asr_lo[T::TM], asr_hi[T::TM];
   const uint32_t perm_sel = (lane & 32) ? 0x07050301u : 0x06040200u;   // blocks 2j + h, j = 0..3
   if constexpr (T::FMT == FMT_FP4) {
     ws_rsrc = make_rsrc(p.w_scales, p.ws_bytes);
@@ -347,16 +438,27 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(Params p) {
     for (int tm = 0; tm < T::TM; ++tm)
       as_off[tm] = (uint32_t)(m0 + wm * T::WM + 32 * tm + l32) * (uint32_t)(p.K / 32);
   }
-  auto load_scales = [&](int ks) {
+  auto issue_loads = [&](int ks, int buf) {
     if constexpr (T::FMT == FMT_FP4) {
 #pragma unroll
       for (int tn = 0; tn < T::TN; ++tn)
-        wsc[tn] = __builtin_amdgcn_raw_buffer_load_b32(ws_rsrc, ws_off[tn], ks * 256, 0);
+        wsc_n[tn] = __builtin_amdgcn_raw_buffer_load_b32(ws_rsrc, ws_off[tn], ks * 256, 0);
 #pragma unroll
       for (int tm = 0; tm < T::TM; ++tm) {
         const auto d = __builtin_amdgcn_raw_buffer_load_b64(as_rsrc, as_off[tm], ks * 8, 0);
-        asc[tm] = __builtin_amdgcn_perm(d[1], d[0], perm_sel);
+        asr_lo[tm] = d[0];
+        asr_hi[tm] = d[1];
       }
+    }
+    copy_to_lds<WCK>(w_rsrc, w_off, ks * 4096, lds + buf * T::STAGE + wave * WCK * 1024);
+    copy_to_lds<ACK>(a_rsrc, a_off, ks * kRowBytes, lds + buf * T::STAGE + T::W_BYTES + wave * ACK * 1024);
+  };
+  auto take_scales = [&]() {
+    if constexpr (T::FMT == FMT_FP4) {
+#pragma unroll
+      for (int tn = 0; tn < T::TN; ++tn) wsc[tn] = wsc_n[tn];
+#pragma unroll
+      for (int tm = 0; tm < T::TM; ++tm) asc[tm] = __builtin_amdgcn_perm(asr_hi[tm], asr_lo[tm], perm_sel);
     }
   };
 
@@ -366,42 +468,22 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(Params p) {
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) acc[tn][tm] = v16f{};
 
-  v4i stw[T::WCH], sta[T::ACH];
-  auto load_stage = [&](int ks) {
-#pragma unroll
-    for (int i = 0; i < T::WCH; ++i)
-      stw[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off[i], ks * 4096, 0));
-#pragma unroll
-    for (int i = 0; i < T::ACH; ++i)
-      sta[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[i], ks * kRowBytes, 0));
-  };
-  auto store_stage = [&](int buf) {
-    uint8_t* base = lds + buf * T::STAGE;
-#pragma unroll
-    for (int i = 0; i < T::WCH; ++i) *reinterpret_cast<v4i*>(base + 16 * (tid + i * T::NT)) = stw[i];
-#pragma unroll
-    for (int i = 0; i < T::ACH; ++i) *reinterpret_cast<v4i*>(base + a_dst[i]) = sta[i];
-  };
-
-  load_stage(0);
-  load_scales(0);
-  store_stage(0);
+  issue_loads(0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  take_scales();
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
     const int cur = ks & 1;
-    uint32_t wsc_cur[T::TN], asc_cur[T::TM];
-#pragma unroll
-    for (int tn = 0; tn < T::TN; ++tn) wsc_cur[tn] = wsc[tn];
-#pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm) asc_cur[tm] = asc[tm];
     const bool more = ks + 1 < nks;
-    if (more) {
-      load_stage(ks + 1);
-      load_scales(ks + 1);
-    }
-    compute_stage<T>(acc, lds + cur * T::STAGE, wn, wm, lane, wsc_cur, asc_cur);
-    if (more) store_stage(cur ^ 1);
-    __syncthreads();
+    // the other buffer was last read in step ks-1, which every wave finished before the barrier
+    if (more) issue_loads(ks + 1, cur ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage<T>(acc, lds + cur * T::STAGE, wn, wm, lane, wsc, asc);
+    pin_accumulators<T>(acc);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);       // this wave's copies into the other buffer have landed
+    if (more) take_scales();
+    __syncthreads();                            // ... and every other wave's; all reads of `cur` are done
   }
   epilogue<T>(p, acc, n0 + wn * T::WN, m0 + wm * T::WM, lane);
 }
