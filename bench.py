@@ -73,8 +73,8 @@ def build_sets(ditq, torch, wl, n_sets: int, epi: int):
     for i in range(n_sets):
         x = x0 if i == 0 else x0.clone()
         blob = blob0 if i == 0 else blob0.clone()
-        codes = torch.empty((wl.M, wl.K // 2), dtype=torch.uint8, device="cuda")
-        scales = torch.empty((wl.M, wl.K // 32), dtype=torch.uint8, device="cuda")
+        codes = torch.empty((wl.K // 128, wl.M, 64), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((wl.K // 128, wl.M, 4), dtype=torch.uint8, device="cuda")
         out = torch.empty((wl.M, wl.N // 2), dtype=torch.bfloat16, device="cuda")
         sets.append((x, blob, codes, scales, out))
     return d, sets
@@ -253,6 +253,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-configs", action="store_true", help="also time the other workloads' kernels")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run one plain device copy of this many MiB first (the reference dispatch that "
+                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -262,6 +265,15 @@ def main():
         sys.exit(2)
     if args.workload != "mlp_gated_silu":
         raise SystemExit("the headline step is the mlp_gated_silu workload; use --all-configs for the others")
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     res, d = run_gpu(args)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)

@@ -151,11 +151,12 @@ def quantize_act(x, fmt: int):
     cb, sb = dit_act_code_bytes(fmt, M, K), dit_act_scale_bytes(fmt, M, K)
     if cb == 0:
         raise DitError(2, "dit_act_code_bytes")
+    # K-panel-major layouts (include/ditq.h): shapes are [panels, M, bytes per panel row]
     if fmt == FMT_FP4:
-        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((K // 128, M, 64), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((K // 128, M, 4), dtype=torch.uint8, device=x.device)
     else:
-        codes = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((K // 64, M, 64), dtype=torch.uint8, device=x.device)
         scales = torch.empty((M,), dtype=torch.float32, device=x.device)
     assert codes.numel() * codes.element_size() == cb and scales.numel() * scales.element_size() == sb
     dit_quantize_act(fmt, x.data_ptr(), M, K, _ld(x), codes.data_ptr(), scales.data_ptr(), _stream())
@@ -165,7 +166,7 @@ def quantize_act(x, fmt: int):
 def gemm(codes, scales, blob, N: int, K: int, fmt: int, epi: int, rms: RmsNormParams | None = None, out=None):
     """Fused GEMM + epilogue on quantized activations; returns the bf16 output [M, N or N/2]."""
     import torch
-    M = codes.shape[0]
+    M = codes.shape[1]
     width = N // 2 if epi == EPI_GATED_SILU else N
     if out is None:
         out = torch.empty((M, width), dtype=torch.bfloat16, device=codes.device)

@@ -135,7 +135,7 @@ dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const
   }
   if (!shape_ok(FMT_FP4, epi, N, K) || !rows_ok(FMT_FP4, M, K)) return DIT_EUNSUPPORTED;
   const int width = epi == DIT_EPI_GATED_SILU ? N / 2 : N;
-  if (!aligned16(a_codes) || !aligned(a_scales, 8) || !aligned16(w_packed) || !aligned16(out_bf16) ||
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_packed) || !aligned16(out_bf16) ||
       ldo < width || ldo % 8 != 0)
     return DIT_EALIGN;
   if (rms && (!aligned16(rms->gamma_q) || !aligned16(rms->gamma_k))) return DIT_EALIGN;

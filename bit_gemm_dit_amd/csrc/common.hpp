@@ -25,7 +25,7 @@ enum { EPI_IDENTITY = 0, EPI_GATED_SILU = 1, EPI_QK_RMSNORM = 2 };
 
 // ---------------------------------------------------------------- blob layout
 constexpr uint32_t kBlobMagic = 0x51544944u;   // "DITQ"
-constexpr uint32_t kBlobVersion = 1;
+constexpr uint32_t kBlobVersion = 2;
 constexpr int kHeaderBytes = 256;
 constexpr int kRowPad = 256;                   // packed rows are padded to a multiple of this
 

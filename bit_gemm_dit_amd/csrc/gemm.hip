@@ -15,15 +15,18 @@
 //   and a gate row and its up row (interleaved by the packer) meet in the same
 //   lane and register of two adjacent tiles.
 // * FP4: v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands (4 VGPRs) and the
-//   E8M0 block scales applied by the instruction: the scale dword of a lane holds
-//   the scales of its four 64-K steps, picked with op_sel.  FP8: the same
-//   instruction with E4M3 operands (8 VGPRs) and unit block scales; the fp32
-//   row/column scales are applied in the epilogue.
-// * One k-step moves 128 bytes per operand row (FP4: 256 K, FP8: 128 K) through
-//   LDS, double-buffered: global loads of step k+1 are issued before the MFMAs of
-//   step k and written to the other buffer after them; one barrier per step.
-//   Weight tiles are copied verbatim (already in lane order); activation rows are
-//   stored with a 16-byte XOR swizzle so fragment reads are bank-conflict free.
+//   E8M0 block scales applied by the instruction (op_sel picks the byte of the
+//   64-K step).  FP8: the same instruction with E4M3 operands (8 VGPRs) and unit
+//   block scales; the fp32 row/column scales are applied in the epilogue.
+// * A workgroup computes a 256 (features) x 128 (tokens) tile with 4 waves of 128
+//   accumulators each, so two workgroups share a CU: one's epilogue and barrier
+//   waits overlap the other's MFMAs.
+// * K advances in steps of 64 operand bytes per row (FP4: 128 K, FP8: 64 K)
+//   through a 3-stage LDS ring filled by direct-to-LDS buffer loads, two steps
+//   ahead of the MFMAs; one barrier per step.  Each stage also carries the step's
+//   E8M0 scale bytes.  Weight tiles are copied verbatim (the blob is in lane
+//   order); activation rows get a 16-byte XOR swizzle so fragment reads are free
+//   of LDS bank conflicts.
 // * Raw buffer loads return zeros past the end of a tensor, which clips ragged M
 //   without branches; stores are predicated per row.
 // * Workgroups are re-ordered so each XCD (workgroup id mod 8) walks a compact
@@ -33,8 +36,9 @@
 namespace ditq {
 namespace {
 
-constexpr int kRowBytes = 128;   // operand bytes per row per k-step
-constexpr int kGroupM = 4;       // tile-order group height (in M tiles)
+constexpr int kRowBytes = 64;    // operand bytes per row per k-step
+constexpr int kStages = 3;       // LDS ring depth
+constexpr int kGroupM = 8;       // tile-order group height (in M tiles)
 
 template <int FMT_, int EPI_, int WN_, int WM_, int WAVES_N_, int WAVES_M_>
 struct Tile {
@@ -42,15 +46,27 @@ struct Tile {
   static constexpr int WN = WN_, WM = WM_, WAVES_N = WAVES_N_, WAVES_M = WAVES_M_;
   static constexpr int TN = WN / 32, TM = WM / 32;
   static constexpr int BN = WN * WAVES_N, BM = WM * WAVES_M;
-  static constexpr int NT = 64 * WAVES_N * WAVES_M;
-  static constexpr int CH = FMT == FMT_FP4 ? 4 : 2;        // 64-K MFMA steps per k-step
+  static constexpr int NW = WAVES_N * WAVES_M;
+  static constexpr int NT = 64 * NW;
+  static constexpr int CH = FMT == FMT_FP4 ? 2 : 1;         // 64-K MFMA steps per k-step
   static constexpr int KSTEP = 64 * CH;
-  static constexpr int FRAG = FMT == FMT_FP4 ? 1024 : 2048; // bytes of one 32x64 operand fragment
+  static constexpr int FRAG = FMT == FMT_FP4 ? 1024 : 2048;  // bytes of one 32x64 operand fragment
+  static constexpr int GROUP_BYTES = FRAG * CH;              // one 32-row group per k-step (2 KB)
+  // LDS stage: weight codes | activation codes | weight scale records | activation scales
   static constexpr int W_BYTES = BN * kRowBytes, A_BYTES = BM * kRowBytes;
-  static constexpr int STAGE = W_BYTES + A_BYTES;
-  static constexpr int WCH = W_BYTES / 16 / NT, ACH = A_BYTES / 16 / NT;
-  static_assert(W_BYTES % (16 * NT) == 0 && A_BYTES % (16 * NT) == 0, "tile copy must divide evenly");
-  static_assert(FRAG * CH == 4096, "a 32-row group moves 4 KB per k-step");
+  static constexpr int WS_OFF = W_BYTES + A_BYTES;
+  static constexpr int WS_BYTES = FMT == FMT_FP4 ? BN / 32 * 128 : 0;   // 128 B per 32-row group
+  static constexpr int AS_OFF = WS_OFF + WS_BYTES;
+  static constexpr int AS_BYTES = FMT == FMT_FP4 ? BM * 4 : 0;          // 4 B per token
+  static constexpr int STAGE = AS_OFF + AS_BYTES;
+  // direct-to-LDS copies per wave per stage (plus one scale copy on waves 0 and 1 for FP4)
+  static constexpr int WCK = W_BYTES / 1024 / NW;
+  static constexpr int ACK = A_BYTES / 1024 / NW;
+  static constexpr int VMEM_PER_STAGE = WCK + ACK;   // the fewest any wave issues per stage
+  static_assert(W_BYTES % (1024 * NW) == 0 && A_BYTES % (1024 * NW) == 0, "whole 1 KB copies per wave");
+  static_assert(WS_BYTES <= 1024 && AS_BYTES <= 1024, "each scale record set is one copy");
+  static_assert(GROUP_BYTES == 2048, "a 32-row group moves 2 KB per k-step");
+  static_assert(kStages * STAGE * 2 <= 160 * 1024, "two workgroups per CU must fit in LDS");
 };
 
 struct Params {
@@ -68,11 +84,10 @@ struct Params {
   int n_heads;
 };
 
-// Activation LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r is
-// stored at slot c ^ swz(r).  Eight consecutive rows (one 32-bank cycle of a
-// 16-byte read) and sixteen consecutive rows (one 64-bank cycle) both map a fixed
-// logical chunk to distinct banks.
-__device__ __host__ constexpr int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// Activation LDS rows are 64 bytes = 4 chunks of 16 bytes; chunk c of row r is
+// stored at slot c ^ swz(r).  For a fixed logical chunk, rows r..r+7 (one 32-bank
+// cycle of 16-byte reads) and r..r+15 (one 64-bank cycle) land in distinct banks.
+__device__ __host__ constexpr int swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
 __device__ inline void tile_coords(int bid, int total, int tiles_m, int tiles_n, int& tm, int& tn) {
   // workgroup ids are dealt round-robin to the 8 XCDs; give XCD x a contiguous range
@@ -130,6 +145,7 @@ __device__ inline float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+
 // Operand fragments of one 64-K MFMA step: TN weight fragments, TM token fragments.
 template <class T>
 struct Frags {
@@ -138,12 +154,13 @@ struct Frags {
 };
 
 template <class T, int J>
-__device__ __forceinline__ void load_frags(Frags<T>& f, const uint8_t* wb, const uint8_t* ab, int wn, int wm,
-                                           int lane) {
+__device__ __forceinline__ void load_frags(Frags<T>& f, const uint8_t* stage, int wn, int wm, int lane) {
   const int h = lane >> 5, l32 = lane & 31;
+  const uint8_t* wb = stage;
+  const uint8_t* ab = stage + T::W_BYTES;
 #pragma unroll
   for (int tn = 0; tn < T::TN; ++tn) {
-    const uint8_t* fp = wb + ((wn * T::TN + tn) * T::CH + J) * T::FRAG;
+    const uint8_t* fp = wb + (wn * T::TN + tn) * T::GROUP_BYTES + J * T::FRAG;
     if constexpr (T::FMT == FMT_FP4) {
       const v4i x = *reinterpret_cast<const v4i*>(fp + 16 * lane);
       f.w[tn] = __builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1);
@@ -162,7 +179,7 @@ __device__ __forceinline__ void load_frags(Frags<T>& f, const uint8_t* wb, const
       const v4i x = *reinterpret_cast<const v4i*>(row + 16 * (c ^ swz(r)));
       f.a[tm] = __builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1);
     } else {
-      const int c = 4 * J + 2 * h;
+      const int c = 2 * h;
       const v4i x0 = *reinterpret_cast<const v4i*>(row + 16 * (c ^ swz(r)));
       const v4i x1 = *reinterpret_cast<const v4i*>(row + 16 * ((c + 1) ^ swz(r)));
       f.a[tm] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -190,52 +207,51 @@ __device__ __forceinline__ void mfma_frags(v16f (&acc)[T::TN][T::TM], const Frag
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-// Issue order for one 64-K step: the LDS reads of the next step's fragments are
-// spread between this step's MFMAs, so their latency hides behind MFMA work.
+// One k-step from LDS stage `stage`.  FP4: the scale bytes of the step are read
+// from the stage (the weight record's 16-bit word per lane already holds op_sel
+// bytes 0 and 1; activation bytes are picked by lane half), and the fragments of
+// the second 64-K step are read between the first step's MFMAs.
 template <class T>
-__device__ __forceinline__ void interleave_hint(bool next_loads) {
-  constexpr int NMFMA = T::TN * T::TM;
-  constexpr int NDS = (T::TN + T::TM) * (T::FMT == FMT_FP4 ? 1 : 2);
-  if (next_loads) {
+__device__ __forceinline__ void compute_stage(v16f (&acc)[T::TN][T::TM], const uint8_t* stage, int wn, int wm,
+                                              int lane) {
+  uint32_t wsc[T::TN], asc[T::TM];
+  if constexpr (T::FMT == FMT_FP4) {
+    const int l32 = lane & 31;
+    // a token's 4 scale bytes are its blocks 0..3 of the step; this lane's MFMA
+    // steps j = 0, 1 take blocks 2j + h (selector 0x0C gives a zero byte)
+    const uint32_t sel = (lane & 32) ? 0x0C0C0301u : 0x0C0C0200u;
+#pragma unroll
+    for (int tn = 0; tn < T::TN; ++tn)
+      wsc[tn] = *reinterpret_cast<const uint16_t*>(stage + T::WS_OFF + (wn * T::TN + tn) * 128 + 2 * lane);
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm) {
+      const uint32_t d = *reinterpret_cast<const uint32_t*>(stage + T::AS_OFF + 4 * (wm * T::WM + 32 * tm + l32));
+      asc[tm] = __builtin_amdgcn_perm(0u, d, sel);
+    }
+  } else {
+#pragma unroll
+    for (int tn = 0; tn < T::TN; ++tn) wsc[tn] = 0;
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm) asc[tm] = 0;
+  }
+  Frags<T> f0, f1;
+  load_frags<T, 0>(f0, stage, wn, wm, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (T::CH == 2) {
+    load_frags<T, 1>(f1, stage, wn, wm, lane);
+    mfma_frags<T, 0>(acc, f0, wsc, asc);
+    constexpr int NMFMA = T::TN * T::TM;
+    constexpr int NDS = T::TN + T::TM;
 #pragma unroll
     for (int i = 0; i < NDS; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
     if constexpr (NMFMA > NDS) __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - NDS, 0);
-  } else {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA, 0);
-  }
-}
-
-// One k-step: fragments of 64-K step j+1 are read from LDS while the MFMAs of step
-// j run (two register sets, f0 / f1).
-template <class T>
-__device__ __forceinline__ void compute_stage(v16f (&acc)[T::TN][T::TM], const uint8_t* stage, int wn, int wm,
-                                              int lane, const uint32_t* wsc, const uint32_t* asc) {
-  const uint8_t* wb = stage;
-  const uint8_t* ab = stage + T::W_BYTES;
-  Frags<T> f0, f1;
-  load_frags<T, 0>(f0, wb, ab, wn, wm, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  load_frags<T, 1>(f1, wb, ab, wn, wm, lane);
-  mfma_frags<T, 0>(acc, f0, wsc, asc);
-  interleave_hint<T>(true);
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (T::CH == 4) {
-    load_frags<T, 2>(f0, wb, ab, wn, wm, lane);
-    mfma_frags<T, 1>(acc, f1, wsc, asc);
-    interleave_hint<T>(true);
     __builtin_amdgcn_sched_barrier(0);
-    load_frags<T, 3>(f1, wb, ab, wn, wm, lane);
-    mfma_frags<T, 2>(acc, f0, wsc, asc);
-    interleave_hint<T>(true);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_frags<T, 3>(acc, f1, wsc, asc);
-    interleave_hint<T>(false);
-  } else {
     mfma_frags<T, 1>(acc, f1, wsc, asc);
-    interleave_hint<T>(false);
+  } else {
+    mfma_frags<T, 0>(acc, f0, wsc, asc);
   }
 }
 
@@ -368,97 +384,97 @@ __device__ __forceinline__ void pin_accumulators(v16f (&acc)[T::TN][T::TM]) {
 #endif
 }
 
-// N direct-to-LDS copies of 1 KB each: lane L of copy i fetches 16 bytes at
-// voff[i] + soff and the hardware writes them to dst + 1024 i + 16 L.
+// N direct-to-LDS copies of BYTES per lane each: lane L of copy i fetches BYTES at
+// voff[i] + soff and the hardware writes them to dst + 64*BYTES*i + BYTES*L.
 // (A plain device function: inside a lambda the builtin would also be compiled
 // for the host, where it fails and takes the kernel's host stub with it.)
-template <int N>
+template <int N, int BYTES>
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, const uint32_t* voff, int soff,
                                             uint8_t* dst) {
+  static_assert(BYTES == 16 || BYTES == 4, "copy width");
 #pragma unroll
-  for (int i = 0; i < N; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16,
-                                             voff[i], soff, 0, 0);
+  for (int i = 0; i < N; ++i) {
+    auto* d = (__attribute__((address_space(3))) void*)(dst + 64 * BYTES * i);
+    if constexpr (BYTES == 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 16, voff[i], soff, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 4, voff[i], soff, 0, 0);
+  }
 }
 
-// waitcnt immediates (gfx9 encoding: vmcnt[3:0]|expcnt[6:4]|lgkmcnt[11:8]|vmcnt_hi[15:14])
-constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0), others unconstrained
+// s_waitcnt vmcnt(n) with the other counters unconstrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
 
 template <class T>
-__global__ void __launch_bounds__(T::NT) gemm_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * T::STAGE];
-  constexpr int NW = T::NT / 64;
-  constexpr int WCK = T::W_BYTES / 1024 / NW;    // 1 KB LDS chunks per wave per k-step
-  constexpr int ACK = T::A_BYTES / 1024 / NW;
-  static_assert(T::W_BYTES % (1024 * NW) == 0 && T::A_BYTES % (1024 * NW) == 0, "chunks per wave");
+__global__ void __launch_bounds__(T::NT, 2) gemm_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * T::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % T::WAVES_N, wm = wave / T::WAVES_N;
-  const int l32 = lane & 31;
   int tmi, tni;
   tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tmi, tni);
   const int n0 = tni * T::BN, m0 = tmi * T::BM;
   const int nks = p.K / T::KSTEP;
-  const uint32_t arow = T::FMT == FMT_FP4 ? (uint32_t)p.K / 2 : (uint32_t)p.K;
   const uint32_t wgroup = (uint32_t)(p.K / 64) * T::FRAG;
 
   const auto a_rsrc = make_rsrc(p.a_codes, p.a_bytes);
   const auto w_rsrc = make_rsrc(p.w_codes, p.w_bytes);
 
-  // Direct-to-LDS copies: each wave instruction writes 1 KB of LDS, lane L at +16L.
-  // Weight chunk q = 1 KB of row group q/4 (copied verbatim: the blob is in lane
-  // order already).  Activation chunk q = 8 rows of 128 bytes; lane L fetches the
-  // logical 16-byte chunk that the swizzle places at slot L%8 of row 8q + L/8.
-  uint32_t w_off[WCK], a_off[ACK];
+  // Direct-to-LDS copies (each wave instruction writes 64 lanes x 16 bytes = 1 KB):
+  // weight copy q = half of row group q/2 (verbatim: the blob is in lane order);
+  // activation copy q = 16 token rows of the K panel (contiguous 1 KB in the
+  // panel-major layout), lane L fetching the logical chunk that the swizzle
+  // places at slot L%4 of row 16q + L/4.
+  uint32_t w_off[T::WCK], a_off[T::ACK];
 #pragma unroll
-  for (int i = 0; i < WCK; ++i) {
-    const int q = wave * WCK + i;
-    w_off[i] = (uint32_t)(n0 / 32 + (q >> 2)) * wgroup + 1024u * (q & 3) + 16u * lane;
+  for (int i = 0; i < T::WCK; ++i) {
+    const int q = wave * T::WCK + i;
+    w_off[i] = (uint32_t)(n0 / 32 + (q >> 1)) * wgroup + 1024u * (q & 1) + 16u * lane;
   }
 #pragma unroll
-  for (int i = 0; i < ACK; ++i) {
-    const int q = wave * ACK + i;
-    const int r = 8 * q + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    a_off[i] = (uint32_t)(m0 + r) * arow + 16u * c;     // rows >= M lie past the buffer and read as 0
+  for (int i = 0; i < T::ACK; ++i) {
+    const int q = wave * T::ACK + i;
+    const int r = 16 * q + (lane >> 2);
+    const int c = (lane & 3) ^ swz(r);
+    // Rows past M read the next panel's codes (or zeros past the buffer end);
+    // their results are never stored.
+    a_off[i] = (uint32_t)(m0 + r) * kRowBytes + 16u * c;
+  }
+  const uint32_t a_panel = (uint32_t)p.M * kRowBytes;   // bytes of one K panel of the activation codes
+  // FP4 scale copies, one per stage: wave 0 copies the weight scale records of the
+  // block's row groups (1 KB, contiguous for one K step), wave 1 the 4-byte scale
+  // words of the block's tokens (BM * 4 bytes, contiguous in the panel-major layout).
+  [[maybe_unused]] __amdgpu_buffer_rsrc_t s_rsrc;
+  uint32_t s_off[1] = {0};
+  [[maybe_unused]] uint32_t s_step = 0;
+  [[maybe_unused]] bool s_active = false;
+  [[maybe_unused]] int s_dst = 0;
+  if constexpr (T::FMT == FMT_FP4) {
+    if (wave == 0) {
+      s_rsrc = make_rsrc(p.w_scales, p.ws_bytes);
+      s_off[0] = (uint32_t)(n0 / 32) * 128u + 16u * lane;
+      s_step = (uint32_t)(padded_rows(p.N) / 32) * 128u;
+      s_dst = T::WS_OFF;
+      s_active = 16 * lane < T::WS_BYTES;
+    } else if (wave == 1) {
+      s_rsrc = make_rsrc(p.a_scales, p.as_bytes);
+      s_off[0] = (uint32_t)m0 * 4u + 16u * lane;
+      s_step = (uint32_t)p.M * 4u;
+      s_dst = T::AS_OFF;
+      s_active = 16 * lane < T::AS_BYTES;
+    }
   }
 
-  // E8M0 scales (FP4): one dword per weight row tile, 8 bytes per token row.
-  [[maybe_unused]] __amdgpu_buffer_rsrc_t ws_rsrc, as_rsrc;
-  uint32_t ws_off[T::TN], as_off[T::TM];
-  uint32_t wsc[T::TN], asc[T::TM], wsc_n[T::TN];
-  uint32_t asr_lo[T::TM], asr_hi[T::TM];
-  const uint32_t perm_sel = (lane & 32) ? 0x07050301u : 0x06040200u;   // blocks 2j + h, j = 0..3
-  if constexpr (T::FMT == FMT_FP4) {
-    ws_rsrc = make_rsrc(p.w_scales, p.ws_bytes);
-    as_rsrc = make_rsrc(p.a_scales, p.as_bytes);
-#pragma unroll
-    for (int tn = 0; tn < T::TN; ++tn)
-      ws_off[tn] = (uint32_t)(n0 / 32 + wn * T::TN + tn) * (uint32_t)(p.K / 256) * 256u + 4u * lane;
-#pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm)
-      as_off[tm] = (uint32_t)(m0 + wm * T::WM + 32 * tm + l32) * (uint32_t)(p.K / 32);
-  }
-  auto issue_loads = [&](int ks, int buf) {
+  auto issue_stage = [&](int ks) {
+    uint8_t* base = lds + (ks % kStages) * T::STAGE;
+    copy_to_lds<T::WCK, 16>(w_rsrc, w_off, ks * T::GROUP_BYTES, base + wave * T::WCK * 1024);
+    copy_to_lds<T::ACK, 16>(a_rsrc, a_off, ks * a_panel, base + T::W_BYTES + wave * T::ACK * 1024);
     if constexpr (T::FMT == FMT_FP4) {
-#pragma unroll
-      for (int tn = 0; tn < T::TN; ++tn)
-        wsc_n[tn] = __builtin_amdgcn_raw_buffer_load_b32(ws_rsrc, ws_off[tn], ks * 256, 0);
-#pragma unroll
-      for (int tm = 0; tm < T::TM; ++tm) {
-        const auto d = __builtin_amdgcn_raw_buffer_load_b64(as_rsrc, as_off[tm], ks * 8, 0);
-        asr_lo[tm] = d[0];
-        asr_hi[tm] = d[1];
-      }
-    }
-    copy_to_lds<WCK>(w_rsrc, w_off, ks * 4096, lds + buf * T::STAGE + wave * WCK * 1024);
-    copy_to_lds<ACK>(a_rsrc, a_off, ks * kRowBytes, lds + buf * T::STAGE + T::W_BYTES + wave * ACK * 1024);
-  };
-  auto take_scales = [&]() {
-    if constexpr (T::FMT == FMT_FP4) {
-#pragma unroll
-      for (int tn = 0; tn < T::TN; ++tn) wsc[tn] = wsc_n[tn];
-#pragma unroll
-      for (int tm = 0; tm < T::TM; ++tm) asc[tm] = __builtin_amdgcn_perm(asr_hi[tm], asr_lo[tm], perm_sel);
+      if (s_active) copy_to_lds<1, 16>(s_rsrc, s_off, ks * s_step, base + s_dst);
     }
   };
 
@@ -468,22 +484,20 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(Params p) {
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) acc[tn][tm] = v16f{};
 
-  issue_loads(0, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  take_scales();
-  __syncthreads();
+  issue_stage(0);
+  if (nks > 1) issue_stage(1);
   for (int ks = 0; ks < nks; ++ks) {
-    const int cur = ks & 1;
-    const bool more = ks + 1 < nks;
-    // the other buffer was last read in step ks-1, which every wave finished before the barrier
-    if (more) issue_loads(ks + 1, cur ^ 1);
+    // stage ks has landed once at most the next stage's copies are still in flight
+    if (ks + 1 < nks)
+      wait_vmcnt<T::VMEM_PER_STAGE>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();              // every wave's copies of stage ks are visible, and stage ks-1 is free
+    if (ks + 2 < nks) issue_stage(ks + 2);   // overwrites the stage read in step ks-1
     __builtin_amdgcn_sched_barrier(0);
-    compute_stage<T>(acc, lds + cur * T::STAGE, wn, wm, lane, wsc, asc);
+    compute_stage<T>(acc, lds + (ks % kStages) * T::STAGE, wn, wm, lane);
     pin_accumulators<T>(acc);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);       // this wave's copies into the other buffer have landed
-    if (more) take_scales();
-    __syncthreads();                            // ... and every other wave's; all reads of `cur` are done
   }
   epilogue<T>(p, acc, n0 + wn * T::WN, m0 + wm * T::WM, lane);
 }
@@ -524,24 +538,24 @@ hipError_t launch_gemm_fp4(const uint8_t* a_codes, const uint8_t* a_scales, cons
   Params p = make_params(a_codes, a_scales, blob, FMT_FP4, M, N, K, out, ldo);
   switch (epi) {
     case EPI_IDENTITY:
-      return launch<Tile<FMT_FP4, EPI_IDENTITY, 128, 128, 2, 2>>(p, stream);
+      return launch<Tile<FMT_FP4, EPI_IDENTITY, 128, 64, 2, 2>>(p, stream);
     case EPI_GATED_SILU:
-      return launch<Tile<FMT_FP4, EPI_GATED_SILU, 128, 128, 2, 2>>(p, stream);
+      return launch<Tile<FMT_FP4, EPI_GATED_SILU, 128, 64, 2, 2>>(p, stream);
     default:
       p.gamma_q = rms->gamma_q;
       p.gamma_k = rms->gamma_k;
       p.eps = rms->eps;
       p.n_heads = rms->n_heads;
-      if (rms->head_dim == 128) return launch<Tile<FMT_FP4, EPI_QK_RMSNORM, 128, 128, 2, 2>>(p, stream);
-      return launch<Tile<FMT_FP4, EPI_QK_RMSNORM, 256, 64, 1, 4>>(p, stream);
+      if (rms->head_dim == 128) return launch<Tile<FMT_FP4, EPI_QK_RMSNORM, 128, 64, 2, 2>>(p, stream);
+      return launch<Tile<FMT_FP4, EPI_QK_RMSNORM, 256, 32, 1, 4>>(p, stream);
   }
 }
 
 hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scales, const uint8_t* blob, int M, int N,
                            int K, int epi, uint16_t* out, int ldo, hipStream_t stream) {
   Params p = make_params(a_codes, a_scales, blob, FMT_FP8, M, N, K, out, ldo);
-  if (epi == EPI_GATED_SILU) return launch<Tile<FMT_FP8, EPI_GATED_SILU, 128, 128, 2, 2>>(p, stream);
-  return launch<Tile<FMT_FP8, EPI_IDENTITY, 128, 128, 2, 2>>(p, stream);
+  if (epi == EPI_GATED_SILU) return launch<Tile<FMT_FP8, EPI_GATED_SILU, 128, 64, 2, 2>>(p, stream);
+  return launch<Tile<FMT_FP8, EPI_IDENTITY, 128, 64, 2, 2>>(p, stream);
 }
 
 }  // namespace ditq

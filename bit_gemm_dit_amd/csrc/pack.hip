@@ -56,9 +56,9 @@ __global__ __launch_bounds__(256) void pack_fp4_kernel(const uint16_t* __restric
     out.w = (int)fp4_encode8(v3, byte);
   }
   *reinterpret_cast<v4i*>(blob + kHeaderBytes + (size_t)frag * 1024 + 16 * L) = out;
-  // scale group (g, s = c / 4), byte 4L + j with j = c % 4: block 8s + 2j + L/32 == 2c + L/32
+  // scale record (s = c / 2, g), byte 2L + j with j = c % 2: block 4s + 2j + L/32 == 2c + L/32
   uint8_t* sc = blob + blob_scales_offset(FMT_FP4, Np, K);
-  sc[((size_t)g * (K / 256) + c / 4) * 256 + 4 * L + (c & 3)] = (uint8_t)byte;
+  sc[((size_t)(c / 2) * (Np / 32) + g) * 128 + 2 * L + (c & 1)] = (uint8_t)byte;
 }
 
 // FP8: one wave per packed row.  Pass 1 finds the row's amax (-> s_w), pass 2

@@ -1,16 +1,18 @@
 // On-the-fly activation quantizers (gfx950).
 //
-// FP4: bf16 [M, K] -> E2M1 codes [M][K/2] + E8M0 scales [M][K/32].  Activation
+// FP4: bf16 [M, K] -> E2M1 codes + E8M0 block scales, K-panel-major.  Activation
 // statistics change from one diffusion iteration to the next, so the scales are
 // computed from the data on every call rather than calibrated once (page
 // "Versnellende diffusiemodellen met TheStage AI", section on acceleration and
 // compression); the 4-bit float format is that of page "How fal made Ideogram V4
 // 6x faster", paragraph 2.
-// FP8: bf16 [M, K] -> E4M3 codes [M][K] + fp32 row scales [M] (page "WaveSpeedAI
+// FP8: bf16 [M, K] -> E4M3 codes (K-panel-major) + fp32 row scales [M] (page "WaveSpeedAI
 // X DataCrunch", engine list: FP8 mixed precision).
 //
 // Both kernels are HBM-bound streams: 2 bytes read per element, 0.5 + 1/32 (FP4)
-// or 1 (FP8) byte written.  Every wave instruction touches contiguous memory.
+// or 1 (FP8) byte written.  Outputs are K-panel-major (include/ditq.h): the GEMM
+// then copies each 64-byte-per-token panel slice of a token tile as one
+// contiguous run.
 #include "common.hpp"
 
 namespace ditq {
@@ -23,8 +25,10 @@ constexpr int kQuadXor2 = 0x4E;
 // One thread per 8 consecutive elements (16 bytes of bf16); the four threads of a
 // DPP quad cover one 32-element block and agree on its scale.  Grid-stride over
 // all chunks; the chunk count and the stride are multiples of 4, so quads are
-// always fully active together.
-__global__ __launch_bounds__(256) void quant_fp4_kernel(const uint16_t* __restrict__ x, int ldx,
+// always fully active together.  Chunk `col` of a row sits in K panel col/16
+// (128 elements per panel): codes at byte 4*(col%16) of the token's 64-byte panel
+// row, the block scale at byte (col/4)%4 of its 4-byte panel row.
+__global__ __launch_bounds__(256) void quant_fp4_kernel(const uint16_t* __restrict__ x, int M, int ldx,
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales, uint32_t total,
                                                         uint32_t per_row) {
@@ -36,8 +40,9 @@ __global__ __launch_bounds__(256) void quant_fp4_kernel(const uint16_t* __restri
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kQuadXor1, 0xF, 0xF, false));
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kQuadXor2, 0xF, 0xF, false));
     const uint32_t byte = fp4_scale_byte(m);
-    reinterpret_cast<uint32_t*>(codes)[c] = fp4_encode8(v, byte);   // codes are dense: chunk c -> bytes 4c..4c+3
-    if ((threadIdx.x & 3) == 0) scales[c >> 2] = (uint8_t)byte;
+    const size_t prow = (size_t)(col >> 4) * M + row;              // panel-major row index
+    *reinterpret_cast<uint32_t*>(codes + prow * 64 + 4 * (col & 15)) = fp4_encode8(v, byte);
+    if ((threadIdx.x & 3) == 0) scales[prow * 4 + ((col >> 2) & 3)] = (uint8_t)byte;
   }
 }
 
@@ -53,7 +58,8 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;                                   // uniform per wave
   const uint16_t* xr = x + (size_t)row * ldx;
-  uint8_t* cr = codes + (size_t)row * K;
+  // element k lands in K panel k/64 (64 elements per panel), byte k%64 of the token's panel row
+  auto dst = [&](int k) { return codes + ((size_t)(k >> 6) * M + row) * 64 + (k & 63); };
   const int nch = (K + 511) / 512;
   uint32_t m = 0;
   v4i cache[CACHED ? kMaxCached : 1];
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
         uint2 q;
         q.x = fp8_encode4((uint32_t)v.x, (uint32_t)v.y, s);
         q.y = fp8_encode4((uint32_t)v.z, (uint32_t)v.w, s);
-        *reinterpret_cast<uint2*>(cr + k) = q;
+        *reinterpret_cast<uint2*>(dst(k)) = q;
       }
     }
   } else {
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
         uint2 q;
         q.x = fp8_encode4((uint32_t)v.x, (uint32_t)v.y, s);
         q.y = fp8_encode4((uint32_t)v.z, (uint32_t)v.w, s);
-        *reinterpret_cast<uint2*>(cr + k) = q;
+        *reinterpret_cast<uint2*>(dst(k)) = q;
       }
     }
   }
@@ -112,7 +118,7 @@ hipError_t launch_quant_fp4(const uint16_t* x, int M, int K, int ldx, uint8_t* c
   uint32_t blocks = (total + 255) / 256;
   const uint32_t cap = 256u * 32u;                        // 256 CUs x 32 blocks of 4 waves
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(quant_fp4_kernel, dim3(blocks), dim3(256), 0, stream, x, ldx, codes, scales, total,
+  hipLaunchKernelGGL(quant_fp4_kernel, dim3(blocks), dim3(256), 0, stream, x, M, ldx, codes, scales, total,
                      per_row);
   return hipGetLastError();
 }

@@ -102,7 +102,7 @@ size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
  * RNE_E4M3(fl32(w / s_w[n])).
  *
  * Blob layout (little-endian; the GEMM relies on it, tests decode it):
- *   header, 256 bytes: u32 magic 0x51544944 ("DITQ"), u32 layout version 1,
+ *   header, 256 bytes: u32 magic 0x51544944 ("DITQ"), u32 layout version 2,
  *     u32 fmt, u32 epi, u32 N, u32 K, u32 Np, u32 0, u64 codes offset (256),
  *     u64 scales offset, u64 total bytes, then zeros.
  *   packed row p (0 <= p < Np) holds logical weight row perm(p): identity for
@@ -115,11 +115,11 @@ size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
  *     256 + (g*K/64 + c)*1024; its byte 16*L + b (lane L < 64, b < 16) holds
  *     the codes of packed row 32g + L%32 at k = 64c + 32*(L/32) + 2b (low
  *     nibble) and k + 1 (high nibble).
- *   FP4 scales: 256-byte groups (g, s), s < K/256, at
- *     scales offset + (g*K/256 + s)*256; byte 4*L + j is the E8M0 scale of
- *     packed row 32g + L%32 for the 32-element K block 8s + 2j + L/32 (so the
- *     dword of lane L serves its four 64-K MFMA steps through the op_sel byte
- *     select).
+ *   FP4 scales: 128-byte records (s, g), s < K/128 (a 128-element K step),
+ *     g < Np/32, at scales offset + (s*Np/32 + g)*128; byte 2*L + j is the E8M0
+ *     scale of packed row 32g + L%32 for the 32-element K block 4s + 2j + L/32
+ *     (the 16-bit word of lane L holds the scales of its two 64-K MFMA steps,
+ *     picked with op_sel), so one K step of 256 packed rows is 1 KB contiguous.
  *   FP8 codes: 2048-byte fragments (g, c) at 256 + (g*K/64 + c)*2048; byte
  *     32*L + b holds the E4M3 code of packed row 32g + L%32 at
  *     k = 64c + 32*(L/32) + b.
@@ -141,10 +141,16 @@ dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N,
  *   scale byte = clamp(floor(log2 amax) - 2 + 127, 0, 254), 0 if amax == 0;
  *   code = sign(x) | RNE_E2M1(min(|x| / 2^(byte-127), 6)), the sign bit copied
  *   from x even when the magnitude rounds to 0.
- *   codes: u8 [M][K/2], even k in the low nibble; scales: u8 E8M0 [M][K/32].
+ *   Layout (K-panel-major, so that the GEMM copies a token tile of one K panel as
+ *   one contiguous run): panel s = k / 128.  Codes: byte (s*M + m)*64 + (k%128)/2
+ *   holds token m's codes at k (low nibble, k even) and k + 1 (high nibble).
+ *   Scales: byte (s*M + m)*4 + (k%128)/32 is the E8M0 scale of token m's block
+ *   k/32.  (Sizes M*K/2 and M*K/32 bytes.)
  * FP8:
  *   per row: s = fl32(amax / 448) (1 if the row is zero); code =
- *   RNE_E4M3(fl32(x / s)), both divisions IEEE fp32; codes u8 [M][K]; scales fp32 [M].
+ *   RNE_E4M3(fl32(x / s)), both divisions IEEE fp32.  Codes K-panel-major with
+ *   64-element panels: byte (s*M + m)*64 + k%64, s = k / 64, holds token m's code
+ *   at k; scales fp32 [M].
  *
  * Supported: K % 256 == 0, ldx >= K, ldx % 8 == 0, pointers 16-byte aligned
  * (FP4 scales: any alignment).  x must be finite. */
@@ -152,8 +158,8 @@ dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int l
                             void* codes, void* scales, void* stream);
 
 /* ---------------------------------------------------------------- fused GEMM + epilogue, FP4
- * out = epi(A W^T) with A the FP4 activations from dit_quantize_act
- * (a_codes [M][K/2], a_scales [M][K/32]) and W the blob from dit_pack_weights
+ * out = epi(A W^T) with A the FP4 activations from dit_quantize_act (a_codes,
+ * a_scales in its K-panel-major layout) and W the blob from dit_pack_weights
  * (FP4, packed for the same epi family).  The fp32 accumulator goes through the
  * epilogue and is stored once as bf16 (round to nearest even) into out_bf16
  * [M][ldo]; the output width is N/2 for GATED_SILU and N otherwise.
@@ -161,14 +167,14 @@ dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int l
  * the struct; the gammas inside are device pointers), with
  * N == 3 * n_heads * head_dim and head_dim in {128, 256}.
  * Supported: M >= 1 (any), K % 256 == 0, N % 64 == 0 (GATED_SILU: N % 128 == 0),
- * ldo >= output width, ldo % 8 == 0, pointers 16-byte aligned (a_scales: 8). */
+ * ldo >= output width, ldo % 8 == 0, pointers 16-byte aligned. */
 dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const void* w_packed,
                                 int M, int N, int K, dit_epi epi, const dit_rmsnorm_params* rms,
                                 void* out_bf16, int ldo, void* stream);
 
 /* ---------------------------------------------------------------- fused GEMM + epilogue, FP8
- * out = epi((A W^T) * s_a[m] * s_w[n]) with A the E4M3 codes [M][K] and fp32
- * row scales [M] from dit_quantize_act, W an FP8 blob.  epi is IDENTITY or
+ * out = epi((A W^T) * s_a[m] * s_w[n]) with A the E4M3 codes (K-panel-major) and
+ * fp32 row scales [M] from dit_quantize_act, W an FP8 blob.  epi is IDENTITY or
  * GATED_SILU (QK_RMSNORM returns DIT_EUNSUPPORTED).  Same shape rules as the FP4
  * entry point (a_scales 4-byte aligned). */
 dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, const void* w_packed,

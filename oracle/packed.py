@@ -7,7 +7,7 @@ quantizer applied to the same weights.  It shares no code with the packer.
 
 Layout (all offsets in bytes, little-endian):
 
-* header, 256 bytes: u32 magic 0x51544944 ("DITQ"), u32 layout version (1),
+* header, 256 bytes: u32 magic 0x51544944 ("DITQ"), u32 layout version (2),
   u32 fmt, u32 epi, u32 N, u32 K, u32 Np (N rounded up to 256), u32 0,
   u64 codes offset (256), u64 scales offset, u64 total bytes, zeros.
 * packed row p (0 <= p < Np) holds logical weight row perm(p):
@@ -19,9 +19,9 @@ Layout (all offsets in bytes, little-endian):
   K chunk c < K/64 at codes_offset + (g * K/64 + c) * 1024; byte 16*L + b
   (lane L < 64, b < 16) holds the codes of packed row 32g + L%32 at
   k = 64c + 32(L//32) + 2b (low nibble) and k + 1 (high nibble).
-* FP4 scales: 256-byte groups, group (g, s) for s < K/256 at
-  scales_offset + (g * K/256 + s) * 256; byte 4*L + j holds the E8M0 scale of
-  packed row 32g + L%32 for the 32-element K block 8s + 2j + L//32.
+* FP4 scales: 128-byte records, record (s, g) for K step s < K/128 and row
+  group g < Np/32 at scales_offset + (s * Np/32 + g) * 128; byte 2*L + j holds the
+  E8M0 scale of packed row 32g + L%32 for the 32-element K block 4s + 2j + L//32.
 * FP8 codes: 2048-byte fragments, fragment (g, c) at codes_offset +
   (g * K/64 + c) * 2048; byte 32*L + b holds the E4M3 code of packed row
   32g + L%32 at k = 64c + 32(L//32) + b.
@@ -81,13 +81,13 @@ def decode(blob: np.ndarray, fmt: int, epi: int, N: int, K: int):
             for c in range(K // 64):
                 rows[r, c * 32 + col0:c * 32 + col0 + 16] = frag[:, c, L, :]
         sbytes = Np * K // 32
-        sg = b[HEADER + cbytes:HEADER + cbytes + sbytes].reshape(G, K // 256, 64, 4)   # [g][s][L][j]
+        sg = b[HEADER + cbytes:HEADER + cbytes + sbytes].reshape(K // 128, G, 64, 2)   # [s][g][L][j]
         sc = np.empty((Np, K // 32), dtype=np.uint8)
         for L in range(64):
             r = np.arange(G) * 32 + L % 32
-            for s in range(K // 256):
-                for j in range(4):
-                    sc[r, 8 * s + 2 * j + L // 32] = sg[:, s, L, j]
+            for s in range(K // 128):
+                for j in range(2):
+                    sc[r, 4 * s + 2 * j + L // 32] = sg[s, :, L, j]
     elif fmt == FMT_FP8:
         cbytes = Np * K
         frag = b[HEADER:HEADER + cbytes].reshape(G, K // 64, 64, 32)

@@ -22,6 +22,23 @@ def to_host_bits(t) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def act_codes_to_rowmajor(codes: np.ndarray, M: int, K: int, fmt: int) -> np.ndarray:
+    """dit_quantize_act's K-panel-major codes -> row-major (FP4 [M, K/2], FP8 [M, K]).
+
+    Follows the layout include/ditq.h documents: FP4 panels of 128 K elements
+    (64 bytes per token), FP8 panels of 64 elements (64 bytes per token).
+    """
+    c = np.asarray(codes, dtype=np.uint8).reshape(-1)
+    panels = (K // 128) if fmt == 1 else (K // 64)
+    return c.reshape(panels, M, 64).transpose(1, 0, 2).reshape(M, panels * 64)
+
+
+def act_scales_to_rowmajor(scales: np.ndarray, M: int, K: int) -> np.ndarray:
+    """FP4 scale bytes, [K/128][M][4] -> [M, K/32] (block b of token m)."""
+    s = np.asarray(scales, dtype=np.uint8).reshape(-1)
+    return s.reshape(K // 128, M, 4).transpose(1, 0, 2).reshape(M, K // 32)
+
+
 def half_ulp_bf16(y: np.ndarray) -> np.ndarray:
     a = np.abs(y)
     e = np.floor(np.log2(np.where(a > 0, a, 1.0)))

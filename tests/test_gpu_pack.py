@@ -39,7 +39,7 @@ def test_fp4_pack_bitexact(ditq, N, K, epi, ldw):
     d = make_inputs("qkv_rmsnorm_hd128", seed=N, M=1, N=N, K=K)
     blob = _pack(ditq, d["w"], 1, epi, ldw)
     hdr = packed.read_header(blob)
-    assert (hdr["magic"], hdr["version"], hdr["fmt"], hdr["epi"], hdr["N"], hdr["K"]) == (packed.MAGIC, 1, 1, epi, N, K)
+    assert (hdr["magic"], hdr["version"], hdr["fmt"], hdr["epi"], hdr["N"], hdr["K"]) == (packed.MAGIC, 2, 1, epi, N, K)
     assert hdr["total"] == blob.size
     c, s, pad = packed.decode(blob, 1, epi, N, K)
     rc, rs = quant.quantize_fp4(d["w"])

@@ -30,7 +30,9 @@ def _run_fp4(ditq, bits, ldx=None):
     ditq.dit_quantize_act(ditq.FMT_FP4, x.data_ptr(), M, K, ldx, codes.data_ptr(), scales.data_ptr(),
                           torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    return codes.cpu().numpy(), scales.cpu().numpy()
+    from tests.gpu_util import act_codes_to_rowmajor, act_scales_to_rowmajor
+    return (act_codes_to_rowmajor(codes.cpu().numpy(), M, K, 1),
+            act_scales_to_rowmajor(scales.cpu().numpy(), M, K))
 
 
 def _special_rows(rng, M, K):
@@ -102,7 +104,8 @@ def _run_fp8(ditq, bits, ldx=None):
     ditq.dit_quantize_act(ditq.FMT_FP8, x.data_ptr(), M, K, ldx, codes.data_ptr(), scales.data_ptr(),
                           torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    return codes.cpu().numpy(), scales.cpu().numpy()
+    from tests.gpu_util import act_codes_to_rowmajor
+    return act_codes_to_rowmajor(codes.cpu().numpy(), M, K, 2), scales.cpu().numpy()
 
 
 @pytest.mark.parametrize("M,K,ldx", [(1, 256, 256), (77, 3072, 3080), (33, 8448, 8448), (5, 768, 768)])

@@ -17,7 +17,7 @@ def _write_blob(codes, scales, fmt, epi, N, K):
         cbytes, sbytes = Np * K, Np * 4
     blob = np.zeros(packed.HEADER + cbytes + sbytes, dtype=np.uint8)
     hdr = np.zeros(64, dtype=np.uint8)
-    hdr[:28] = np.array([packed.MAGIC, 1, fmt, epi, N, K, Np], dtype=np.uint32).view(np.uint8)
+    hdr[:28] = np.array([packed.MAGIC, 2, fmt, epi, N, K, Np], dtype=np.uint32).view(np.uint8)
     hdr[32:56] = np.array([256, 256 + cbytes, blob.size], dtype=np.uint64).view(np.uint8)
     blob[:64] = hdr
     for p in range(Np):
@@ -32,10 +32,10 @@ def _write_blob(codes, scales, fmt, epi, N, K):
                 b = (within % 32) // 2
                 blob[256 + (g * (K // 64) + c) * 1024 + 16 * L + b] = codes[n, k // 2]
             for blk in range(K // 32):
-                s, r = blk // 8, blk % 8
+                s, r = blk // 4, blk % 4
                 j, half = r // 2, r % 2
                 L = lane_lo + 32 * half
-                blob[256 + cbytes + (g * (K // 256) + s) * 256 + 4 * L + j] = scales[n, blk]
+                blob[256 + cbytes + (s * (Np // 32) + g) * 128 + 2 * L + j] = scales[n, blk]
         else:
             for k in range(K):
                 c, within = k // 64, k % 64
