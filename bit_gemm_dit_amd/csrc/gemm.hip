@@ -18,11 +18,12 @@
 //   E8M0 block scales applied by the instruction (op_sel picks the byte of the
 //   64-K step).  FP8: the same instruction with E4M3 operands (8 VGPRs) and unit
 //   block scales; the fp32 row/column scales are applied in the epilogue.
-// * A workgroup computes a 256 (features) x 128 (tokens) tile with 4 waves of 128
-//   accumulators each, so two workgroups share a CU: one's epilogue and barrier
-//   waits overlap the other's MFMAs.
+// * A workgroup computes a 256 (features) x 256 (tokens) tile with 8 waves (two per
+//   SIMD, 128 accumulators each).  The large tile keeps the L2 -> LDS traffic at
+//   about half of what the CU's load path can move while the MFMAs run at full
+//   rate; two waves per SIMD let one wave's LDS waits overlap the other's MFMAs.
 // * K advances in steps of 64 operand bytes per row (FP4: 128 K, FP8: 64 K)
-//   through a 3-stage LDS ring filled by direct-to-LDS buffer loads, two steps
+//   through a 4-stage LDS ring filled by direct-to-LDS buffer loads, three steps
 //   ahead of the MFMAs; one barrier per step.  Each stage also carries the step's
 //   E8M0 scale bytes.  Weight tiles are copied verbatim (the blob is in lane
 //   order); activation rows get a 16-byte XOR swizzle so fragment reads are free
@@ -37,8 +38,8 @@ namespace ditq {
 namespace {
 
 constexpr int kRowBytes = 64;    // operand bytes per row per k-step
-constexpr int kStages = 3;       // LDS ring depth
-constexpr int kGroupM = 8;       // tile-order group height (in M tiles)
+constexpr int kStages = 4;       // LDS ring depth
+constexpr int kGroupM = 4;       // tile-order group height (in M tiles)
 
 template <int FMT_, int EPI_, int WN_, int WM_, int WAVES_N_, int WAVES_M_>
 struct Tile {
@@ -66,7 +67,8 @@ struct Tile {
   static_assert(W_BYTES % (1024 * NW) == 0 && A_BYTES % (1024 * NW) == 0, "whole 1 KB copies per wave");
   static_assert(WS_BYTES <= 1024 && AS_BYTES <= 1024, "each scale record set is one copy");
   static_assert(GROUP_BYTES == 2048, "a 32-row group moves 2 KB per k-step");
-  static_assert(kStages * STAGE * 2 <= 160 * 1024, "two workgroups per CU must fit in LDS");
+  static_assert(kStages * STAGE <= 160 * 1024, "the LDS ring must fit in a CU's LDS");
+  static_assert(NW % 4 == 0, "whole waves per SIMD");
 };
 
 struct Params {
@@ -187,72 +189,77 @@ __device__ __forceinline__ void load_frags(Frags<T>& f, const uint8_t* stage, in
   }
 }
 
-template <class T, int J>
-__device__ __forceinline__ void mfma_frags(v16f (&acc)[T::TN][T::TM], const Frags<T>& f, const uint32_t* wsc,
-                                           const uint32_t* asc) {
+// sched_group_barrier masks
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Scale words of one k-step (FP4): the weight record's 16-bit word per lane holds
+// op_sel bytes 0 and 1; a token's 4 scale bytes are its blocks 0..3 of the step,
+// and this lane's MFMA steps j = 0, 1 take blocks 2j + h (selector byte 0x0C
+// gives a zero byte).
+template <class T>
+struct Scales {
+  uint32_t w[T::TN];
+  uint32_t a[T::TM];
+};
+
+// Raw scale words of a stage (the activation bytes are selected later, once the
+// LDS reads have landed, so that no MFMA waits on them).
+template <class T>
+__device__ __forceinline__ void load_scales(Scales<T>& sc, const uint8_t* stage, int wn, int wm, int lane) {
+  if constexpr (T::FMT == FMT_FP4) {
+    const int l32 = lane & 31;
+#pragma unroll
+    for (int tn = 0; tn < T::TN; ++tn)
+      sc.w[tn] = *reinterpret_cast<const uint16_t*>(stage + T::WS_OFF + (wn * T::TN + tn) * 128 + 2 * lane);
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm)
+      sc.a[tm] = *reinterpret_cast<const uint32_t*>(stage + T::AS_OFF + 4 * (wm * T::WM + 32 * tm + l32));
+  } else {
+#pragma unroll
+    for (int tn = 0; tn < T::TN; ++tn) sc.w[tn] = 0;
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm) sc.a[tm] = 0;
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void select_scales(Scales<T>& sc, int lane) {
+  if constexpr (T::FMT == FMT_FP4) {
+    const uint32_t sel = (lane & 32) ? 0x0C0C0301u : 0x0C0C0200u;
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm) sc.a[tm] = __builtin_amdgcn_perm(0u, sc.a[tm], sel);
+  }
+}
+
+// MFMAs of 64-K step J over token tiles [TM0, TM1), with the LDS reads that are
+// issued in the same region spread between them.
+template <class T, int J, int TM0, int TM1>
+__device__ __forceinline__ void mfma_part(v16f (&acc)[T::TN][T::TM], const Frags<T>& f, const Scales<T>& sc) {
 #pragma unroll
   for (int tn = 0; tn < T::TN; ++tn)
 #pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm) {
+    for (int tm = TM0; tm < TM1; ++tm) {
       if constexpr (T::FMT == FMT_FP4)
         acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[tn], f.a[tm], acc[tn][tm], 4, 4, J,
-                                                                      (int)wsc[tn], J, (int)asc[tm]);
+                                                                      (int)sc.w[tn], J, (int)sc.a[tm]);
       else
         acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[tn], f.a[tm], acc[tn][tm], 0, 0, 0,
                                                                       0x7F7F7F7F, 0, 0x7F7F7F7F);
     }
 }
 
-// sched_group_barrier masks
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-
-// One k-step from LDS stage `stage`.  FP4: the scale bytes of the step are read
-// from the stage (the weight record's 16-bit word per lane already holds op_sel
-// bytes 0 and 1; activation bytes are picked by lane half), and the fragments of
-// the second 64-K step are read between the first step's MFMAs.
-template <class T>
-__device__ __forceinline__ void compute_stage(v16f (&acc)[T::TN][T::TM], const uint8_t* stage, int wn, int wm,
-                                              int lane) {
-  uint32_t wsc[T::TN], asc[T::TM];
-  if constexpr (T::FMT == FMT_FP4) {
-    const int l32 = lane & 31;
-    // a token's 4 scale bytes are its blocks 0..3 of the step; this lane's MFMA
-    // steps j = 0, 1 take blocks 2j + h (selector 0x0C gives a zero byte)
-    const uint32_t sel = (lane & 32) ? 0x0C0C0301u : 0x0C0C0200u;
+// Spread NDS LDS reads between NMFMA MFMAs of the current scheduling region.
+template <int NMFMA, int NDS>
+__device__ __forceinline__ void interleave() {
+  constexpr int pairs = NDS < NMFMA ? NDS : NMFMA;
 #pragma unroll
-    for (int tn = 0; tn < T::TN; ++tn)
-      wsc[tn] = *reinterpret_cast<const uint16_t*>(stage + T::WS_OFF + (wn * T::TN + tn) * 128 + 2 * lane);
-#pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm) {
-      const uint32_t d = *reinterpret_cast<const uint32_t*>(stage + T::AS_OFF + 4 * (wm * T::WM + 32 * tm + l32));
-      asc[tm] = __builtin_amdgcn_perm(0u, d, sel);
-    }
-  } else {
-#pragma unroll
-    for (int tn = 0; tn < T::TN; ++tn) wsc[tn] = 0;
-#pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm) asc[tm] = 0;
+  for (int i = 0; i < pairs; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
   }
-  Frags<T> f0, f1;
-  load_frags<T, 0>(f0, stage, wn, wm, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (T::CH == 2) {
-    load_frags<T, 1>(f1, stage, wn, wm, lane);
-    mfma_frags<T, 0>(acc, f0, wsc, asc);
-    constexpr int NMFMA = T::TN * T::TM;
-    constexpr int NDS = T::TN + T::TM;
-#pragma unroll
-    for (int i = 0; i < NDS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    if constexpr (NMFMA > NDS) __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - NDS, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_frags<T, 1>(acc, f1, wsc, asc);
-  } else {
-    mfma_frags<T, 0>(acc, f0, wsc, asc);
-  }
+  if constexpr (NMFMA > pairs) __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - pairs, 0);
+  if constexpr (NDS > pairs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NDS - pairs, 0);
 }
 
 // ---------------------------------------------------------------- epilogues
@@ -411,9 +418,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <class T>
-__global__ void __launch_bounds__(T::NT, 2) gemm_kernel(Params p) {
+__global__ void __launch_bounds__(T::NT, T::NW / 4) gemm_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * T::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // readfirstlane: the wave index is uniform, and the compiler must know it (a
+  // per-wave buffer descriptor would otherwise become a loop over lanes)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % T::WAVES_N, wm = wave / T::WAVES_N;
   int tmi, tni;
   tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tmi, tni);
@@ -484,21 +493,65 @@ __global__ void __launch_bounds__(T::NT, 2) gemm_kernel(Params p) {
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) acc[tn][tm] = v16f{};
 
-  issue_stage(0);
-  if (nks > 1) issue_stage(1);
+  // Pipeline.  Step ks computes from ring slot ks % kStages.  The barrier of step ks
+  // sits between its two halves of MFMAs: before it the wave has issued the first
+  // half (which keeps the MFMA pipe busy through the wait), after it stage ks+1 is
+  // visible to every wave and slot ks % kStages is free, so the copy of stage
+  // ks + kStages goes there and the next stage's first fragments are read while
+  // the second half of the MFMAs runs.  Copies are issued for every step up to
+  // nks + kStages - 1: those past the end of K read zeros or unused rows (the
+  // buffer descriptors bound every read) into slots that are no longer read,
+  // which keeps the wait counts constant and the loop body free of branches.
+  auto stage_ptr = [&](int ks) { return lds + (ks % kStages) * T::STAGE; };
+
+#pragma unroll
+  for (int i = 0; i < kStages; ++i) issue_stage(i);
+  wait_vmcnt<(kStages - 1) * T::VMEM_PER_STAGE>();   // stage 0 has landed
+  __syncthreads();
+  Frags<T> fa, fb;
+  Scales<T> sc, sn;
+  load_scales<T>(sc, stage_ptr(0), wn, wm, lane);
+  load_frags<T, 0>(fa, stage_ptr(0), wn, wm, lane);
+  select_scales<T>(sc, lane);
+  constexpr int NDS = (T::TN + T::TM) * (T::FMT == FMT_FP4 ? 1 : 2);
+  constexpr int NSC = T::FMT == FMT_FP4 ? T::TN + T::TM : 0;
   for (int ks = 0; ks < nks; ++ks) {
-    // stage ks has landed once at most the next stage's copies are still in flight
-    if (ks + 1 < nks)
-      wait_vmcnt<T::VMEM_PER_STAGE>();
-    else
-      wait_vmcnt<0>();
-    __syncthreads();              // every wave's copies of stage ks are visible, and stage ks-1 is free
-    if (ks + 2 < nks) issue_stage(ks + 2);   // overwrites the stage read in step ks-1
     __builtin_amdgcn_sched_barrier(0);
-    compute_stage<T>(acc, lds + (ks % kStages) * T::STAGE, wn, wm, lane);
+    if constexpr (T::CH == 2) {
+      // first half: MFMA step 0 of stage ks, reading step 1's fragments meanwhile
+      load_frags<T, 1>(fb, stage_ptr(ks), wn, wm, lane);
+      mfma_part<T, 0, 0, T::TM>(acc, fa, sc);
+      interleave<T::TN * T::TM, NDS>();
+    } else {
+      mfma_part<T, 0, 0, T::TM / 2>(acc, fa, sc);
+    }
     pin_accumulators<T>(acc);
     __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(kStages - 2) * T::VMEM_PER_STAGE>();   // stage ks+1 has landed
+    __syncthreads();
+    issue_stage(ks + kStages);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (T::CH == 2) {
+      // second half: MFMA step 1 of stage ks, reading stage ks+1's step-0 operands
+      load_scales<T>(sn, stage_ptr(ks + 1), wn, wm, lane);
+      load_frags<T, 0>(fa, stage_ptr(ks + 1), wn, wm, lane);
+      mfma_part<T, 1, 0, T::TM>(acc, fb, sc);
+      interleave<T::TN * T::TM, NDS + NSC>();
+      pin_accumulators<T>(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      sc = sn;
+      select_scales<T>(sc, lane);
+    } else {
+      load_frags<T, 0>(fb, stage_ptr(ks + 1), wn, wm, lane);
+      mfma_part<T, 0, T::TM / 2, T::TM>(acc, fa, sc);
+      interleave<T::TN * (T::TM - T::TM / 2), NDS>();
+      pin_accumulators<T>(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      fa = fb;
+    }
   }
+  wait_vmcnt<0>();     // no copy into this workgroup's LDS may outlive it
+  __builtin_amdgcn_sched_barrier(0);
   epilogue<T>(p, acc, n0 + wn * T::WN, m0 + wm * T::WM, lane);
 }
 
@@ -538,24 +591,24 @@ hipError_t launch_gemm_fp4(const uint8_t* a_codes, const uint8_t* a_scales, cons
   Params p = make_params(a_codes, a_scales, blob, FMT_FP4, M, N, K, out, ldo);
   switch (epi) {
     case EPI_IDENTITY:
-      return launch<Tile<FMT_FP4, EPI_IDENTITY, 128, 64, 2, 2>>(p, stream);
+      return launch<Tile<FMT_FP4, EPI_IDENTITY, 128, 64, 2, 4>>(p, stream);
     case EPI_GATED_SILU:
-      return launch<Tile<FMT_FP4, EPI_GATED_SILU, 128, 64, 2, 2>>(p, stream);
+      return launch<Tile<FMT_FP4, EPI_GATED_SILU, 128, 64, 2, 4>>(p, stream);
     default:
       p.gamma_q = rms->gamma_q;
       p.gamma_k = rms->gamma_k;
       p.eps = rms->eps;
       p.n_heads = rms->n_heads;
-      if (rms->head_dim == 128) return launch<Tile<FMT_FP4, EPI_QK_RMSNORM, 128, 64, 2, 2>>(p, stream);
-      return launch<Tile<FMT_FP4, EPI_QK_RMSNORM, 256, 32, 1, 4>>(p, stream);
+      if (rms->head_dim == 128) return launch<Tile<FMT_FP4, EPI_QK_RMSNORM, 128, 64, 2, 4>>(p, stream);
+      return launch<Tile<FMT_FP4, EPI_QK_RMSNORM, 256, 32, 1, 8>>(p, stream);
   }
 }
 
 hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scales, const uint8_t* blob, int M, int N,
                            int K, int epi, uint16_t* out, int ldo, hipStream_t stream) {
   Params p = make_params(a_codes, a_scales, blob, FMT_FP8, M, N, K, out, ldo);
-  if (epi == EPI_GATED_SILU) return launch<Tile<FMT_FP8, EPI_GATED_SILU, 128, 64, 2, 2>>(p, stream);
-  return launch<Tile<FMT_FP8, EPI_IDENTITY, 128, 64, 2, 2>>(p, stream);
+  if (epi == EPI_GATED_SILU) return launch<Tile<FMT_FP8, EPI_GATED_SILU, 128, 64, 2, 4>>(p, stream);
+  return launch<Tile<FMT_FP8, EPI_IDENTITY, 128, 64, 2, 4>>(p, stream);
 }
 
 }  // namespace ditq
