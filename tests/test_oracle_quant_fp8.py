@@ -93,6 +93,20 @@ def test_row_scale_matches_exact_rational_division():
             assert c[r, k] == quant.e4m3_rne_bruteforce(np.array([y], np.float32))[0]
 
 
+@pytest.mark.parametrize("amax_bits", [0x3FC4, 0x40C4])
+def test_every_bf16_below_row_max_matches_exact_division(amax_bits):
+    """One row holding every non-negative bf16 value up to its maximum.  For these
+    maxima, x * fl32(1 / s) and fl32(x / s) land on opposite sides of an E4M3
+    rounding boundary for some elements, so a reciprocal-multiply quantizer fails."""
+    bits = np.arange(0, amax_bits + 1, dtype=np.uint16)[None, :]
+    c, s = quant.quantize_fp8(bits)
+    s_ref = _rn32(Fraction(float(formats.bf16_to_f64(np.uint16(amax_bits)))) / 448)
+    assert np.float32(s[0]) == s_ref
+    xv = formats.bf16_to_f64(bits[0])
+    y = np.array([_rn32(Fraction(float(v)) / Fraction(float(s_ref))) for v in xv], dtype=np.float32)
+    assert np.array_equal(c[0], quant.e4m3_rne_bruteforce(y))
+
+
 def test_row_quantization_error_bound():
     rng = np.random.default_rng(4)
     from workloads import f32_to_bf16_bits
