@@ -1,11 +1,11 @@
 // Fused low-bit GEMM + epilogue on gfx950 scaled MFMA.
 //
-// out = epi(A W^T): A = on-the-fly quantized activations [M, K] (row-major codes),
-// W = packed weights (fragment layout, include/ditq.h).  The small op after the
-// GEMM runs on the fp32 accumulators in registers and the result is written to
-// HBM once as bf16 ("epilogue fusion": page "How fal made Ideogram V4 6x faster",
-// paragraph 3; gated-SiLU with interleaved columns: paragraph 4; FP8 as the second
-// precision: page "WaveSpeedAI X DataCrunch", engine list).
+// out = epi(A W^T): A = on-the-fly quantized activations [M, K] (K-panel-major
+// codes), W = packed weights (MFMA fragment layout, include/ditq.h).  The small op
+// after the GEMM runs on the fp32 accumulators in registers and the result is
+// written to HBM once as bf16 ("epilogue fusion": page "How fal made Ideogram V4 6x
+// faster", paragraph 3; gated-SiLU with interleaved columns: paragraph 4; FP8 as the
+// second precision: page "WaveSpeedAI X DataCrunch", engine list).
 //
 // Mapping to CDNA4:
 // * MFMA operand A = a 32-row weight fragment, operand B = 32 tokens, so the
@@ -18,57 +18,104 @@
 //   E8M0 block scales applied by the instruction (op_sel picks the byte of the
 //   64-K step).  FP8: the same instruction with E4M3 operands (8 VGPRs) and unit
 //   block scales; the fp32 row/column scales are applied in the epilogue.
-// * A workgroup computes a 256 (features) x 256 (tokens) tile with 8 waves (two per
-//   SIMD, 128 accumulators each).  The large tile keeps the L2 -> LDS traffic at
-//   about half of what the CU's load path can move while the MFMAs run at full
-//   rate; two waves per SIMD let one wave's LDS waits overlap the other's MFMAs.
-// * K advances in steps of 64 operand bytes per row (FP4: 128 K, FP8: 64 K)
-//   through a 4-stage LDS ring filled by direct-to-LDS buffer loads, three steps
-//   ahead of the MFMAs; one barrier per step.  Each stage also carries the step's
-//   E8M0 scale bytes.  Weight tiles are copied verbatim (the blob is in lane
-//   order); activation rows get a 16-byte XOR swizzle so fragment reads are free
-//   of LDS bank conflicts.
+// * A workgroup of 4 waves (one per SIMD) computes a 256 (features) x BM (tokens)
+//   tile; wave (wn, wm) owns 128 features x BM/2 tokens (4 x TM result tiles of
+//   32 x 32, TM = 3 or 4, up to 256 accumulators).
+// * Of each wave's 4 weight row groups, 2 come through LDS (one copy per workgroup,
+//   read by the two waves of a row band) and 2 are loaded straight into a ring of
+//   registers several 64-K steps ahead: the blob holds every fragment in the lane
+//   order of the MFMA operand, so no reshuffle is needed either way.  The
+//   activation tile, which the waves share, also goes through LDS, in a ring of
+//   stages filled by direct-to-LDS buffer loads together with the step's E8M0 scale
+//   bytes.  Staging all weights in LDS or none of them loads one of the two paths
+//   (LDS, or the per-CU vector memory path) well above the other; the even split
+//   measured fastest on every workload.
+// * Persistent: one workgroup per CU walks its share of the tiles, and the loads
+//   run ahead across tile boundaries, so the next tile's first steps are in flight
+//   while the current tile's epilogue runs.
+// * Every half-step issues the same number of memory operations, so each wait is a
+//   constant count of outstanding operations, and the workgroup barrier carries no
+//   memory fence (the kernel orders its LDS accesses itself).
 // * Raw buffer loads return zeros past the end of a tensor, which clips ragged M
-//   without branches; stores are predicated per row.
-// * Workgroups are re-ordered so each XCD (workgroup id mod 8) walks a compact
-//   band of output tiles and shares operand rows through its own L2.
+//   and padded rows without branches; stores are predicated per row and column.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace ditq {
 namespace {
 
 constexpr int kRowBytes = 64;    // operand bytes per row per k-step
-constexpr int kStages = 4;       // LDS ring depth
+// Weight row groups per wave staged through LDS (measured best): FP4 splits the
+// four evenly; FP8, whose MFMAs take twice as long per byte, loads all of them into
+// registers.
+constexpr int wlds_for(int fmt) { return fmt == FMT_FP4 ? 2 : 0; }
 constexpr int kGroupM = 4;       // tile-order group height (in M tiles)
 
-template <int FMT_, int EPI_, int WN_, int WM_, int WAVES_N_, int WAVES_M_>
+// WLDS: how many of the wave's 4 weight row groups come through LDS (shared by the
+// two waves of a row band, one copy per workgroup); the other TN - WLDS groups are
+// loaded straight into registers.  RING: length of that register ring in units (a
+// unit = one 64-K MFMA step); unit u is loaded RING-1 units before it is used.
+// HD: head_dim of the QK-RMSNorm epilogue (0 otherwise).
+template <int FMT_, int EPI_, int TM_, int RING_, int WLDS_, int HD_ = 0>
 struct Tile {
-  static constexpr int FMT = FMT_, EPI = EPI_;
-  static constexpr int WN = WN_, WM = WM_, WAVES_N = WAVES_N_, WAVES_M = WAVES_M_;
-  static constexpr int TN = WN / 32, TM = WM / 32;
+  static constexpr int FMT = FMT_, EPI = EPI_, TM = TM_, RING = RING_, WLDS = WLDS_, HD = HD_;
+  static constexpr int TN = 4, WAVES_N = 2, WAVES_M = 2, NW = 4, NT = 256;
+  static constexpr int WN = 32 * TN, WM = 32 * TM;
   static constexpr int BN = WN * WAVES_N, BM = WM * WAVES_M;
-  static constexpr int NW = WAVES_N * WAVES_M;
-  static constexpr int NT = 64 * NW;
-  static constexpr int CH = FMT == FMT_FP4 ? 2 : 1;         // 64-K MFMA steps per k-step
+  static constexpr int CH = FMT == FMT_FP4 ? 2 : 1;           // units per k-step
   static constexpr int KSTEP = 64 * CH;
-  static constexpr int FRAG = FMT == FMT_FP4 ? 1024 : 2048;  // bytes of one 32x64 operand fragment
-  static constexpr int GROUP_BYTES = FRAG * CH;              // one 32-row group per k-step (2 KB)
-  // LDS stage: weight codes | activation codes | weight scale records | activation scales
-  static constexpr int W_BYTES = BN * kRowBytes, A_BYTES = BM * kRowBytes;
-  static constexpr int WS_OFF = W_BYTES + A_BYTES;
-  static constexpr int WS_BYTES = FMT == FMT_FP4 ? BN / 32 * 128 : 0;   // 128 B per 32-row group
-  static constexpr int AS_OFF = WS_OFF + WS_BYTES;
-  static constexpr int AS_BYTES = FMT == FMT_FP4 ? BM * 4 : 0;          // 4 B per token
-  static constexpr int STAGE = AS_OFF + AS_BYTES;
-  // direct-to-LDS copies per wave per stage (plus one scale copy on waves 0 and 1 for FP4)
-  static constexpr int WCK = W_BYTES / 1024 / NW;
-  static constexpr int ACK = A_BYTES / 1024 / NW;
-  static constexpr int VMEM_PER_STAGE = WCK + ACK;   // the fewest any wave issues per stage
-  static_assert(W_BYTES % (1024 * NW) == 0 && A_BYTES % (1024 * NW) == 0, "whole 1 KB copies per wave");
-  static_assert(WS_BYTES <= 1024 && AS_BYTES <= 1024, "each scale record set is one copy");
-  static_assert(GROUP_BYTES == 2048, "a 32-row group moves 2 KB per k-step");
-  static_assert(kStages * STAGE <= 160 * 1024, "the LDS ring must fit in a CU's LDS");
-  static_assert(NW % 4 == 0, "whole waves per SIMD");
+  static constexpr int FRAG = FMT == FMT_FP4 ? 1024 : 2048;    // bytes of one 32x64 operand fragment
+  static constexpr int FRAG_LOADS = FRAG / 1024;               // 16-byte loads per lane per fragment
+  static constexpr int TND = TN - WLDS;                        // weight groups loaded into registers
+  static constexpr int UNIT_LOADS = TND * FRAG_LOADS;
+  static constexpr int STEPS_PER_GROUP = RING / CH;            // k-steps per unrolled group
+  static constexpr int GROUP_BYTES = FRAG * CH;                // one 32-row group per k-step (2 KB)
+  // LDS stage: weight codes of the LDS groups | activation codes | activation scale
+  // words | weight scale records
+  static constexpr int W_BYTES = WAVES_N * WLDS * GROUP_BYTES;
+  static constexpr int A_OFF = W_BYTES;
+  static constexpr int A_BYTES = BM * kRowBytes;
+  static constexpr int AS_OFF = A_OFF + A_BYTES;
+  static constexpr int AS_BYTES = FMT == FMT_FP4 ? (3 * BM + 256 + 255) / 256 * 256 : 0;
+  static constexpr int WS_OFF = AS_OFF + AS_BYTES;
+  static constexpr int WS_BYTES = FMT == FMT_FP4 ? BN / 32 * 128 : 0;
+  static constexpr int STAGE = (WS_OFF + WS_BYTES + 255) / 256 * 256;
+  static constexpr int STAGES_FIT = (160 * 1024 - 1024 - (HD == 256 ? WAVES_N * BM * 4 : 0)) / STAGE;
+  static constexpr int STAGES = STAGES_FIT < 5 ? STAGES_FIT : 5;
+  static constexpr int JUNK_OFF = STAGES * STAGE;            // target of the prologue's padding copies
+  static constexpr int RED_OFF = JUNK_OFF + 1024;            // per-token partial sums (head_dim 256)
+  static constexpr int RED_BYTES = HD == 256 ? WAVES_N * BM * 4 : 0;
+  static constexpr int LDS_BYTES = RED_OFF + RED_BYTES;
+  static constexpr int WCK = W_BYTES / 1024 / NW;            // 1 KB weight copies per wave per stage
+  static constexpr int ACK = A_BYTES / 1024 / NW;            // 1 KB activation copies per wave per stage
+  static constexpr int NCOPY = WCK + ACK + (FMT == FMT_FP4 ? 2 : 0);   // + activation / weight scale copies
+  // Memory operations every wave issues per half-step: FP4 loads one unit per
+  // half and copies a stage in the second half; FP8 does both in the second half.
+  static constexpr int OPS_H0 = FMT == FMT_FP4 ? UNIT_LOADS : 0;
+  static constexpr int OPS_H1 = NCOPY + UNIT_LOADS;
+  static constexpr int OPS_STEP = OPS_H0 + OPS_H1;
+  // Waits, as the number of operations that may stay outstanding (vmcnt counts
+  // in issue order; the counts below hold whatever the order inside a half).
+  //   unit u used in half h: issued in half h - (RING - 1), so the RING - 2 halves
+  //   in between were all issued after it (FP8: units are steps, issued in the
+  //   second half of step g - (RING - 1)).
+  static constexpr int WAIT_UNIT = FMT == FMT_FP4 ? (RING - 2) / 2 * OPS_STEP : (RING - 2) * OPS_H1;
+  //   stage g+1 (needed at the barrier of step g): issued in the second half of
+  //   step g + 1 - STAGES; steps g+2-STAGES .. g-1 and the first half of g follow.
+  static constexpr int WAIT_STAGE = (STAGES - 2) * OPS_STEP + OPS_H0;
+  static constexpr int WAIT_BARRIER =
+      FMT == FMT_FP4 ? (WAIT_UNIT < WAIT_STAGE ? WAIT_UNIT : WAIT_STAGE) : WAIT_STAGE;
+  // prologue: the half-steps before step 0 that issue stage 0 .. STAGES-1 and unit 0 .. RING-2
+  static constexpr int PRO_HALVES = FMT == FMT_FP4 ? (2 * STAGES - 1 > RING - 1 ? 2 * STAGES - 1 : RING - 1)
+                                                   : 2 * (STAGES > RING - 1 ? STAGES : RING - 1);
+  static_assert(A_BYTES == ACK * 1024 * NW && W_BYTES == WCK * 1024 * NW, "whole 1 KB copies per wave");
+  static_assert(WLDS >= 0 && WLDS <= TN, "weight groups split between LDS and registers");
+  static_assert(3 * BM + 256 <= AS_BYTES || FMT != FMT_FP4, "overlapping scale-word copies fit");
+  static_assert(RING % CH == 0 && RING >= 4, "ring holds whole k-steps");
+  static_assert(WAIT_UNIT < 64 && WAIT_STAGE < 64, "vmcnt range");
+  static_assert(LDS_BYTES <= 160 * 1024 && STAGES >= 3, "LDS");
+  static_assert(TN * TM * 16 <= 256, "accumulators fit in the AGPRs");
 };
 
 struct Params {
@@ -78,7 +125,7 @@ struct Params {
   const void* w_scales;       // FP4: E8M0 groups; FP8: f32 [Np]
   uint16_t* out;
   int M, N, K, ldo;
-  int tiles_m, tiles_n;
+  int tiles_m, tiles_n, tiles;
   uint32_t a_bytes, w_bytes, as_bytes, ws_bytes;
   const float* gamma_q;
   const float* gamma_k;
@@ -91,12 +138,11 @@ struct Params {
 // cycle of 16-byte reads) and r..r+15 (one 64-bank cycle) land in distinct banks.
 __device__ __host__ constexpr int swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
-__device__ inline void tile_coords(int bid, int total, int tiles_m, int tiles_n, int& tm, int& tn) {
-  // workgroup ids are dealt round-robin to the 8 XCDs; give XCD x a contiguous range
-  const int q = total >> 3, r = total & 7;
-  const int x = bid & 7, i = bid >> 3;
-  const int t = x * q + min(x, r) + i;
-  // grouped order inside the range: kGroupM tiles down M, then across N
+// Tile order: kGroupM tiles down M, then across N, group after group; a workgroup
+// that sits on XCD x (workgroup id mod 8, the round-robin the dispatcher deals
+// ids in) walks a contiguous eighth of that order, so the tiles that are in
+// flight on one XCD share operand rows through its L2.
+__device__ inline void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int per_group = kGroupM * tiles_n;
   const int group = t / per_group;
   const int first = group * kGroupM;
@@ -148,78 +194,70 @@ __device__ inline float silu(float x) {
 }
 
 
-// Operand fragments of one 64-K MFMA step: TN weight fragments, TM token fragments.
+// ---------------------------------------------------------------- operands
+// Activation fragments of one unit (TM token tiles): lane L holds token row
+// wm*WM + 32*tm + L%32, K chunk 32*(L/32) of the unit (FP4: 16 bytes at logical
+// chunk 2J + L/32 of the 64-byte row; FP8: 32 bytes, chunks 2*(L/32), +1).
 template <class T>
-struct Frags {
-  v8i w[T::TN];
-  v8i a[T::TM];
+struct AFrag {
+  v4i a[T::TM][T::FRAG_LOADS];
+  v4i w[T::WLDS > 0 ? T::WLDS : 1][T::FRAG_LOADS];   // weight groups read from LDS
 };
 
 template <class T, int J>
-__device__ __forceinline__ void load_frags(Frags<T>& f, const uint8_t* stage, int wn, int wm, int lane) {
+__device__ __forceinline__ void load_act(AFrag<T>& f, const uint8_t* stage, int wn, int wm, int lane) {
   const int h = lane >> 5, l32 = lane & 31;
-  const uint8_t* wb = stage;
-  const uint8_t* ab = stage + T::W_BYTES;
+  // weight fragments of the LDS groups: copied verbatim from the blob (lane order)
 #pragma unroll
-  for (int tn = 0; tn < T::TN; ++tn) {
-    const uint8_t* fp = wb + (wn * T::TN + tn) * T::GROUP_BYTES + J * T::FRAG;
-    if constexpr (T::FMT == FMT_FP4) {
-      const v4i x = *reinterpret_cast<const v4i*>(fp + 16 * lane);
-      f.w[tn] = __builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1);
-    } else {
-      const v4i x0 = *reinterpret_cast<const v4i*>(fp + 32 * lane);
-      const v4i x1 = *reinterpret_cast<const v4i*>(fp + 32 * lane + 16);
-      f.w[tn] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  }
+  for (int g = 0; g < T::WLDS; ++g)
+#pragma unroll
+    for (int l = 0; l < T::FRAG_LOADS; ++l)
+      f.w[g][l] = *reinterpret_cast<const v4i*>(stage + (wn * T::WLDS + g) * T::GROUP_BYTES + J * T::FRAG +
+                                                (T::FRAG / 64) * lane + 16 * l);
+  stage += T::A_OFF;
 #pragma unroll
   for (int tm = 0; tm < T::TM; ++tm) {
     const int r = wm * T::WM + 32 * tm + l32;
-    const uint8_t* row = ab + r * kRowBytes;
+    const uint8_t* row = stage + r * kRowBytes;
     if constexpr (T::FMT == FMT_FP4) {
-      const int c = 2 * J + h;
-      const v4i x = *reinterpret_cast<const v4i*>(row + 16 * (c ^ swz(r)));
-      f.a[tm] = __builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1);
+      f.a[tm][0] = *reinterpret_cast<const v4i*>(row + 16 * ((2 * J + h) ^ swz(r)));
     } else {
-      const int c = 2 * h;
-      const v4i x0 = *reinterpret_cast<const v4i*>(row + 16 * (c ^ swz(r)));
-      const v4i x1 = *reinterpret_cast<const v4i*>(row + 16 * ((c + 1) ^ swz(r)));
-      f.a[tm] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+      f.a[tm][0] = *reinterpret_cast<const v4i*>(row + 16 * ((2 * h) ^ swz(r)));
+      f.a[tm][1] = *reinterpret_cast<const v4i*>(row + 16 * ((2 * h + 1) ^ swz(r)));
     }
   }
 }
 
-// sched_group_barrier masks
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
+// Weight fragments of one unit, straight from the blob into registers.
+template <class T>
+struct WUnit {
+  v4i w[T::TND > 0 ? T::TND : 1][T::FRAG_LOADS];
+};
 
-// Scale words of one k-step (FP4): the weight record's 16-bit word per lane holds
-// op_sel bytes 0 and 1; a token's 4 scale bytes are its blocks 0..3 of the step,
-// and this lane's MFMA steps j = 0, 1 take blocks 2j + h (selector byte 0x0C
+// Scale words of one k-step (FP4): a weight record's 16-bit word per lane holds the
+// bytes of units J = 0, 1; two row groups share a register (group tn in bytes
+// 2*(tn%2) + J, picked by op_sel).  A token's 4 scale bytes are its blocks 0..3 of
+// the step, and this lane's units J = 0, 1 take blocks 2J + h (selector byte 0x0C
 // gives a zero byte).
 template <class T>
 struct Scales {
-  uint32_t w[T::TN];
+  uint32_t w[T::TN / 2];
   uint32_t a[T::TM];
 };
 
-// Raw scale words of a stage (the activation bytes are selected later, once the
-// LDS reads have landed, so that no MFMA waits on them).
 template <class T>
 __device__ __forceinline__ void load_scales(Scales<T>& sc, const uint8_t* stage, int wn, int wm, int lane) {
   if constexpr (T::FMT == FMT_FP4) {
     const int l32 = lane & 31;
 #pragma unroll
-    for (int tn = 0; tn < T::TN; ++tn)
-      sc.w[tn] = *reinterpret_cast<const uint16_t*>(stage + T::WS_OFF + (wn * T::TN + tn) * 128 + 2 * lane);
+    for (int t2 = 0; t2 < T::TN / 2; ++t2) {
+      const uint8_t* rec = stage + T::WS_OFF + (wn * T::TN + 2 * t2) * 128 + 2 * lane;
+      sc.w[t2] = (uint32_t)*reinterpret_cast<const uint16_t*>(rec) |
+                 ((uint32_t)*reinterpret_cast<const uint16_t*>(rec + 128) << 16);
+    }
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm)
       sc.a[tm] = *reinterpret_cast<const uint32_t*>(stage + T::AS_OFF + 4 * (wm * T::WM + 32 * tm + l32));
-  } else {
-#pragma unroll
-    for (int tn = 0; tn < T::TN; ++tn) sc.w[tn] = 0;
-#pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm) sc.a[tm] = 0;
   }
 }
 
@@ -232,43 +270,78 @@ __device__ __forceinline__ void select_scales(Scales<T>& sc, int lane) {
   }
 }
 
-// MFMAs of 64-K step J over token tiles [TM0, TM1), with the LDS reads that are
-// issued in the same region spread between them.
-template <class T, int J, int TM0, int TM1>
-__device__ __forceinline__ void mfma_part(v16f (&acc)[T::TN][T::TM], const Frags<T>& f, const Scales<T>& sc) {
-#pragma unroll
-  for (int tn = 0; tn < T::TN; ++tn)
-#pragma unroll
-    for (int tm = TM0; tm < TM1; ++tm) {
-      if constexpr (T::FMT == FMT_FP4)
-        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[tn], f.a[tm], acc[tn][tm], 4, 4, J,
-                                                                      (int)sc.w[tn], J, (int)sc.a[tm]);
-      else
-        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[tn], f.a[tm], acc[tn][tm], 0, 0, 0,
-                                                                      0x7F7F7F7F, 0, 0x7F7F7F7F);
-    }
+// MFMAs of unit J (FP4 op_sel byte) over token tiles [TM0, TM1); ZERO starts the
+// sums from 0 (first step of a tile) instead of the accumulators.
+template <class T>
+__device__ __forceinline__ v8i operand(const v4i (&x)[T::FRAG_LOADS]) {
+  if constexpr (T::FMT == FMT_FP4)
+    return __builtin_shufflevector(x[0], x[0], 0, 1, 2, 3, -1, -1, -1, -1);
+  else
+    return __builtin_shufflevector(x[0], x[T::FRAG_LOADS - 1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Spread NDS LDS reads between NMFMA MFMAs of the current scheduling region.
-template <int NMFMA, int NDS>
-__device__ __forceinline__ void interleave() {
-  constexpr int pairs = NDS < NMFMA ? NDS : NMFMA;
-#pragma unroll
-  for (int i = 0; i < pairs; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
   }
-  if constexpr (NMFMA > pairs) __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - pairs, 0);
-  if constexpr (NDS > pairs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NDS - pairs, 0);
+}
+
+template <class T, int J, int TM0, int TM1, bool ZERO>
+__device__ __forceinline__ void mfma_part(v16f (&acc)[T::TN][T::TM], const WUnit<T>& wu, const AFrag<T>& f,
+                                          const Scales<T>& sc) {
+  static_for<0, T::TN>([&](auto tn_c) __attribute__((always_inline)) {
+    constexpr int tn = decltype(tn_c)::value;
+    v8i w;
+    if constexpr (tn < T::WLDS)
+      w = operand<T>(f.w[tn]);
+    else
+      w = operand<T>(wu.w[tn - T::WLDS]);
+#pragma unroll
+    for (int tm = TM0; tm < TM1; ++tm) {
+      const v16f c = ZERO ? v16f{} : acc[tn][tm];
+      if constexpr (T::FMT == FMT_FP4)
+        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            w, operand<T>(f.a[tm]), c, 4, 4, 2 * (tn & 1) + J, (int)sc.w[tn / 2], J, (int)sc.a[tm]);
+      else
+        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, operand<T>(f.a[tm]), c, 0, 0, 0,
+                                                                      0x7F7F7F7F, 0, 0x7F7F7F7F);
+    }
+  });
+}
+
+// Order of the current scheduling region: LDS reads first, then the MFMAs with
+// the NV vector-memory operations spread evenly between them.
+template <int NM, int NV>
+__device__ __forceinline__ void spread_vmem() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008, kVmem = 0x010;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, 64, 0);
+  if constexpr (NV == 0) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, NM, 0);
+  } else {
+    constexpr int per = NM / (NV + 1) > 0 ? NM / (NV + 1) : 1;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, per, 0);
+      __builtin_amdgcn_sched_group_barrier(kVmem, 1, 0);
+    }
+    if constexpr (NM > per * NV) __builtin_amdgcn_sched_group_barrier(kMfma, NM - per * NV, 0);
+  }
 }
 
 // ---------------------------------------------------------------- epilogues
+__device__ __forceinline__ void barrier();
+__device__ __forceinline__ void wait_lds();
+
 template <class T>
-__device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::TM], int n0w, int m0w, int lane) {
+__device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::TM], int n0w, int m0w, int lane,
+                                         int wn, int wm, uint8_t* lds) {
   const int h = lane >> 5, l32 = lane & 31;
   if constexpr (T::EPI == EPI_IDENTITY || T::EPI == EPI_GATED_SILU) {
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) {
+      __builtin_amdgcn_sched_barrier(0);     // one token tile at a time keeps register use low
       const int row = m0w + 32 * tm + l32;
       const bool ok = row < p.M;
       float sa = 1.0f;
@@ -276,6 +349,7 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
       if constexpr (T::EPI == EPI_IDENTITY) {
 #pragma unroll
         for (int tn = 0; tn < T::TN; ++tn) {
+          __builtin_amdgcn_sched_barrier(0);   // one result tile at a time
           float v[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) v[r] = acc[tn][tm][r];
@@ -293,6 +367,7 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
       } else {
 #pragma unroll
         for (int q = 0; q < T::TN / 2; ++q) {
+          __builtin_amdgcn_sched_barrier(0);   // one gate/up pair at a time
           float gate[16], up[16], v[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -319,31 +394,37 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
       }
     }
   } else {
-    // Per-head QK-RMSNorm; the wave's WN columns are exactly one head.
-    constexpr int D = T::WN;
-    const int head = n0w / D;
+    // Per-head QK-RMSNorm.  head_dim 128: the wave's 128 columns are one head.
+    // head_dim 256: the workgroup's 256 columns are one head; waves wn = 0 and 1
+    // hold its first and second 128 columns and exchange per-token partial sums of
+    // squares through LDS (both add the same two numbers, so both get the same sum).
+    constexpr int D = T::HD;
+    static_assert(D == T::WN || D == T::BN, "a head is one wave or one workgroup wide");
+    const int head = D == T::WN ? n0w / D : (n0w - wn * T::WN) / D;
     const int part = head / p.n_heads;          // 0 = Q, 1 = K, 2 = V, 3 = padding past N
-    if (part >= 3) return;
-    const float* gamma = part == 0 ? p.gamma_q : p.gamma_k;
+    if (part >= 3) return;                      // uniform over the workgroup when D == BN
+    if (part == 2) {
 #pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm) {
-      const int row = m0w + 32 * tm + l32;
-      const bool ok = row < p.M;
-      if (part == 2) {
+      for (int tm = 0; tm < T::TM; ++tm) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int row = m0w + 32 * tm + l32;
 #pragma unroll
         for (int tn = 0; tn < T::TN; ++tn) {
           float v[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) v[r] = acc[tn][tm][r];
-          store_tile(p.out, p.ldo, row, ok, n0w + 32 * tn, p.N, h, v);
+          store_tile(p.out, p.ldo, row, row < p.M, n0w + 32 * tn, p.N, h, v);
         }
-        continue;
       }
-      // Revisit schedule: the first half of the head (tiles [0, TN/2)) keeps its
-      // fp32 values and its partial sum of squares in registers while the second
-      // half's partial sum is formed; the combined sum then normalises the second
-      // half, which is stored, and the first half is revisited and stored.  For
-      // head_dim 128 the same code runs over two 64-column halves.
+      return;
+    }
+    const float* gamma = (part == 0 ? p.gamma_q : p.gamma_k) + (D == T::WN ? 0 : wn * T::WN);
+    // Sums of squares per token: the two 64-column halves of the wave (the first
+    // half's values stay in registers while the second half's sum is formed), then
+    // the partner lane's 16 rows of each tile, then (head_dim 256) the other wave.
+    float ss[T::TM];
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm) {
       float ss_first = 0.0f, ss_second = 0.0f;
 #pragma unroll
       for (int tn = 0; tn < T::TN / 2; ++tn)
@@ -353,9 +434,26 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
       for (int tn = T::TN / 2; tn < T::TN; ++tn)
 #pragma unroll
         for (int r = 0; r < 16; ++r) ss_second += acc[tn][tm][r] * acc[tn][tm][r];
-      float ss = ss_first + ss_second;
-      ss += __shfl_xor(ss, 32);                   // the partner lane holds the other 16 rows of each tile
-      const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
+      ss[tm] = ss_first + ss_second;
+      ss[tm] += __shfl_xor(ss[tm], 32);
+    }
+    if constexpr (D != T::WN) {
+      float* red = reinterpret_cast<float*>(lds + T::RED_OFF);
+      if (lane < 32) {
+#pragma unroll
+        for (int tm = 0; tm < T::TM; ++tm) red[wn * T::BM + wm * T::WM + 32 * tm + l32] = ss[tm];
+      }
+      wait_lds();
+      barrier();
+#pragma unroll
+      for (int tm = 0; tm < T::TM; ++tm) ss[tm] += red[(1 - wn) * T::BM + wm * T::WM + 32 * tm + l32];
+    }
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int row = m0w + 32 * tm + l32;
+      const bool ok = row < p.M;
+      const float rs = __builtin_amdgcn_rsqf(ss[tm] * (1.0f / D) + p.eps);
 #pragma unroll
       for (int step = 0; step < 2; ++step) {
         const int t0 = step == 0 ? T::TN / 2 : 0;   // second half first, then revisit the first
@@ -376,11 +474,12 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
 }
 
 // ---------------------------------------------------------------- kernel
-// An empty volatile asm that reads every accumulator: the MFMAs of a k-step must
-// then be issued before it, and it stays ordered with the wait and the barrier that
-// follow (MFMAs touch no memory, so without it they may be sunk below the barrier).
-// The asm exists only in the device pass: on the host pass "a" would name an x86
-// register, and the failed constraint would silently drop the kernel's host stub.
+// An empty volatile asm that reads every accumulator: the MFMAs of a half-step
+// must then be issued before it, and it stays ordered with the wait and the barrier
+// that follow (MFMAs touch no memory, so without it they may be sunk below the
+// barrier).  The asm exists only in the device pass: on the host pass "a" would
+// name an x86 register, and the failed constraint would silently drop the kernel's
+// host stub.
 template <class T>
 __device__ __forceinline__ void pin_accumulators(v16f (&acc)[T::TN][T::TM]) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -391,177 +490,341 @@ __device__ __forceinline__ void pin_accumulators(v16f (&acc)[T::TN][T::TM]) {
 #endif
 }
 
-// N direct-to-LDS copies of BYTES per lane each: lane L of copy i fetches BYTES at
-// voff[i] + soff and the hardware writes them to dst + 64*BYTES*i + BYTES*L.
-// (A plain device function: inside a lambda the builtin would also be compiled
-// for the host, where it fails and takes the kernel's host stub with it.)
-template <int N, int BYTES>
-__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, const uint32_t* voff, int soff,
-                                            uint8_t* dst) {
+// One direct-to-LDS copy: lane L fetches BYTES at voff + soff and the hardware
+// writes them to dst + BYTES*L.  (A plain device function: inside a lambda the
+// builtin would also be compiled for the host, where it fails and takes the
+// kernel's host stub with it.)
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int soff, uint8_t* dst) {
   static_assert(BYTES == 16 || BYTES == 4, "copy width");
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    auto* d = (__attribute__((address_space(3))) void*)(dst + 64 * BYTES * i);
-    if constexpr (BYTES == 16)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 16, voff[i], soff, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 4, voff[i], soff, 0, 0);
-  }
+  auto* d = (__attribute__((address_space(3))) void*)dst;
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 16, voff, soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 4, voff, soff, 0, 0);
 }
 
-// s_waitcnt vmcnt(n) with the other counters unconstrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-template <int N>
+// The weight fragments of one unit: lane L's FRAG/64 bytes of fragment (group
+// tn of the wave's band, unit `unit`), straight into registers; wbase addresses
+// the band's first group for this lane, wgroup is the blob stride of a group.
+template <class T>
+__device__ __forceinline__ void load_unit(WUnit<T>& wu, __amdgpu_buffer_rsrc_t rsrc, uint32_t wbase, int unit,
+                                          int wgroup) {
+#pragma unroll
+  for (int tn = 0; tn < T::TND; ++tn)
+#pragma unroll
+    for (int l = 0; l < T::FRAG_LOADS; ++l)
+      wu.w[tn][l] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(rsrc, wbase, tn * wgroup + unit * T::FRAG + 16 * l, 0));
+}
+
+// s_waitcnt vmcnt(n) with the other counters unconstrained, or with lgkmcnt(0)
+// as well (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N, bool LDS_TOO = false>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | ((LDS_TOO ? 0x0 : 0xF) << 8) | ((N >> 4) << 14));
+}
+// s_waitcnt lgkmcnt(0) only
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier without a memory fence.  __syncthreads() is also a release
+// fence, and with the output stores in the same loop nest the compiler has to
+// drain every outstanding memory operation before it, which exposes the latency
+// of all the loads in flight on every k-step.  The kernel orders its own memory:
+// each wave waits for exactly the operations the barrier protects; the empty asm
+// statements keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <class T>
-__global__ void __launch_bounds__(T::NT, T::NW / 4) gemm_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * T::STAGE];
+__global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[T::LDS_BYTES];
+  constexpr int S = T::STAGES;
   // readfirstlane: the wave index is uniform, and the compiler must know it (a
   // per-wave buffer descriptor would otherwise become a loop over lanes)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % T::WAVES_N, wm = wave / T::WAVES_N;
-  int tmi, tni;
-  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tmi, tni);
-  const int n0 = tni * T::BN, m0 = tmi * T::BM;
-  const int nks = p.K / T::KSTEP;
-  const uint32_t wgroup = (uint32_t)(p.K / 64) * T::FRAG;
 
-  const auto a_rsrc = make_rsrc(p.a_codes, p.a_bytes);
-  const auto w_rsrc = make_rsrc(p.w_codes, p.w_bytes);
-
-  // Direct-to-LDS copies (each wave instruction writes 64 lanes x 16 bytes = 1 KB):
-  // weight copy q = half of row group q/2 (verbatim: the blob is in lane order);
-  // activation copy q = 16 token rows of the K panel (contiguous 1 KB in the
-  // panel-major layout), lane L fetching the logical chunk that the swizzle
-  // places at slot L%4 of row 16q + L/4.
-  uint32_t w_off[T::WCK], a_off[T::ACK];
-#pragma unroll
-  for (int i = 0; i < T::WCK; ++i) {
-    const int q = wave * T::WCK + i;
-    w_off[i] = (uint32_t)(n0 / 32 + (q >> 1)) * wgroup + 1024u * (q & 1) + 16u * lane;
-  }
-#pragma unroll
-  for (int i = 0; i < T::ACK; ++i) {
-    const int q = wave * T::ACK + i;
-    const int r = 16 * q + (lane >> 2);
-    const int c = (lane & 3) ^ swz(r);
-    // Rows past M read the next panel's codes (or zeros past the buffer end);
-    // their results are never stored.
-    a_off[i] = (uint32_t)(m0 + r) * kRowBytes + 16u * c;
-  }
-  const uint32_t a_panel = (uint32_t)p.M * kRowBytes;   // bytes of one K panel of the activation codes
-  // FP4 scale copies, one per stage: wave 0 copies the weight scale records of the
-  // block's row groups (1 KB, contiguous for one K step), wave 1 the 4-byte scale
-  // words of the block's tokens (BM * 4 bytes, contiguous in the panel-major layout).
-  [[maybe_unused]] __amdgpu_buffer_rsrc_t s_rsrc;
-  uint32_t s_off[1] = {0};
-  [[maybe_unused]] uint32_t s_step = 0;
-  [[maybe_unused]] bool s_active = false;
-  [[maybe_unused]] int s_dst = 0;
-  if constexpr (T::FMT == FMT_FP4) {
-    if (wave == 0) {
-      s_rsrc = make_rsrc(p.w_scales, p.ws_bytes);
-      s_off[0] = (uint32_t)(n0 / 32) * 128u + 16u * lane;
-      s_step = (uint32_t)(padded_rows(p.N) / 32) * 128u;
-      s_dst = T::WS_OFF;
-      s_active = 16 * lane < T::WS_BYTES;
-    } else if (wave == 1) {
-      s_rsrc = make_rsrc(p.a_scales, p.as_bytes);
-      s_off[0] = (uint32_t)m0 * 4u + 16u * lane;
-      s_step = (uint32_t)p.M * 4u;
-      s_dst = T::AS_OFF;
-      s_active = 16 * lane < T::AS_BYTES;
-    }
-  }
-
-  auto issue_stage = [&](int ks) {
-    uint8_t* base = lds + (ks % kStages) * T::STAGE;
-    copy_to_lds<T::WCK, 16>(w_rsrc, w_off, ks * T::GROUP_BYTES, base + wave * T::WCK * 1024);
-    copy_to_lds<T::ACK, 16>(a_rsrc, a_off, ks * a_panel, base + T::W_BYTES + wave * T::ACK * 1024);
-    if constexpr (T::FMT == FMT_FP4) {
-      if (s_active) copy_to_lds<1, 16>(s_rsrc, s_off, ks * s_step, base + s_dst);
-    }
+  // Persistent schedule: one workgroup per CU.  The XCD of workgroup b (b mod 8)
+  // owns a contiguous range of the tile order; its workgroups take every gx-th
+  // tile of that range, so the tiles in flight on one XCD stay adjacent.
+  const int G = gridDim.x;
+  const int X = G < 8 ? G : 8;                     // XCDs that hold workgroups
+  const int x = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int gx = (G - x + 7) >> 3;                 // workgroups on this XCD
+  const int q = p.tiles / X, r = p.tiles % X;
+  const int x0 = x * q + min(x, r), len = q + (x < r ? 1 : 0);
+  const int n_mine = jx < len ? (len - jx + gx - 1) / gx : 0;
+  if (n_mine == 0) return;                         // uniform over the workgroup
+  auto tile_of = [&](int i, int& n0, int& m0) __attribute__((always_inline)) {
+    int tmi, tni;
+    tile_coords(x0 + jx + (i < n_mine ? i : n_mine - 1) * gx, p.tiles_m, p.tiles_n, tmi, tni);
+    n0 = tni * T::BN;
+    m0 = tmi * T::BM;
   };
 
-  v16f acc[T::TN][T::TM];
-#pragma unroll
-  for (int tn = 0; tn < T::TN; ++tn)
-#pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm) acc[tn][tm] = v16f{};
+  const int nks = p.K / T::KSTEP;
+  const int units = nks * T::CH;                                  // units per tile
+  const uint32_t wgroup = (uint32_t)(p.K / 64) * T::FRAG;         // blob bytes of one 32-row group
+  const uint32_t a_panel = (uint32_t)p.M * kRowBytes;            // bytes of one K panel of activation codes
+  const auto a_rsrc = make_rsrc(p.a_codes, p.a_bytes);
+  const auto w_rsrc = make_rsrc(p.w_codes, p.w_bytes);
+  [[maybe_unused]] const auto as_rsrc = make_rsrc(p.a_scales, p.as_bytes);
+  [[maybe_unused]] const auto ws_rsrc = make_rsrc(p.w_scales, p.ws_bytes);
+  [[maybe_unused]] const uint32_t as_step = (uint32_t)p.M * 4u;  // one K panel of activation scale words
+  [[maybe_unused]] const uint32_t ws_step = (uint32_t)(padded_rows(p.N) / 32) * 128u;
 
-  // Pipeline.  Step ks computes from ring slot ks % kStages.  The barrier of step ks
-  // sits between its two halves of MFMAs: before it the wave has issued the first
-  // half (which keeps the MFMA pipe busy through the wait), after it stage ks+1 is
-  // visible to every wave and slot ks % kStages is free, so the copy of stage
-  // ks + kStages goes there and the next stage's first fragments are read while
-  // the second half of the MFMAs runs.  Copies are issued for every step up to
-  // nks + kStages - 1: those past the end of K read zeros or unused rows (the
-  // buffer descriptors bound every read) into slots that are no longer read,
-  // which keeps the wait counts constant and the loop body free of branches.
-  auto stage_ptr = [&](int ks) { return lds + (ks % kStages) * T::STAGE; };
-
-#pragma unroll
-  for (int i = 0; i < kStages; ++i) issue_stage(i);
-  wait_vmcnt<(kStages - 1) * T::VMEM_PER_STAGE>();   // stage 0 has landed
-  __syncthreads();
-  Frags<T> fa, fb;
-  Scales<T> sc, sn;
-  load_scales<T>(sc, stage_ptr(0), wn, wm, lane);
-  load_frags<T, 0>(fa, stage_ptr(0), wn, wm, lane);
-  select_scales<T>(sc, lane);
-  constexpr int NDS = (T::TN + T::TM) * (T::FMT == FMT_FP4 ? 1 : 2);
-  constexpr int NSC = T::FMT == FMT_FP4 ? T::TN + T::TM : 0;
-  for (int ks = 0; ks < nks; ++ks) {
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (T::CH == 2) {
-      // first half: MFMA step 0 of stage ks, reading step 1's fragments meanwhile
-      load_frags<T, 1>(fb, stage_ptr(ks), wn, wm, lane);
-      mfma_part<T, 0, 0, T::TM>(acc, fa, sc);
-      interleave<T::TN * T::TM, NDS>();
-    } else {
-      mfma_part<T, 0, 0, T::TM / 2>(acc, fa, sc);
+  // Weight cursor: tile and unit that the next weight loads fetch.  Lane L of
+  // fragment (group g, unit u) sits at g * wgroup + u * FRAG + L * FRAG/64.
+  int wc_i = 0, wc_u = 0;
+  uint32_t wbase = 0;
+  auto set_w_tile = [&](int i) __attribute__((always_inline)) {
+    int n0, m0;
+    tile_of(i, n0, m0);
+    wbase = (uint32_t)(n0 / 32 + wn * T::TN + T::WLDS) * wgroup + (uint32_t)(T::FRAG / 64) * lane;
+  };
+  auto advance_w = [&]() __attribute__((always_inline)) {
+    if (++wc_u == units) {
+      wc_u = 0;
+      set_w_tile(++wc_i);
     }
-    pin_accumulators<T>(acc);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<(kStages - 2) * T::VMEM_PER_STAGE>();   // stage ks+1 has landed
-    __syncthreads();
-    issue_stage(ks + kStages);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (T::CH == 2) {
-      // second half: MFMA step 1 of stage ks, reading stage ks+1's step-0 operands
-      load_scales<T>(sn, stage_ptr(ks + 1), wn, wm, lane);
-      load_frags<T, 0>(fa, stage_ptr(ks + 1), wn, wm, lane);
-      mfma_part<T, 1, 0, T::TM>(acc, fb, sc);
-      interleave<T::TN * T::TM, NDS + NSC>();
+  };
+  // Activation cursor: tile and k-step of the next stage.  Activation copy c of
+  // wave w = 16 token rows of the K panel (contiguous in the panel-major layout),
+  // lane L fetching the logical chunk that the swizzle places at slot L%4 of row
+  // 16(w*ACK + c) + L/4.  FP4 scale copies, 4 bytes per lane: wave w copies the
+  // tile's activation scale words from byte w*BM and weight scale records from
+  // byte 256w (the activation copies overlap and write the same bytes).  Rows
+  // past M read other data; their results are never stored.
+  int ac_i = 0, ac_ks = 0;
+  uint32_t a_off = 0;
+  [[maybe_unused]] uint32_t w_off[T::WCK > 0 ? T::WCK : 1];
+  [[maybe_unused]] uint32_t as_off = 0, ws_off = 0;
+  auto set_a_tile = [&](int i) __attribute__((always_inline)) {
+    int n0, m0;
+    tile_of(i, n0, m0);
+    // the swizzle of row 16k + L/4 depends on L only, so copy c of the wave is copy 0
+    // moved by c * 1 KB
+    const int rr = 16 * (wave * T::ACK) + (lane >> 2);
+    a_off = (uint32_t)(m0 + rr) * kRowBytes + 16u * ((lane & 3) ^ swz(rr));
+    // weight copy q of the workgroup = half (q % 2) of LDS group q / 2 = group g of
+    // row band wn', in the stage's weight area in that order
+#pragma unroll
+    for (int c = 0; c < T::WCK; ++c) {
+      const int q = wave * T::WCK + c, grp = q >> 1;
+      const int band = grp / (T::WLDS > 0 ? T::WLDS : 1), g = grp % (T::WLDS > 0 ? T::WLDS : 1);
+      w_off[c] = (uint32_t)(n0 / 32 + band * T::TN + g) * wgroup + 1024u * (q & 1) + 16u * lane;
+    }
+    if constexpr (T::FMT == FMT_FP4) {
+      as_off = (uint32_t)m0 * 4u + (uint32_t)(wave * T::BM) + 4u * lane;
+      ws_off = (uint32_t)(n0 / 32) * 128u + 256u * wave + 4u * lane;
+    }
+  };
+  auto copy_stage = [&](int slot) __attribute__((always_inline)) {
+    uint8_t* base = lds + slot;
+#pragma unroll
+    for (int c = 0; c < T::WCK; ++c)
+      copy_to_lds<16>(w_rsrc, w_off[c], ac_ks * T::GROUP_BYTES, base + (wave * T::WCK + c) * 1024);
+#pragma unroll
+    for (int c = 0; c < T::ACK; ++c)
+      copy_to_lds<16>(a_rsrc, a_off, ac_ks * a_panel + c * 1024, base + T::A_OFF + (wave * T::ACK + c) * 1024);
+    if constexpr (T::FMT == FMT_FP4) {
+      copy_to_lds<4>(as_rsrc, as_off, ac_ks * as_step, base + T::AS_OFF + wave * T::BM);
+      copy_to_lds<4>(ws_rsrc, ws_off, ac_ks * ws_step, base + T::WS_OFF + 256 * wave);
+    }
+  };
+  auto advance_a = [&]() __attribute__((always_inline)) {
+    if (++ac_ks == nks) {
+      ac_ks = 0;
+      set_a_tile(++ac_i);
+    }
+  };
+  // Copies that only keep the operation count of a prologue half-step uniform.
+  auto pad = [&](auto n_c) __attribute__((always_inline)) {
+    constexpr int n = decltype(n_c)::value;
+#pragma unroll
+    for (int i = 0; i < n; ++i) copy_to_lds<16>(a_rsrc, 16u * lane, 0, lds + T::JUNK_OFF);
+  };
+
+  WUnit<T> ring[T::RING];
+  AFrag<T> fa, fb;
+  Scales<T> sc, sn;
+  v16f acc[T::TN][T::TM];
+
+  // Prologue: the half-steps before step 0, issuing what they would issue in the
+  // steady state (stages 0 .. S-1, units 0 .. RING-2), padded where the target
+  // does not exist yet.
+  set_w_tile(0);
+  set_a_tile(0);
+  constexpr int PRO = T::PRO_HALVES;
+  static_for<0, PRO>([&](auto k_c) __attribute__((always_inline)) {
+    constexpr int h = decltype(k_c)::value - PRO;           // half-step index, negative
+    constexpr int J = h & 1, g = h >> 1;                     // k-step g (floor), second half if J
+    if constexpr (T::FMT == FMT_FP4 || J == 1) {
+      if constexpr (J == 1) {
+        if constexpr (g + S >= 0) {
+          copy_stage(((g + S) % S) * T::STAGE);
+          advance_a();
+        } else {
+          pad(std::integral_constant<int, T::NCOPY>{});
+        }
+      }
+      constexpr int u = T::FMT == FMT_FP4 ? h + T::RING - 1 : g + T::RING - 1;
+      if constexpr (u >= 0) {
+        load_unit<T>(ring[u % T::RING], w_rsrc, wbase, wc_u, (int)wgroup);
+        advance_w();
+      } else {
+        pad(std::integral_constant<int, T::UNIT_LOADS>{});
+      }
+    }
+  });
+  // Stage 0 went out in the second half of step -S; everything issued after that
+  // half may still be in flight.
+  constexpr int PRO_WAIT = []() {
+    int n = 0;
+    for (int h = -2 * S + 2; h < 0; ++h) {
+      const bool second = (h & 1) != 0;
+      n += T::FMT == FMT_FP4 ? (second ? T::OPS_H1 : T::OPS_H0) : (second ? T::OPS_H1 : 0);
+    }
+    return n < 63 ? n : 63;
+  }();
+  static_assert(2 * S - 1 <= PRO, "the prologue issues stage 0");
+  wait_vmcnt<PRO_WAIT>();
+  barrier();
+  load_scales<T>(sc, lds, wn, wm, lane);
+  load_act<T, 0>(fa, lds, wn, wm, lane);
+  select_scales<T>(sc, lane);
+
+  // One k-step.  Step g computes from LDS slot g mod S (byte offset `cur`) and
+  // weight ring slots (units).  The barrier sits between the two halves of the
+  // MFMAs: before it every wave has issued the first half (which keeps the matrix
+  // core busy through the wait); after it stage g+1 is visible to all waves and
+  // slot `cur` is free, so the copy of stage g+S goes there while the second half
+  // runs.  Each half issues its LDS reads before its MFMAs, so the fragments
+  // being read live in other registers than the ones being consumed; weight loads
+  // go into the ring slot consumed one half earlier.  ZERO: the tile's first step,
+  // whose MFMAs start from zero.
+  int cur = 0;
+  auto step = [&](auto si_c, auto zero_c) __attribute__((always_inline)) {
+    constexpr int SI = decltype(si_c)::value;
+    constexpr bool ZERO = decltype(zero_c)::value;
+    const int nxt = cur + T::STAGE == S * T::STAGE ? 0 : cur + T::STAGE;
+    if constexpr (T::FMT == FMT_FP4) {
+      constexpr int u0 = (2 * SI) % T::RING, u1 = u0 + 1;
+      constexpr int l0 = (u0 + T::RING - 1) % T::RING, l1 = u0;
+      wait_vmcnt<T::WAIT_UNIT>();                  // unit u0 has landed
+      __builtin_amdgcn_sched_barrier(0);
+      load_act<T, 1>(fb, lds + cur, wn, wm, lane);
+      load_unit<T>(ring[l0], w_rsrc, wbase, wc_u, (int)wgroup);
+      mfma_part<T, 0, 0, T::TM, ZERO>(acc, ring[u0], fa, sc);
+      spread_vmem<T::TN * T::TM, T::UNIT_LOADS>();
       pin_accumulators<T>(acc);
       __builtin_amdgcn_sched_barrier(0);
+      advance_w();
+      wait_vmcnt<T::WAIT_BARRIER, true>();         // stage g+1 and unit u1 have landed; reads of `cur` done
+      barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      copy_stage(cur);
+      load_unit<T>(ring[l1], w_rsrc, wbase, wc_u, (int)wgroup);
+      load_scales<T>(sn, lds + nxt, wn, wm, lane);
+      load_act<T, 0>(fa, lds + nxt, wn, wm, lane);
+      mfma_part<T, 1, 0, T::TM, false>(acc, ring[u1], fb, sc);
+      spread_vmem<T::TN * T::TM, T::NCOPY + T::UNIT_LOADS>();
+      pin_accumulators<T>(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      advance_w();
+      advance_a();
       sc = sn;
       select_scales<T>(sc, lane);
     } else {
-      load_frags<T, 0>(fb, stage_ptr(ks + 1), wn, wm, lane);
-      mfma_part<T, 0, T::TM / 2, T::TM>(acc, fa, sc);
-      interleave<T::TN * (T::TM - T::TM / 2), NDS>();
+      constexpr int u = SI % T::RING, l = (u + T::RING - 1) % T::RING;
+      wait_vmcnt<T::WAIT_UNIT>();                  // unit u has landed
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_part<T, 0, 0, T::TM / 2, ZERO>(acc, ring[u], fa, sc);
       pin_accumulators<T>(acc);
       __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<T::WAIT_BARRIER, true>();         // stage g+1 has landed; reads of `cur` done
+      barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      copy_stage(cur);
+      load_unit<T>(ring[l], w_rsrc, wbase, wc_u, (int)wgroup);
+      load_act<T, 0>(fb, lds + nxt, wn, wm, lane);
+      mfma_part<T, 0, T::TM / 2, T::TM, ZERO>(acc, ring[u], fa, sc);
+      spread_vmem<T::TN * (T::TM - T::TM / 2), T::NCOPY + T::UNIT_LOADS>();
+      pin_accumulators<T>(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      advance_w();
+      advance_a();
       fa = fb;
     }
+    cur = nxt;
+  };
+
+  constexpr int SPG = T::STEPS_PER_GROUP;
+  for (int i = 0; i < n_mine; ++i) {
+    static_for<0, SPG>([&](auto si_c) __attribute__((always_inline)) {
+      step(si_c, std::integral_constant<bool, decltype(si_c)::value == 0>{});
+    });
+    for (int gi = SPG; gi < nks; gi += SPG)
+      static_for<0, SPG>([&](auto si_c) __attribute__((always_inline)) { step(si_c, std::false_type{}); });
+    int n0, m0;
+    tile_of(i, n0, m0);
+    epilogue<T>(p, acc, n0 + wn * T::WN, m0 + wm * T::WM, lane, wn, wm, lds);
   }
   wait_vmcnt<0>();     // no copy into this workgroup's LDS may outlive it
-  __builtin_amdgcn_sched_barrier(0);
-  epilogue<T>(p, acc, n0 + wn * T::WN, m0 + wm * T::WM, lane);
+}
+
+// Tiles are dealt to one persistent workgroup per CU.
+int cu_count() {
+  static int count = 0;
+  if (count == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      count = n;
+    else
+      count = 256;
+  }
+  return count;
 }
 
 template <class T>
 hipError_t launch(Params& p, hipStream_t stream) {
   p.tiles_m = (p.M + T::BM - 1) / T::BM;
   p.tiles_n = padded_rows(p.N) / T::BN;
-  const int grid = p.tiles_m * p.tiles_n;
+  p.tiles = p.tiles_m * p.tiles_n;
+  const int grid = p.tiles < cu_count() ? p.tiles : cu_count();
   hipLaunchKernelGGL(gemm_kernel<T>, dim3(grid), dim3(T::NT), 0, stream, p);
   return hipGetLastError();
+}
+
+// Token-tile height 192 or 256 (TM = 3 or 4 per wave), whichever gives the fewest
+// rounds of tiles over the CUs, weighted by the tile's work plus a fixed cost of
+// about half a token tile (FP8 always 192: with 256 its operand registers spill);
+// weight ring of 8 units when the k-steps come in groups of 4, else 4.
+template <int FMT, int EPI, int HD = 0, int WLDS = wlds_for(FMT)>
+hipError_t launch_cfg(Params& p, hipStream_t stream) {
+  constexpr int CH = FMT == FMT_FP4 ? 2 : 1;
+  const int nks = p.K / (64 * CH);
+  const int cus = cu_count();
+  const long tn = padded_rows(p.N) / 256;
+  const long r3 = ((p.M + 191) / 192 * tn + cus - 1) / cus, r4 = ((p.M + 255) / 256 * tn + cus - 1) / cus;
+  const bool tm3 = FMT == FMT_FP8 || r3 * 7 < r4 * 9;
+  if (FMT == FMT_FP4 && nks % 4 != 0) {
+    if (tm3) return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
+    return launch<Tile<FMT, EPI, 4, 4, WLDS, HD>>(p, stream);
+  }
+  constexpr int RING = FMT == FMT_FP4 ? 8 : 4;
+  if constexpr (FMT == FMT_FP8) {
+    return launch<Tile<FMT, EPI, 3, RING, WLDS, HD>>(p, stream);
+  } else {
+    if (tm3) return launch<Tile<FMT, EPI, 3, RING, WLDS, HD>>(p, stream);
+    return launch<Tile<FMT, EPI, 4, RING, WLDS, HD>>(p, stream);
+  }
 }
 
 Params make_params(const uint8_t* a_codes, const void* a_scales, const uint8_t* blob, int fmt, int M, int N,
@@ -591,24 +854,24 @@ hipError_t launch_gemm_fp4(const uint8_t* a_codes, const uint8_t* a_scales, cons
   Params p = make_params(a_codes, a_scales, blob, FMT_FP4, M, N, K, out, ldo);
   switch (epi) {
     case EPI_IDENTITY:
-      return launch<Tile<FMT_FP4, EPI_IDENTITY, 128, 64, 2, 4>>(p, stream);
+      return launch_cfg<FMT_FP4, EPI_IDENTITY>(p, stream);
     case EPI_GATED_SILU:
-      return launch<Tile<FMT_FP4, EPI_GATED_SILU, 128, 64, 2, 4>>(p, stream);
+      return launch_cfg<FMT_FP4, EPI_GATED_SILU>(p, stream);
     default:
       p.gamma_q = rms->gamma_q;
       p.gamma_k = rms->gamma_k;
       p.eps = rms->eps;
       p.n_heads = rms->n_heads;
-      if (rms->head_dim == 128) return launch<Tile<FMT_FP4, EPI_QK_RMSNORM, 128, 64, 2, 4>>(p, stream);
-      return launch<Tile<FMT_FP4, EPI_QK_RMSNORM, 256, 32, 1, 8>>(p, stream);
+      if (rms->head_dim == 128) return launch_cfg<FMT_FP4, EPI_QK_RMSNORM, 128>(p, stream);
+      return launch_cfg<FMT_FP4, EPI_QK_RMSNORM, 256>(p, stream);
   }
 }
 
 hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scales, const uint8_t* blob, int M, int N,
                            int K, int epi, uint16_t* out, int ldo, hipStream_t stream) {
   Params p = make_params(a_codes, a_scales, blob, FMT_FP8, M, N, K, out, ldo);
-  if (epi == EPI_GATED_SILU) return launch<Tile<FMT_FP8, EPI_GATED_SILU, 128, 64, 2, 4>>(p, stream);
-  return launch<Tile<FMT_FP8, EPI_IDENTITY, 128, 64, 2, 4>>(p, stream);
+  if (epi == EPI_GATED_SILU) return launch_cfg<FMT_FP8, EPI_GATED_SILU>(p, stream);
+  return launch_cfg<FMT_FP8, EPI_IDENTITY>(p, stream);
 }
 
 }  // namespace ditq
