@@ -147,9 +147,51 @@ def run_gpu(args):
             "quant_fp4_hbm_frac": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / HBM_GBPS, 4),
         },
     }
+    if not args.no_fusion_compare:
+        res["kernels"].update(time_quantized_output(ditq, torch, wl, sets, epi, args))
     if args.all_configs:
         res["other_configs"] = time_other_configs(ditq, torch, args)
     return res, d
+
+
+def time_quantized_output(ditq, torch, wl, sets, epi, args):
+    """The same GEMM when its output feeds another FP4 GEMM: fused (the epilogue
+    writes FP4 codes + E8M0 scales, no bf16) against unfused (bf16 output, then a
+    separate activation-quantizer pass over it).  Back-to-back sustained runs."""
+    M, N, K = wl.M, wl.N, wl.K
+    width = N // 2
+    sptr = torch.cuda.current_stream().cuda_stream
+    qc = torch.empty((width // 128, M, 64), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((width // 128, M, 4), dtype=torch.uint8, device="cuda")
+    n = max(20, args.steps // 4)
+
+    def fused(i):
+        _, blob, codes, scales, _ = sets[i % len(sets)]
+        ditq.dit_gemm_q4_epilogue_q4(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi, None,
+                                     None, 0, qc.data_ptr(), qs.data_ptr(), sptr)
+
+    def unfused(i):
+        _, blob, codes, scales, out = sets[i % len(sets)]
+        ditq.dit_gemm_q4_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi, None,
+                                  out.data_ptr(), width, sptr)
+        ditq.dit_quantize_act(ditq.FMT_FP4, out.data_ptr(), M, width, width, qc.data_ptr(), qs.data_ptr(), sptr)
+
+    times = {}
+    for name, fn in (("fused", fused), ("unfused", unfused)):
+        for i in range(n // 2):
+            fn(i)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        times[name] = sum(a.elapsed_time(b) for a, b in ev) / n * 1e3
+    return {
+        "gemm_q4out_fused_us": round(times["fused"], 2),
+        "gemm_then_quantize_us": round(times["unfused"], 2),
+        "q4out_fusion_saving_us": round(times["unfused"] - times["fused"], 2),
+    }
 
 
 def time_other_configs(ditq, torch, args):
@@ -258,6 +300,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-configs", action="store_true", help="also time the other workloads' kernels")
+    ap.add_argument("--no-fusion-compare", action="store_true",
+                    help="skip the fused vs unfused quantized-output timing (keeps a kernel trace to the timed steps)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of this many MiB first (the reference dispatch that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")

@@ -16,8 +16,9 @@ import os
 __all__ = [
     "FMT_FP4", "FMT_FP8", "EPI_IDENTITY", "EPI_GATED_SILU", "EPI_QK_RMSNORM", "DitError", "RmsNormParams",
     "dit_packed_weight_bytes", "dit_act_code_bytes", "dit_act_scale_bytes", "dit_pack_weights",
-    "dit_quantize_act", "dit_gemm_q4_epilogue", "dit_gemm_q8_epilogue", "dit_status_str", "dit_last_error",
-    "pack_weights", "quantize_act", "gemm", "linear", "library_path", "EXPORTED",
+    "dit_quantize_act", "dit_gemm_q4_epilogue", "dit_gemm_q4_epilogue_q4", "dit_gemm_q8_epilogue",
+    "dit_status_str", "dit_last_error", "pack_weights", "quantize_act", "gemm", "gemm_q4out", "linear",
+    "library_path", "EXPORTED",
 ]
 
 FMT_FP4 = 1
@@ -57,6 +58,8 @@ _SIGS = {
     "dit_pack_weights": (_i, [_i, _i, _p, _i, _i, _i, _p, _p]),
     "dit_quantize_act": (_i, [_i, _p, _i, _i, _i, _p, _p, _p]),
     "dit_gemm_q4_epilogue": (_i, [_p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams), _p, _i, _p]),
+    "dit_gemm_q4_epilogue_q4": (_i, [_p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams), _p, _i, _p, _p,
+                                     _p]),
     "dit_gemm_q8_epilogue": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _i, _p]),
     "dit_status_str": (ctypes.c_char_p, [_i]),
     "dit_last_error": (ctypes.c_char_p, []),
@@ -113,6 +116,13 @@ def dit_gemm_q4_epilogue(a_codes, a_scales, w_packed, M, N, K, epi, rms, out, ld
     rp = ctypes.byref(rms) if rms is not None else None
     _check(_lib.dit_gemm_q4_epilogue(a_codes, a_scales, w_packed, M, N, K, epi, rp, out, ldo, stream),
            "dit_gemm_q4_epilogue")
+
+
+def dit_gemm_q4_epilogue_q4(a_codes, a_scales, w_packed, M, N, K, epi, rms, out, ldo, out_codes, out_scales,
+                            stream=None) -> None:
+    rp = ctypes.byref(rms) if rms is not None else None
+    _check(_lib.dit_gemm_q4_epilogue_q4(a_codes, a_scales, w_packed, M, N, K, epi, rp, out, ldo, out_codes,
+                                        out_scales, stream), "dit_gemm_q4_epilogue_q4")
 
 
 def dit_gemm_q8_epilogue(a_codes, a_scales, w_packed, M, N, K, epi, out, ldo, stream=None) -> None:
@@ -177,6 +187,25 @@ def gemm(codes, scales, blob, N: int, K: int, fmt: int, epi: int, rms: RmsNormPa
         dit_gemm_q8_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi,
                              out.data_ptr(), _ld(out), _stream())
     return out
+
+
+def gemm_q4out(codes, scales, blob, N: int, K: int, epi: int, rms: RmsNormParams | None = None,
+               with_bf16: bool = False):
+    """FP4 GEMM + epilogue whose output is quantized to FP4 for the next GEMM.
+
+    Returns (out_codes, out_scales) in the activation layout of quantize_act (ready
+    to be the next layer's input), plus the bf16 output when with_bf16.
+    """
+    import torch
+    M = codes.shape[1]
+    width = N // 2 if epi == EPI_GATED_SILU else N
+    q_codes = torch.empty((width // 128, M, 64), dtype=torch.uint8, device=codes.device)
+    q_scales = torch.empty((width // 128, M, 4), dtype=torch.uint8, device=codes.device)
+    out = torch.empty((M, width), dtype=torch.bfloat16, device=codes.device) if with_bf16 else None
+    dit_gemm_q4_epilogue_q4(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi, rms,
+                            out.data_ptr() if out is not None else None, _ld(out) if out is not None else 0,
+                            q_codes.data_ptr(), q_scales.data_ptr(), _stream())
+    return (q_codes, q_scales, out) if with_bf16 else (q_codes, q_scales)
 
 
 def linear(x, blob, N: int, fmt: int, epi: int, rms: RmsNormParams | None = None, out=None):

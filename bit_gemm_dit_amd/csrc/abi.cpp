@@ -122,11 +122,15 @@ dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int l
       ditq::launch_quant_fp8(x, M, K, ldx, static_cast<uint8_t*>(codes), static_cast<float*>(scales), st));
 }
 
-dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const void* w_packed, int M, int N,
-                                int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
-                                void* stream) {
-  if (!a_codes || !a_scales || !w_packed || !out_bf16 || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi))
-    return DIT_EINVAL;
+namespace {
+// Checks and launch shared by the two FP4 GEMM entry points.
+dit_status gemm_q4(const void* a_codes, const void* a_scales, const void* w_packed, int M, int N, int K,
+                   dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo, void* out_codes,
+                   void* out_scales, void* stream) {
+  const bool quantized = out_codes != nullptr;
+  if (!a_codes || !a_scales || !w_packed || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi)) return DIT_EINVAL;
+  if (!quantized && !out_bf16) return DIT_EINVAL;
+  if (quantized && !out_scales) return DIT_EINVAL;
   if ((epi == DIT_EPI_QK_RMSNORM) != (rms != nullptr)) return DIT_EINVAL;
   if (rms) {
     if (!rms->gamma_q || !rms->gamma_k || rms->n_heads <= 0 || !(rms->eps > 0.0f)) return DIT_EINVAL;
@@ -135,9 +139,11 @@ dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const
   }
   if (!shape_ok(FMT_FP4, epi, N, K) || !rows_ok(FMT_FP4, M, K)) return DIT_EUNSUPPORTED;
   const int width = epi == DIT_EPI_GATED_SILU ? N / 2 : N;
-  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_packed) || !aligned16(out_bf16) ||
-      ldo < width || ldo % 8 != 0)
-    return DIT_EALIGN;
+  // the quantized output is an FP4 activation of M rows and K' = width columns
+  if (quantized && (width % 256 != 0 || !rows_ok(FMT_FP4, M, width))) return DIT_EUNSUPPORTED;
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_packed)) return DIT_EALIGN;
+  if (out_bf16 && (!aligned16(out_bf16) || ldo < width || ldo % 8 != 0)) return DIT_EALIGN;
+  if (quantized && (!aligned16(out_codes) || !aligned16(out_scales))) return DIT_EALIGN;
   if (rms && (!aligned16(rms->gamma_q) || !aligned16(rms->gamma_k))) return DIT_EALIGN;
   if (dit_status s = check_device()) return s;
   (void)hipGetLastError();
@@ -145,7 +151,23 @@ dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const
   if (rms) r = ditq::RmsArgs{rms->head_dim, rms->n_heads, rms->gamma_q, rms->gamma_k, rms->eps};
   return launched(ditq::launch_gemm_fp4(static_cast<const uint8_t*>(a_codes), static_cast<const uint8_t*>(a_scales),
                                         static_cast<const uint8_t*>(w_packed), M, N, K, epi, rms ? &r : nullptr,
-                                        static_cast<uint16_t*>(out_bf16), ldo, static_cast<hipStream_t>(stream)));
+                                        static_cast<uint16_t*>(out_bf16), ldo, static_cast<uint8_t*>(out_codes),
+                                        static_cast<uint8_t*>(out_scales), static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const void* w_packed, int M, int N,
+                                int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
+                                void* stream) {
+  if (!out_bf16) return DIT_EINVAL;
+  return gemm_q4(a_codes, a_scales, w_packed, M, N, K, epi, rms, out_bf16, ldo, nullptr, nullptr, stream);
+}
+
+dit_status dit_gemm_q4_epilogue_q4(const void* a_codes, const void* a_scales, const void* w_packed, int M, int N,
+                                   int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
+                                   void* out_codes, void* out_scales, void* stream) {
+  if (!out_codes || !out_scales) return DIT_EINVAL;
+  return gemm_q4(a_codes, a_scales, w_packed, M, N, K, epi, rms, out_bf16, ldo, out_codes, out_scales, stream);
 }
 
 dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, const void* w_packed, int M, int N,

@@ -152,9 +152,11 @@ hipError_t launch_quant_fp8(const uint16_t* x, int M, int K, int ldx, uint8_t* c
                             hipStream_t stream);
 hipError_t launch_pack(int fmt, int epi, const uint16_t* w, int N, int K, int ldw, uint8_t* blob,
                        hipStream_t stream);
+// q_codes / q_scales: optional FP4 quantization of the output (null: none);
+// out may be null when q_codes is set.
 hipError_t launch_gemm_fp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* blob, int M,
                            int N, int K, int epi, const RmsArgs* rms, uint16_t* out, int ldo,
-                           hipStream_t stream);
+                           uint8_t* q_codes, uint8_t* q_scales, hipStream_t stream);
 hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scales, const uint8_t* blob, int M,
                            int N, int K, int epi, uint16_t* out, int ldo, hipStream_t stream);
 

@@ -123,7 +123,9 @@ struct Params {
   const void* a_scales;       // FP4: u8 [M][K/32]; FP8: f32 [M]
   const uint8_t* w_codes;     // blob + header
   const void* w_scales;       // FP4: E8M0 groups; FP8: f32 [Np]
-  uint16_t* out;
+  uint16_t* out;              // bf16 output, or null when only the quantized output is wanted
+  uint8_t* q_codes;           // FP4 quantization of the output for the next GEMM, or null
+  uint8_t* q_scales;
   int M, N, K, ldo;
   int tiles_m, tiles_n, tiles;
   uint32_t a_bytes, w_bytes, as_bytes, ws_bytes;
@@ -160,8 +162,17 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 // Store one 32x32 result tile of this lane (16 values, see the layout above) as
 // bf16.  Partner lanes (lane, lane ^ 32) swap half-groups first so that each lane
 // owns two runs of 8 consecutive columns: [8h, 8h+8) and [16+8h, 16+8h+8).
-__device__ inline void store_tile(uint16_t* __restrict__ out, int ldo, int row, bool row_ok, int col0,
-                                  int ncols, int h, const float* v) {
+//
+// With q_codes set, the tile's 32 columns of each token (one E8M0 block) are also
+// quantized to FP4 for the next GEMM, in the activation layout dit_quantize_act
+// writes: the bf16 values (exactly what the bf16 output holds) get the block
+// scale from their largest magnitude, shared by the two partner lanes, and the
+// same E2M1 rounding (page "How fal made Ideogram V4 6x faster", paragraph 2;
+// page "Versnellende diffusiemodellen met TheStage AI", on-the-fly activation
+// scales).  The result equals quantizing the bf16 output, bit for bit.
+template <class T>
+__device__ inline void store_tile(const Params& p, int row, bool row_ok, int col0, int ncols, int h,
+                                  const float* v) {
   uint32_t g[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -178,11 +189,30 @@ __device__ inline void store_tile(uint16_t* __restrict__ out, int ldo, int row, 
     g[4 + d] = t[0];
     g[6 + d] = t[1];
   }
-  if (row_ok) {
-    uint16_t* o = out + (size_t)row * ldo;
-    const int c0 = col0 + 8 * h, c1 = col0 + 16 + 8 * h;
+  const int c0 = col0 + 8 * h, c1 = col0 + 16 + 8 * h;
+  if ((T::FMT == FMT_FP8 || p.out != nullptr) && row_ok) {
+    uint16_t* o = p.out + (size_t)row * p.ldo;
     if (c0 < ncols) *reinterpret_cast<v4i*>(o + c0) = v4i{(int)g[0], (int)g[1], (int)g[2], (int)g[3]};
     if (c1 < ncols) *reinterpret_cast<v4i*>(o + c1) = v4i{(int)g[4], (int)g[5], (int)g[6], (int)g[7]};
+  }
+  if (T::FMT == FMT_FP4 && p.q_codes != nullptr) {
+    const v4i r0 = {(int)g[0], (int)g[1], (int)g[2], (int)g[3]};
+    const v4i r1 = {(int)g[4], (int)g[5], (int)g[6], (int)g[7]};
+    uint32_t m = max(absmax8(r0), absmax8(r1));
+    // permlane32_swap(m, m) gives lanes 32..63 their partner's m in element 0 and
+    // lanes 0..31 theirs in element 1 (the other element is the lane's own m)
+    const auto mm = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    m = max(m, max((uint32_t)mm[0], (uint32_t)mm[1]));
+    const uint32_t byte = fp4_scale_byte(m);
+    const uint32_t q0 = fp4_encode8(r0, byte), q1 = fp4_encode8(r1, byte);
+    if (row_ok && col0 < ncols) {
+      // K-panel-major: panel col/128, byte (col % 128) / 2 of the token's 64-byte row;
+      // the scale byte of block col/32 at byte (col / 32) % 4 of its 4-byte row
+      const size_t prow = (size_t)(col0 >> 7) * p.M + row;
+      *reinterpret_cast<uint32_t*>(p.q_codes + prow * 64 + ((c0 & 127) >> 1)) = q0;
+      *reinterpret_cast<uint32_t*>(p.q_codes + prow * 64 + ((c1 & 127) >> 1)) = q1;
+      if (h == 0) p.q_scales[prow * 4 + ((col0 >> 5) & 3)] = (uint8_t)byte;
+    }
   }
 }
 
@@ -362,7 +392,7 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
               for (int i = 0; i < 4; ++i) v[4 * g + i] *= sa * sw[i];
             }
           }
-          store_tile(p.out, p.ldo, row, ok, n0w + 32 * tn, p.N, h, v);
+          store_tile<T>(p, row, ok, n0w + 32 * tn, p.N, h, v);
         }
       } else {
 #pragma unroll
@@ -389,7 +419,7 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) v[r] = silu(gate[r]) * up[r];
-          store_tile(p.out, p.ldo, row, ok, n0w / 2 + 32 * q, p.N / 2, h, v);
+          store_tile<T>(p, row, ok, n0w / 2 + 32 * q, p.N / 2, h, v);
         }
       }
     }
@@ -413,7 +443,7 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
           float v[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) v[r] = acc[tn][tm][r];
-          store_tile(p.out, p.ldo, row, row < p.M, n0w + 32 * tn, p.N, h, v);
+          store_tile<T>(p, row, row < p.M, n0w + 32 * tn, p.N, h, v);
         }
       }
       return;
@@ -466,7 +496,7 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[4 * g + i] = acc[tn][tm][4 * g + i] * rs * gm[i];
           }
-          store_tile(p.out, p.ldo, row, ok, n0w + 32 * tn, p.N, h, v);
+          store_tile<T>(p, row, ok, n0w + 32 * tn, p.N, h, v);
         }
       }
     }
@@ -814,16 +844,17 @@ hipError_t launch_cfg(Params& p, hipStream_t stream) {
   const long tn = padded_rows(p.N) / 256;
   const long r3 = ((p.M + 191) / 192 * tn + cus - 1) / cus, r4 = ((p.M + 255) / 256 * tn + cus - 1) / cus;
   const bool tm3 = FMT == FMT_FP8 || r3 * 7 < r4 * 9;
-  if (FMT == FMT_FP4 && nks % 4 != 0) {
-    if (tm3) return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
-    return launch<Tile<FMT, EPI, 4, 4, WLDS, HD>>(p, stream);
-  }
-  constexpr int RING = FMT == FMT_FP4 ? 8 : 4;
   if constexpr (FMT == FMT_FP8) {
-    return launch<Tile<FMT, EPI, 3, RING, WLDS, HD>>(p, stream);
+    (void)tm3;
+    (void)nks;
+    return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
   } else {
-    if (tm3) return launch<Tile<FMT, EPI, 3, RING, WLDS, HD>>(p, stream);
-    return launch<Tile<FMT, EPI, 4, RING, WLDS, HD>>(p, stream);
+    if (nks % 4 != 0) {
+      if (tm3) return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
+      return launch<Tile<FMT, EPI, 4, 4, WLDS, HD>>(p, stream);
+    }
+    if (tm3) return launch<Tile<FMT, EPI, 3, 8, WLDS, HD>>(p, stream);
+    return launch<Tile<FMT, EPI, 4, 8, WLDS, HD>>(p, stream);
   }
 }
 
@@ -850,8 +881,11 @@ Params make_params(const uint8_t* a_codes, const void* a_scales, const uint8_t* 
 }  // namespace
 
 hipError_t launch_gemm_fp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* blob, int M, int N,
-                           int K, int epi, const RmsArgs* rms, uint16_t* out, int ldo, hipStream_t stream) {
+                           int K, int epi, const RmsArgs* rms, uint16_t* out, int ldo, uint8_t* q_codes,
+                           uint8_t* q_scales, hipStream_t stream) {
   Params p = make_params(a_codes, a_scales, blob, FMT_FP4, M, N, K, out, ldo);
+  p.q_codes = q_codes;
+  p.q_scales = q_scales;
   switch (epi) {
     case EPI_IDENTITY:
       return launch_cfg<FMT_FP4, EPI_IDENTITY>(p, stream);

@@ -172,6 +172,27 @@ dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const
                                 int M, int N, int K, dit_epi epi, const dit_rmsnorm_params* rms,
                                 void* out_bf16, int ldo, void* stream);
 
+/* ---------------------------------------------------------------- fused GEMM + epilogue + FP4 output
+ * The FP4 GEMM of dit_gemm_q4_epilogue whose epilogue also quantizes its output
+ * for the next GEMM, so the output need not be read back by a separate
+ * dit_quantize_act pass: the small op after each big GEMM is fused so that its
+ * result goes to HBM once, and activations are quantized on the fly (page "How
+ * fal made Ideogram V4 6x faster", paragraphs 2-3).
+ *   y = bf16_RNE(epi(A W^T)) -- the value dit_gemm_q4_epilogue stores --
+ *   (out_codes, out_scales) = FP4 quantization of y exactly as dit_quantize_act
+ *   computes it (same block rule, rounding and K-panel-major layout), for M rows
+ *   and K' = output width (N/2 for GATED_SILU, N otherwise) columns; sizes
+ *   dit_act_code_bytes(FP4, M, K') and dit_act_scale_bytes(FP4, M, K').
+ * out_bf16 may be NULL (then only the quantized output is written and ldo is
+ * ignored); otherwise it is written as by dit_gemm_q4_epilogue.  The quantized
+ * output equals dit_quantize_act applied to that bf16 output, bit for bit.
+ * Supported: as dit_gemm_q4_epilogue, plus K' % 256 == 0; out_codes and
+ * out_scales 16-byte aligned and not aliasing any input. */
+dit_status dit_gemm_q4_epilogue_q4(const void* a_codes, const void* a_scales, const void* w_packed,
+                                   int M, int N, int K, dit_epi epi, const dit_rmsnorm_params* rms,
+                                   void* out_bf16, int ldo, void* out_codes, void* out_scales,
+                                   void* stream);
+
 /* ---------------------------------------------------------------- fused GEMM + epilogue, FP8
  * out = epi((A W^T) * s_a[m] * s_w[n]) with A the E4M3 codes (K-panel-major) and
  * fp32 row scales [M] from dit_quantize_act, W an FP8 blob.  epi is IDENTITY or

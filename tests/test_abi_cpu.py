@@ -80,6 +80,32 @@ def test_gemm_q4_validation():
         assert _q4() == EDEVICE
 
 
+E = 0x50000
+F = 0x60000
+
+
+def _q4q(a=A, s=B, w=C, M=64, N=512, K=256, epi=1, rms=None, out=D, ldo=256, qc=E, qs=F):
+    return ditq._lib.dit_gemm_q4_epilogue_q4(a, s, w, M, N, K, epi, ctypes.byref(rms) if rms else None, out, ldo,
+                                             qc, qs, None)
+
+
+def test_gemm_q4_quantized_output_validation():
+    assert _q4q(qc=None) == EINVAL
+    assert _q4q(qs=None) == EINVAL
+    assert _q4q(a=None) == EINVAL
+    assert _q4q(epi=2) == EINVAL                                     # RMSNorm without params
+    assert _q4q(N=384) == EUNSUP                                     # gated output width 192: not whole k-steps
+    assert _q4q(epi=0, N=320, ldo=320) == EUNSUP                     # identity output width 320
+    assert _q4q(qc=E + 4) == EALIGN
+    assert _q4q(qs=F + 8) == EALIGN
+    assert _q4q(ldo=255) == EALIGN                                   # a bf16 output still needs its ldo
+    # the bf16 output is optional: without it ldo is not looked at
+    if not _has_gpu():
+        assert _q4q(out=None, ldo=0) == EDEVICE
+        assert _q4q() == EDEVICE
+        assert _q4q(epi=2, rms=ditq.RmsNormParams(128, 2, A, B, 1e-6), N=768, ldo=768) == EDEVICE
+
+
 def test_other_entry_points_validation():
     lib = ditq._lib
     assert lib.dit_quantize_act(1, None, 4, 256, 256, B, C, None) == EINVAL
