@@ -18,6 +18,13 @@ FP8: acc[m, n] = (sum_k e4m3(a)[m, k] * e4m3(w)[n, k]) * s_a[m] * s_w[n].  Every
 E4M3 value is a multiple of 2**-9 below 2**9, so every product is a multiple of
 2**-18 below 2**18 and a sum of K <= 2**14 of them fits in 50 bits: the sum is
 exact in float64; the two scale multiplications round once each (~1e-16).
+
+MXFP8: acc[m, n] = sum_k dec(a)[m, k] * dec(w)[n, k], every operand an E4M3 value
+times its block's E8M0 scale.  A product spans up to 36 significant bits, so
+blocks with different scales need not sum exactly in float64; the float64 sum is
+within K * 2**-53 * sum_k |a_k w_k| of the exact value (below 1e-12 relative to
+the sum of magnitudes for K <= 16384), many orders of magnitude under any fp32
+accumulation or bf16 storage error the layer makes.
 """
 from __future__ import annotations
 
@@ -74,4 +81,16 @@ def gemm_fp8(a_codes, a_scales, w_codes, w_scales, rows=None) -> np.ndarray:
         Ad = formats.e4m3_decode(np.asarray(a_codes)[r])
         sa = np.asarray(a_scales, dtype=np.float64)[r]
         out[i:i + ROW_CHUNK] = (Ad @ Wd.T) * sa[:, None] * sw[None, :]
+    return out
+
+
+def gemm_mx8(a_codes, a_scales, w_codes, w_scales, rows=None) -> np.ndarray:
+    """acc = dequant(A) @ dequant(W)^T in float64, MXFP8 operands, [M, N] (or the chosen rows)."""
+    Wd = quant.dequantize_mx8(w_codes, w_scales)
+    sel = np.arange(np.asarray(a_codes).shape[0]) if rows is None else np.asarray(rows)
+    out = np.empty((sel.size, Wd.shape[0]), dtype=np.float64)
+    for i in range(0, sel.size, ROW_CHUNK):
+        r = sel[i:i + ROW_CHUNK]
+        Ad = quant.dequantize_mx8(np.asarray(a_codes)[r], np.asarray(a_scales)[r])
+        out[i:i + ROW_CHUNK] = Ad @ Wd.T
     return out

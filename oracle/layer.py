@@ -18,12 +18,16 @@ def quantize_operands(x_bits, w_bits, fmt: str):
         return quant.quantize_fp4(x_bits), quant.quantize_fp4(w_bits)
     if fmt == "fp8":
         return quant.quantize_fp8(x_bits), quant.quantize_fp8(w_bits)
+    if fmt == "mx8":
+        return quant.quantize_mx8(x_bits), quant.quantize_mx8(w_bits)
     raise ValueError(fmt)
 
 
 def accumulate(a, w, fmt: str, rows=None) -> np.ndarray:
     if fmt == "fp4":
         return gemm.gemm_fp4(a[0], a[1], w[0], w[1], rows=rows)
+    if fmt == "mx8":
+        return gemm.gemm_mx8(a[0], a[1], w[0], w[1], rows=rows)
     return gemm.gemm_fp8(a[0], a[1], w[0], w[1], rows=rows)
 
 

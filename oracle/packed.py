@@ -26,6 +26,9 @@ Layout (all offsets in bytes, little-endian):
   (g * K/64 + c) * 2048; byte 32*L + b holds the E4M3 code of packed row
   32g + L%32 at k = 64c + 32(L//32) + b.
 * FP8 scales: float32 [Np] at scales_offset, in packed row order.
+* MXFP8 codes: as FP8 codes (2048-byte fragments, one E4M3 byte per element).
+* MXFP8 scales: as FP4 scales (128-byte records (s, g), byte 2*L + j = E8M0 scale
+  of packed row 32g + L%32 for the K block 4s + 2j + L//32).
 """
 from __future__ import annotations
 
@@ -33,7 +36,7 @@ import numpy as np
 
 MAGIC = 0x51544944
 HEADER = 256
-FMT_FP4, FMT_FP8 = 1, 2
+FMT_FP4, FMT_FP8, FMT_MX8 = 1, 2, 3
 EPI_IDENTITY, EPI_GATED_SILU, EPI_QK_RMSNORM = 0, 1, 2
 
 
@@ -66,6 +69,7 @@ def decode(blob: np.ndarray, fmt: int, epi: int, N: int, K: int):
 
     FP4: codes uint8 [N, K/2] (low nibble = even k), scales uint8 [N, K/32].
     FP8: codes uint8 [N, K], scales float32 [N].
+    MXFP8: codes uint8 [N, K], scales uint8 [N, K/32].
     """
     b = np.asarray(blob, dtype=np.uint8)
     Np = padded_rows(N)
@@ -80,15 +84,7 @@ def decode(blob: np.ndarray, fmt: int, epi: int, N: int, K: int):
             col0 = (L // 32) * 16                                            # byte offset in the 32-byte chunk
             for c in range(K // 64):
                 rows[r, c * 32 + col0:c * 32 + col0 + 16] = frag[:, c, L, :]
-        sbytes = Np * K // 32
-        sg = b[HEADER + cbytes:HEADER + cbytes + sbytes].reshape(K // 128, G, 64, 2)   # [s][g][L][j]
-        sc = np.empty((Np, K // 32), dtype=np.uint8)
-        for L in range(64):
-            r = np.arange(G) * 32 + L % 32
-            for s in range(K // 128):
-                for j in range(2):
-                    sc[r, 4 * s + 2 * j + L // 32] = sg[s, :, L, j]
-    elif fmt == FMT_FP8:
+    elif fmt in (FMT_FP8, FMT_MX8):
         cbytes = Np * K
         frag = b[HEADER:HEADER + cbytes].reshape(G, K // 64, 64, 32)
         rows = np.empty((Np, K), dtype=np.uint8)
@@ -97,9 +93,19 @@ def decode(blob: np.ndarray, fmt: int, epi: int, N: int, K: int):
             col0 = (L // 32) * 32
             for c in range(K // 64):
                 rows[r, c * 64 + col0:c * 64 + col0 + 32] = frag[:, c, L, :]
-        sc = b[HEADER + cbytes:HEADER + cbytes + 4 * Np].copy().view(np.float32)
     else:
         raise ValueError("unknown format")
+    if fmt == FMT_FP8:
+        sc = b[HEADER + cbytes:HEADER + cbytes + 4 * Np].copy().view(np.float32)
+    else:
+        sbytes = Np * K // 32
+        sg = b[HEADER + cbytes:HEADER + cbytes + sbytes].reshape(K // 128, G, 64, 2)   # [s][g][L][j]
+        sc = np.empty((Np, K // 32), dtype=np.uint8)
+        for L in range(64):
+            r = np.arange(G) * 32 + L % 32
+            for s in range(K // 128):
+                for j in range(2):
+                    sc[r, 4 * s + 2 * j + L // 32] = sg[s, :, L, j]
     codes = np.zeros((N,) + rows.shape[1:], dtype=rows.dtype)
     scales = np.zeros((N,) + sc.shape[1:], dtype=sc.dtype)
     valid = perm >= 0

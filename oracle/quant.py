@@ -26,6 +26,17 @@ B200", engine list: BF16/FP8 mixed precision; page on FLUX.1-dev LoRA inference
     amax = max |x|,  s = fl32(amax / 448)  (s = 1 when amax == 0)
     q    = RNE_E4M3(fl32(x / s))           OCP E4M3, saturating at 448, sign kept.
 
+MXFP8 path (FP8 as the safer precision, pages above; the block structure of the
+4-bit path, so both formats run through the same block-scaled matrix units):
+
+  per row r and per block b of 32 consecutive K elements
+    amax  = max |x| over the block (exact)
+    byte  = clamp(floor(log2 amax) - 8 + 127, 0, 254)      (E8M0 scale); 0 when amax == 0.
+            The "-8" is the exponent of E4M3's largest magnitude (448 = 1.75 * 2**8),
+            so the block maximum lands in [256, 512) and (448, 512) clips to 448.
+    v     = x * 2**-(byte - 127)                             (exact)
+    code  = RNE_E4M3(v), saturating at 448, sign kept.
+
 Every rounding function below exists twice (a closed-form threshold rule and a
 brute-force nearest-point search); the tests require them to agree on every
 input class.
@@ -37,7 +48,9 @@ import numpy as np
 from . import formats
 
 FP4_BLOCK = 32
+MX_BLOCK = 32
 E2M1_EMAX = 2            # largest E2M1 magnitude is 6 = 1.5 * 2**2
+E4M3_EMAX = 8            # largest E4M3 magnitude is 448 = 1.75 * 2**8
 E4M3_MAX = 448.0
 
 
@@ -201,3 +214,44 @@ def quantize_fp8(x_bits: np.ndarray, rounding=e4m3_rne_fields):
 
 def dequantize_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return formats.e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[:, None]
+
+
+# ---------------------------------------------------------------- MXFP8 quantizer
+def mx8_scale_byte(amax: np.ndarray) -> np.ndarray:
+    """E8M0 scale byte of an MXFP8 block with exact maximum magnitude ``amax``:
+    clamp(floor(log2 amax) - 8 + 127, 0, 254), 0 for an all-zero block.  floor(log2)
+    is read off frexp, exact for every float64."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(amax)
+    e = ex.astype(np.int64) - 1 - E4M3_EMAX
+    byte = np.clip(e + 127, 0, 254)
+    return np.where(amax == 0, 0, byte).astype(np.uint8)
+
+
+def quantize_mx8(x_bits: np.ndarray, rounding=e4m3_rne_fields):
+    """Quantize bf16 rows [R, K] (uint16 bits) to E4M3 codes [R, K] with one E8M0
+    scale per 32-element K block, [R, K/32].
+
+    v = x * 2**(127 - byte) is exact in float64.  The rounding functions take fp32;
+    the conversion is exact for every |v| >= 2**-126 (a bf16 significand times a
+    power of two) and below that only moves values that lie far under E4M3's
+    smallest rounding threshold 2**-10, whose code is a signed zero either way.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    R, K = x_bits.shape
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    x = formats.bf16_to_f64(x_bits)
+    _check_finite(x)
+    xb = x.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    scales = mx8_scale_byte(np.abs(xb).max(axis=-1))
+    v = xb * np.ldexp(1.0, 127 - scales.astype(np.int64))[..., None]
+    codes = rounding(v.reshape(R, K).astype(np.float32))
+    return codes, scales
+
+
+def dequantize_mx8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8)
+    R, K = c.shape
+    vals = formats.e4m3_decode(c).reshape(R, K // MX_BLOCK, MX_BLOCK)
+    return (vals * formats.e8m0_decode(scales)[..., None]).reshape(R, K)

@@ -13,6 +13,8 @@ def _write_blob(codes, scales, fmt, epi, N, K):
     perm = packed.row_perm(epi, N, Np)
     if fmt == packed.FMT_FP4:
         cbytes, sbytes = Np * K // 2, Np * K // 32
+    elif fmt == packed.FMT_MX8:
+        cbytes, sbytes = Np * K, Np * K // 32
     else:
         cbytes, sbytes = Np * K, Np * 4
     blob = np.zeros(packed.HEADER + cbytes + sbytes, dtype=np.uint8)
@@ -41,16 +43,26 @@ def _write_blob(codes, scales, fmt, epi, N, K):
                 c, within = k // 64, k % 64
                 L = lane_lo + 32 * (within // 32)
                 blob[256 + (g * (K // 64) + c) * 2048 + 32 * L + within % 32] = codes[n, k]
-            blob[256 + cbytes + 4 * p:256 + cbytes + 4 * p + 4] = np.array([scales[n]], np.float32).view(np.uint8)
+            if fmt == packed.FMT_MX8:
+                for blk in range(K // 32):
+                    s, r = blk // 4, blk % 4
+                    L = lane_lo + 32 * (r % 2)
+                    blob[256 + cbytes + (s * (Np // 32) + g) * 128 + 2 * L + r // 2] = scales[n, blk]
+            else:
+                blob[256 + cbytes + 4 * p:256 + cbytes + 4 * p + 4] = np.array([scales[n]], np.float32).view(np.uint8)
     return blob
 
 
 @pytest.mark.parametrize("fmt,epi,N,K", [(1, 0, 64, 256), (1, 1, 128, 512), (1, 2, 300 - 300 % 32 + 32, 256),
-                                         (2, 0, 96, 256), (2, 1, 128, 256)])
+                                         (2, 0, 96, 256), (2, 1, 128, 256), (3, 0, 96, 256), (3, 1, 128, 512),
+                                         (3, 2, 64, 384)])
 def test_writer_and_decoder_invert(fmt, epi, N, K):
     rng = np.random.default_rng(N + K + fmt)
     if fmt == 1:
         codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        scales = rng.integers(100, 150, (N, K // 32), dtype=np.uint8)
+    elif fmt == 3:
+        codes = rng.integers(0, 256, (N, K), dtype=np.uint8)
         scales = rng.integers(100, 150, (N, K // 32), dtype=np.uint8)
     else:
         codes = rng.integers(0, 256, (N, K), dtype=np.uint8)
