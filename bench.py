@@ -32,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused FP4 GEMM+epilogue TFLOP/s and % of MI355X FP4 MFMA peak, M=4608 K=3072"
-PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0}        # MI355X dense MFMA peaks
+PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "mx8": 5000.0}   # MI355X dense MFMA peaks (MXFP8 runs at the FP8 rate)
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_fp4_mlp_gated_silu.txt")
 GEMM_SRC = os.path.join(ROOT, "bit_gemm_dit_amd", "csrc", "gemm.hip")
@@ -198,13 +198,19 @@ def time_other_configs(ditq, torch, args):
     """GEMM-only and quantizer timings of the other full-size workloads (informational)."""
     from workloads import WORKLOADS, make_inputs
     out = {}
-    plans = [("qkv_rmsnorm_hd128", "qk_rmsnorm"), ("qkv_rmsnorm_hd256", "qk_rmsnorm"),
-             ("fp8_cfg_pair", "identity"), ("fp8_cfg_pair", "gated_silu")]
+    # (workload, epilogue, format: None = the workload's own)
+    plans = [("qkv_rmsnorm_hd128", "qk_rmsnorm", None), ("qkv_rmsnorm_hd256", "qk_rmsnorm", None),
+             ("fp8_cfg_pair", "identity", None), ("fp8_cfg_pair", "gated_silu", None),
+             ("qkv_rmsnorm_hd128", "qk_rmsnorm", "fp8"), ("qkv_rmsnorm_hd256", "qk_rmsnorm", "fp8"),
+             ("mlp_gated_silu", "gated_silu", "mx8"), ("qkv_rmsnorm_hd128", "qk_rmsnorm", "mx8"),
+             ("fp8_cfg_pair", "identity", "mx8")]
     epis = {"identity": 0, "gated_silu": 1, "qk_rmsnorm": 2}
-    for name, epi_name in plans:
+    fmts = {"fp4": ditq.FMT_FP4, "fp8": ditq.FMT_FP8, "mx8": ditq.FMT_MX8}
+    for name, epi_name, fmt_name in plans:
         wl = WORKLOADS[name]
         d = make_inputs(name, seed=0)
-        fmt = ditq.FMT_FP4 if wl.fmt == "fp4" else ditq.FMT_FP8
+        fmt_name = fmt_name or wl.fmt
+        fmt = fmts[fmt_name]
         epi = epis[epi_name]
         x = torch.from_numpy(d["x"].view("int16")).cuda().view(torch.bfloat16)
         w = torch.from_numpy(d["w"].view("int16")).cuda().view(torch.bfloat16)
@@ -238,11 +244,13 @@ def time_other_configs(ditq, torch, args):
         times_q.sort()
         g = times_g[len(times_g) // 2]
         q = times_q[len(times_q) // 2]
-        qbytes = wl.M * wl.K * 2 + (wl.M * wl.K // 2 + wl.M * wl.K // 32 if fmt == 1 else wl.M * wl.K + 4 * wl.M)
-        out[f"{name}/{epi_name}"] = {
+        qbytes = wl.M * wl.K * 2 + {1: wl.M * wl.K // 2 + wl.M * wl.K // 32, 2: wl.M * wl.K + 4 * wl.M,
+                                    3: wl.M * wl.K + wl.M * wl.K // 32}[fmt]
+        key = f"{name}/{epi_name}" + ("" if fmt_name == wl.fmt else f"/{fmt_name}")
+        out[key] = {
             "gemm_us": round(g * 1e3, 2),
             "tflops": round(wl.flops / (g * 1e-3) / 1e12, 1),
-            "frac_of_peak": round(wl.flops / (g * 1e-3) / 1e12 / PEAK_TFLOPS[wl.fmt], 4),
+            "frac_of_peak": round(wl.flops / (g * 1e-3) / 1e12 / PEAK_TFLOPS[fmt_name], 4),
             "quant_us": round(q * 1e3, 2),
             "quant_GBps": round(qbytes / (q * 1e-3) / 1e9, 1),
         }

@@ -14,15 +14,18 @@ import ctypes
 import os
 
 __all__ = [
-    "FMT_FP4", "FMT_FP8", "EPI_IDENTITY", "EPI_GATED_SILU", "EPI_QK_RMSNORM", "DitError", "RmsNormParams",
+    "FMT_FP4", "FMT_FP8", "FMT_MX8", "EPI_IDENTITY", "EPI_GATED_SILU", "EPI_QK_RMSNORM", "DitError",
+    "RmsNormParams",
     "dit_packed_weight_bytes", "dit_act_code_bytes", "dit_act_scale_bytes", "dit_pack_weights",
     "dit_quantize_act", "dit_gemm_q4_epilogue", "dit_gemm_q4_epilogue_q4", "dit_gemm_q8_epilogue",
+    "dit_gemm_epilogue",
     "dit_status_str", "dit_last_error", "pack_weights", "quantize_act", "gemm", "gemm_q4out", "linear",
     "library_path", "EXPORTED",
 ]
 
 FMT_FP4 = 1
 FMT_FP8 = 2
+FMT_MX8 = 3
 EPI_IDENTITY = 0
 EPI_GATED_SILU = 1
 EPI_QK_RMSNORM = 2
@@ -61,6 +64,7 @@ _SIGS = {
     "dit_gemm_q4_epilogue_q4": (_i, [_p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams), _p, _i, _p, _p,
                                      _p]),
     "dit_gemm_q8_epilogue": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _i, _p]),
+    "dit_gemm_epilogue": (_i, [_i, _p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams), _p, _i, _p]),
     "dit_status_str": (ctypes.c_char_p, [_i]),
     "dit_last_error": (ctypes.c_char_p, []),
 }
@@ -130,6 +134,12 @@ def dit_gemm_q8_epilogue(a_codes, a_scales, w_packed, M, N, K, epi, out, ldo, st
            "dit_gemm_q8_epilogue")
 
 
+def dit_gemm_epilogue(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, out, ldo, stream=None) -> None:
+    rp = ctypes.byref(rms) if rms is not None else None
+    _check(_lib.dit_gemm_epilogue(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rp, out, ldo, stream),
+           "dit_gemm_epilogue")
+
+
 # ---------------------------------------------------------------- torch helpers
 def _stream():
     import torch
@@ -165,6 +175,9 @@ def quantize_act(x, fmt: int):
     if fmt == FMT_FP4:
         codes = torch.empty((K // 128, M, 64), dtype=torch.uint8, device=x.device)
         scales = torch.empty((K // 128, M, 4), dtype=torch.uint8, device=x.device)
+    elif fmt == FMT_MX8:
+        codes = torch.empty((K // 64, M, 64), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((K // 128, M, 4), dtype=torch.uint8, device=x.device)
     else:
         codes = torch.empty((K // 64, M, 64), dtype=torch.uint8, device=x.device)
         scales = torch.empty((M,), dtype=torch.float32, device=x.device)
@@ -183,9 +196,12 @@ def gemm(codes, scales, blob, N: int, K: int, fmt: int, epi: int, rms: RmsNormPa
     if fmt == FMT_FP4:
         dit_gemm_q4_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi, rms,
                              out.data_ptr(), _ld(out), _stream())
-    else:
+    elif fmt == FMT_FP8 and epi != EPI_QK_RMSNORM:
         dit_gemm_q8_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi,
                              out.data_ptr(), _ld(out), _stream())
+    else:
+        dit_gemm_epilogue(fmt, codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi, rms,
+                          out.data_ptr(), _ld(out), _stream())
     return out
 
 

@@ -18,10 +18,13 @@ namespace {
 
 using ditq::FMT_FP4;
 using ditq::FMT_FP8;
+using ditq::FMT_MX8;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-bool valid_fmt(int f) { return f == DIT_FMT_FP4_E2M1_MX32 || f == DIT_FMT_FP8_E4M3_ROWCOL; }
+bool valid_fmt(int f) {
+  return f == DIT_FMT_FP4_E2M1_MX32 || f == DIT_FMT_FP8_E4M3_ROWCOL || f == DIT_FMT_FP8_E4M3_MX32;
+}
 bool valid_epi(int e) { return e == DIT_EPI_IDENTITY || e == DIT_EPI_GATED_SILU || e == DIT_EPI_QK_RMSNORM; }
 
 // Shapes the kernels implement.  K: whole 256-element k-steps (FP4 scale groups);
@@ -79,7 +82,6 @@ extern "C" {
 size_t dit_packed_weight_bytes(dit_fmt fmt, dit_epi epi, int N, int K) {
   if (!valid_fmt(fmt) || !valid_epi(epi) || N <= 0 || K <= 0) return 0;
   if (!shape_ok(fmt, epi, N, K)) return 0;
-  if (fmt == DIT_FMT_FP8_E4M3_ROWCOL && epi == DIT_EPI_QK_RMSNORM) return 0;
   return ditq::blob_total_bytes(fmt, ditq::padded_rows(N), K);
 }
 
@@ -90,14 +92,13 @@ size_t dit_act_code_bytes(dit_fmt fmt, int M, int K) {
 
 size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K) {
   if (!valid_fmt(fmt) || M <= 0 || K <= 0 || K % 256 != 0) return 0;
-  return fmt == DIT_FMT_FP4_E2M1_MX32 ? (size_t)M * K / 32 : (size_t)M * 4;
+  return fmt == DIT_FMT_FP8_E4M3_ROWCOL ? (size_t)M * 4 : (size_t)M * K / 32;
 }
 
 dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N, int K, int ldw, void* packed,
                             void* stream) {
   if (!valid_fmt(fmt) || !valid_epi(epi) || !w_bf16 || !packed || N <= 0 || K <= 0) return DIT_EINVAL;
   if (!shape_ok(fmt, epi, N, K)) return DIT_EUNSUPPORTED;
-  if (fmt == DIT_FMT_FP8_E4M3_ROWCOL && epi == DIT_EPI_QK_RMSNORM) return DIT_EUNSUPPORTED;
   if (!aligned16(w_bf16) || !aligned16(packed) || ldw < K || ldw % 8 != 0) return DIT_EALIGN;
   if (dit_status s = check_device()) return s;
   (void)hipGetLastError();
@@ -118,17 +119,22 @@ dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int l
   if (fmt == DIT_FMT_FP4_E2M1_MX32)
     return launched(ditq::launch_quant_fp4(x, M, K, ldx, static_cast<uint8_t*>(codes),
                                            static_cast<uint8_t*>(scales), st));
+  if (fmt == DIT_FMT_FP8_E4M3_MX32)
+    return launched(ditq::launch_quant_mx8(x, M, K, ldx, static_cast<uint8_t*>(codes),
+                                           static_cast<uint8_t*>(scales), st));
   return launched(
       ditq::launch_quant_fp8(x, M, K, ldx, static_cast<uint8_t*>(codes), static_cast<float*>(scales), st));
 }
 
 namespace {
-// Checks and launch shared by the two FP4 GEMM entry points.
-dit_status gemm_q4(const void* a_codes, const void* a_scales, const void* w_packed, int M, int N, int K,
-                   dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo, void* out_codes,
-                   void* out_scales, void* stream) {
+// Checks and launch shared by every GEMM entry point.  out_codes set: the FP4
+// quantization of the output is written too (FP4 only), and out_bf16 may be null.
+dit_status gemm_any(int fmt, const void* a_codes, const void* a_scales, const void* w_packed, int M, int N, int K,
+                    dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo, void* out_codes,
+                    void* out_scales, void* stream) {
   const bool quantized = out_codes != nullptr;
-  if (!a_codes || !a_scales || !w_packed || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi)) return DIT_EINVAL;
+  if (!valid_fmt(fmt) || !a_codes || !a_scales || !w_packed || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi))
+    return DIT_EINVAL;
   if (!quantized && !out_bf16) return DIT_EINVAL;
   if (quantized && !out_scales) return DIT_EINVAL;
   if ((epi == DIT_EPI_QK_RMSNORM) != (rms != nullptr)) return DIT_EINVAL;
@@ -137,11 +143,12 @@ dit_status gemm_q4(const void* a_codes, const void* a_scales, const void* w_pack
     if ((long long)N != 3LL * rms->n_heads * rms->head_dim) return DIT_EINVAL;
     if (rms->head_dim != 128 && rms->head_dim != 256) return DIT_EUNSUPPORTED;
   }
-  if (!shape_ok(FMT_FP4, epi, N, K) || !rows_ok(FMT_FP4, M, K)) return DIT_EUNSUPPORTED;
+  if (!shape_ok(fmt, epi, N, K) || !rows_ok(fmt, M, K)) return DIT_EUNSUPPORTED;
   const int width = epi == DIT_EPI_GATED_SILU ? N / 2 : N;
   // the quantized output is an FP4 activation of M rows and K' = width columns
-  if (quantized && (width % 256 != 0 || !rows_ok(FMT_FP4, M, width))) return DIT_EUNSUPPORTED;
-  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_packed)) return DIT_EALIGN;
+  if (quantized && (fmt != FMT_FP4 || width % 256 != 0 || !rows_ok(FMT_FP4, M, width))) return DIT_EUNSUPPORTED;
+  if (!aligned16(a_codes) || !aligned16(w_packed)) return DIT_EALIGN;
+  if (fmt == FMT_FP8 ? !aligned(a_scales, 4) : !aligned16(a_scales)) return DIT_EALIGN;
   if (out_bf16 && (!aligned16(out_bf16) || ldo < width || ldo % 8 != 0)) return DIT_EALIGN;
   if (quantized && (!aligned16(out_codes) || !aligned16(out_scales))) return DIT_EALIGN;
   if (rms && (!aligned16(rms->gamma_q) || !aligned16(rms->gamma_k))) return DIT_EALIGN;
@@ -149,10 +156,10 @@ dit_status gemm_q4(const void* a_codes, const void* a_scales, const void* w_pack
   (void)hipGetLastError();
   ditq::RmsArgs r{};
   if (rms) r = ditq::RmsArgs{rms->head_dim, rms->n_heads, rms->gamma_q, rms->gamma_k, rms->eps};
-  return launched(ditq::launch_gemm_fp4(static_cast<const uint8_t*>(a_codes), static_cast<const uint8_t*>(a_scales),
-                                        static_cast<const uint8_t*>(w_packed), M, N, K, epi, rms ? &r : nullptr,
-                                        static_cast<uint16_t*>(out_bf16), ldo, static_cast<uint8_t*>(out_codes),
-                                        static_cast<uint8_t*>(out_scales), static_cast<hipStream_t>(stream)));
+  return launched(ditq::launch_gemm(fmt, static_cast<const uint8_t*>(a_codes), a_scales,
+                                    static_cast<const uint8_t*>(w_packed), M, N, K, epi, rms ? &r : nullptr,
+                                    static_cast<uint16_t*>(out_bf16), ldo, static_cast<uint8_t*>(out_codes),
+                                    static_cast<uint8_t*>(out_scales), static_cast<hipStream_t>(stream)));
 }
 }  // namespace
 
@@ -160,31 +167,32 @@ dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const
                                 int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
                                 void* stream) {
   if (!out_bf16) return DIT_EINVAL;
-  return gemm_q4(a_codes, a_scales, w_packed, M, N, K, epi, rms, out_bf16, ldo, nullptr, nullptr, stream);
+  return gemm_any(FMT_FP4, a_codes, a_scales, w_packed, M, N, K, epi, rms, out_bf16, ldo, nullptr, nullptr,
+                  stream);
 }
 
 dit_status dit_gemm_q4_epilogue_q4(const void* a_codes, const void* a_scales, const void* w_packed, int M, int N,
                                    int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
                                    void* out_codes, void* out_scales, void* stream) {
   if (!out_codes || !out_scales) return DIT_EINVAL;
-  return gemm_q4(a_codes, a_scales, w_packed, M, N, K, epi, rms, out_bf16, ldo, out_codes, out_scales, stream);
+  return gemm_any(FMT_FP4, a_codes, a_scales, w_packed, M, N, K, epi, rms, out_bf16, ldo, out_codes, out_scales,
+                  stream);
 }
 
 dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, const void* w_packed, int M, int N,
                                 int K, dit_epi epi, void* out_bf16, int ldo, void* stream) {
   if (!a_codes || !a_scales || !w_packed || !out_bf16 || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi))
     return DIT_EINVAL;
-  if (epi == DIT_EPI_QK_RMSNORM) return DIT_EUNSUPPORTED;
-  if (!shape_ok(FMT_FP8, epi, N, K) || !rows_ok(FMT_FP8, M, K)) return DIT_EUNSUPPORTED;
-  const int width = epi == DIT_EPI_GATED_SILU ? N / 2 : N;
-  if (!aligned16(a_codes) || !aligned(a_scales, 4) || !aligned16(w_packed) || !aligned16(out_bf16) ||
-      ldo < width || ldo % 8 != 0)
-    return DIT_EALIGN;
-  if (dit_status s = check_device()) return s;
-  (void)hipGetLastError();
-  return launched(ditq::launch_gemm_fp8(static_cast<const uint8_t*>(a_codes), a_scales,
-                                        static_cast<const uint8_t*>(w_packed), M, N, K, epi,
-                                        static_cast<uint16_t*>(out_bf16), ldo, static_cast<hipStream_t>(stream)));
+  if (epi == DIT_EPI_QK_RMSNORM) return DIT_EUNSUPPORTED;     // no RMSNorm parameters here
+  return gemm_any(FMT_FP8, a_codes, a_scales, w_packed, M, N, K, epi, nullptr, out_bf16, ldo, nullptr, nullptr,
+                  stream);
+}
+
+dit_status dit_gemm_epilogue(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed, int M,
+                             int N, int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
+                             void* stream) {
+  if (!out_bf16) return DIT_EINVAL;
+  return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, out_bf16, ldo, nullptr, nullptr, stream);
 }
 
 const char* dit_last_error(void) { return g_last_error; }

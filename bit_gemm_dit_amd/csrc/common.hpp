@@ -1,12 +1,13 @@
 // Shared device/host definitions of the fused low-bit linear layer (gfx950).
 //
-// Blob layout constants, vector types and the FP4 / FP8 element encoders used by
-// both the activation quantizer and the weight packer.  The encoders follow the
-// quantization rule documented in include/ditq.h (per 32-element block: E8M0
-// scale = 2^(floor(log2 amax) - 2); element = RNE_E2M1(x / scale); FP8: RNE_E4M3
-// of x / s with s = amax / 448), the formats of page "How fal made Ideogram V4 6x
-// faster" (paragraph 2, a 4-bit float format) and page "WaveSpeedAI X DataCrunch"
-// (engine list, FP8).
+// Blob layout constants, vector types and the FP4 / FP8 / MXFP8 element encoders
+// used by both the activation quantizer and the weight packer.  The encoders follow
+// the quantization rules documented in include/ditq.h (FP4, per 32-element block:
+// E8M0 scale = 2^(floor(log2 amax) - 2), element = RNE_E2M1(x / scale); FP8:
+// RNE_E4M3 of x / s with s = amax / 448; MXFP8, per 32-element block: E8M0 scale
+// = 2^(floor(log2 amax) - 8), element = RNE_E4M3(x / scale)), the formats of page
+// "How fal made Ideogram V4 6x faster" (paragraph 2, a 4-bit float format) and
+// page "WaveSpeedAI X DataCrunch" (engine list, FP8).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,7 +21,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-enum { FMT_FP4 = 1, FMT_FP8 = 2 };
+enum { FMT_FP4 = 1, FMT_FP8 = 2, FMT_MX8 = 3 };
 enum { EPI_IDENTITY = 0, EPI_GATED_SILU = 1, EPI_QK_RMSNORM = 2 };
 
 // ---------------------------------------------------------------- blob layout
@@ -34,7 +35,7 @@ __host__ __device__ inline size_t blob_code_bytes(int fmt, int Np, int K) {
   return fmt == FMT_FP4 ? (size_t)Np * K / 2 : (size_t)Np * K;
 }
 __host__ __device__ inline size_t blob_scale_bytes(int fmt, int Np, int K) {
-  return fmt == FMT_FP4 ? (size_t)Np * K / 32 : (size_t)Np * 4;
+  return fmt == FMT_FP8 ? (size_t)Np * 4 : (size_t)Np * K / 32;
 }
 __host__ __device__ inline size_t blob_scales_offset(int fmt, int Np, int K) {
   return kHeaderBytes + blob_code_bytes(fmt, Np, K);
@@ -129,6 +130,32 @@ __device__ inline uint32_t fp8_encode4(uint32_t w0, uint32_t w1, float s) {
   return (uint32_t)r;
 }
 
+// ---------------------------------------------------------------- MXFP8 encoding
+// E8M0 scale byte of an MXFP8 block from its largest bf16 magnitude (sign cleared):
+// floor(log2 amax) - 8 + 127 clamped at 0 is max(exponent field - 8, 0); subnormal
+// maxima (exponent field 0) clamp to 0 as well.  At most 246 for finite bf16.
+__device__ inline uint32_t mx8_scale_byte(uint32_t amax_bits) {
+  const uint32_t ex = amax_bits >> 7;
+  return ex > 8 ? ex - 8 : 0;
+}
+
+// Four bf16 values -> four E4M3 codes (byte i = element i) for scale byte `byte`:
+// RNE_E4M3(x * 2^(127 - byte)).  The factor is a normal fp32 power of two for every
+// byte <= 246, so the product is exact down to fp32's normal range; smaller
+// products lie far below E4M3's smallest rounding threshold (2^-10) and encode as a
+// signed zero either way.  The clamp is the saturation at 448.
+__device__ inline uint32_t mx8_encode4(uint32_t w0, uint32_t w1, uint32_t byte) {
+  const float f = __uint_as_float((254u - byte) << 23);
+  float a = bf16_lo(w0) * f, b = bf16_hi(w0) * f, c = bf16_lo(w1) * f, d = bf16_hi(w1) * f;
+  a = fmaxf(fminf(a, 448.0f), -448.0f);
+  b = fmaxf(fminf(b, 448.0f), -448.0f);
+  c = fmaxf(fminf(c, 448.0f), -448.0f);
+  d = fmaxf(fminf(d, 448.0f), -448.0f);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
 // ---------------------------------------------------------------- buffer resources
 // Raw buffer descriptors: loads past num_records bytes return zeros, which
 // clips ragged tiles without branches.
@@ -150,14 +177,16 @@ hipError_t launch_quant_fp4(const uint16_t* x, int M, int K, int ldx, uint8_t* c
                             hipStream_t stream);
 hipError_t launch_quant_fp8(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, float* scales,
                             hipStream_t stream);
+hipError_t launch_quant_mx8(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream);
 hipError_t launch_pack(int fmt, int epi, const uint16_t* w, int N, int K, int ldw, uint8_t* blob,
                        hipStream_t stream);
-// q_codes / q_scales: optional FP4 quantization of the output (null: none);
-// out may be null when q_codes is set.
-hipError_t launch_gemm_fp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* blob, int M,
-                           int N, int K, int epi, const RmsArgs* rms, uint16_t* out, int ldo,
-                           uint8_t* q_codes, uint8_t* q_scales, hipStream_t stream);
-hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scales, const uint8_t* blob, int M,
-                           int N, int K, int epi, uint16_t* out, int ldo, hipStream_t stream);
+// Fused GEMM + epilogue in any format.  a_scales: FP4 / MXFP8 E8M0 bytes, FP8 fp32
+// row scales.  rms: non-null exactly for EPI_QK_RMSNORM.  q_codes / q_scales
+// (FP4 only): optional FP4 quantization of the output (null: none); out may be
+// null when q_codes is set.
+hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, const uint8_t* blob, int M, int N,
+                       int K, int epi, const RmsArgs* rms, uint16_t* out, int ldo, uint8_t* q_codes,
+                       uint8_t* q_scales, hipStream_t stream);
 
 }  // namespace ditq

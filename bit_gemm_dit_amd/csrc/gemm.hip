@@ -16,8 +16,9 @@
 //   lane and register of two adjacent tiles.
 // * FP4: v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands (4 VGPRs) and the
 //   E8M0 block scales applied by the instruction (op_sel picks the byte of the
-//   64-K step).  FP8: the same instruction with E4M3 operands (8 VGPRs) and unit
-//   block scales; the fp32 row/column scales are applied in the epilogue.
+//   64-K step).  MXFP8: the same with E4M3 operands (8 VGPRs) and E8M0 block
+//   scales, in the FP4 path's k-step of two 64-K units.  FP8: E4M3 operands and
+//   unit block scales; the fp32 row/column scales are applied in the epilogue.
 // * A workgroup of 4 waves (one per SIMD) computes a 256 (features) x BM (tokens)
 //   tile; wave (wn, wm) owns 128 features x BM/2 tokens (4 x TM result tiles of
 //   32 x 32, TM = 3 or 4, up to 256 accumulators).
@@ -47,8 +48,8 @@ namespace {
 
 constexpr int kRowBytes = 64;    // operand bytes per row per k-step
 // Weight row groups per wave staged through LDS (measured best): FP4 splits the
-// four evenly; FP8, whose MFMAs take twice as long per byte, loads all of them into
-// registers.
+// four evenly; FP8 and MXFP8, whose MFMAs take twice as long per byte, load all of
+// them into registers.
 constexpr int wlds_for(int fmt) { return fmt == FMT_FP4 ? 2 : 0; }
 constexpr int kGroupM = 4;       // tile-order group height (in M tiles)
 
@@ -63,10 +64,12 @@ struct Tile {
   static constexpr int TN = 4, WAVES_N = 2, WAVES_M = 2, NW = 4, NT = 256;
   static constexpr int WN = 32 * TN, WM = 32 * TM;
   static constexpr int BN = WN * WAVES_N, BM = WM * WAVES_M;
-  static constexpr int CH = FMT == FMT_FP4 ? 2 : 1;           // units per k-step
+  static constexpr bool MX = FMT != FMT_FP8;                   // E8M0 block scales applied by the MFMA
+  static constexpr int CH = MX ? 2 : 1;                        // units per k-step
   static constexpr int KSTEP = 64 * CH;
   static constexpr int FRAG = FMT == FMT_FP4 ? 1024 : 2048;    // bytes of one 32x64 operand fragment
   static constexpr int FRAG_LOADS = FRAG / 1024;               // 16-byte loads per lane per fragment
+  static constexpr int APANELS = FMT == FMT_MX8 ? 2 : 1;       // 64-byte activation code panels per k-step
   static constexpr int TND = TN - WLDS;                        // weight groups loaded into registers
   static constexpr int UNIT_LOADS = TND * FRAG_LOADS;
   static constexpr int STEPS_PER_GROUP = RING / CH;            // k-steps per unrolled group
@@ -75,43 +78,49 @@ struct Tile {
   // words | weight scale records
   static constexpr int W_BYTES = WAVES_N * WLDS * GROUP_BYTES;
   static constexpr int A_OFF = W_BYTES;
-  static constexpr int A_BYTES = BM * kRowBytes;
+  static constexpr int A_BYTES = BM * kRowBytes * APANELS;
   static constexpr int AS_OFF = A_OFF + A_BYTES;
-  static constexpr int AS_BYTES = FMT == FMT_FP4 ? (3 * BM + 256 + 255) / 256 * 256 : 0;
+  static constexpr int AS_BYTES = MX ? (3 * BM + 256 + 255) / 256 * 256 : 0;
   static constexpr int WS_OFF = AS_OFF + AS_BYTES;
-  static constexpr int WS_BYTES = FMT == FMT_FP4 ? BN / 32 * 128 : 0;
+  static constexpr int WS_BYTES = MX ? BN / 32 * 128 : 0;
   static constexpr int STAGE = (WS_OFF + WS_BYTES + 255) / 256 * 256;
   static constexpr int STAGES_FIT = (160 * 1024 - 1024 - (HD == 256 ? WAVES_N * BM * 4 : 0)) / STAGE;
-  static constexpr int STAGES = STAGES_FIT < 5 ? STAGES_FIT : 5;
+  static constexpr int WCK = W_BYTES / 1024 / NW;            // 1 KB weight copies per wave per stage
+  static constexpr int ACK = A_BYTES / 1024 / NW;            // 1 KB activation copies per wave per stage
+  static constexpr int ACKP = ACK / APANELS;                   // ... per code panel
+  static constexpr int NCOPY = WCK + ACK + (MX ? 2 : 0);       // + activation / weight scale copies
+  // Memory operations every wave issues per half-step: FP4 / MXFP8 load one unit
+  // per half and copy a stage in the second half; FP8 does both in the second half.
+  static constexpr int OPS_H0 = MX ? UNIT_LOADS : 0;
+  static constexpr int OPS_H1 = NCOPY + UNIT_LOADS;
+  static constexpr int OPS_STEP = OPS_H0 + OPS_H1;
+  // Ring depth: at most 5 stages, as many as fit in LDS, and few enough that the
+  // wait for a stage stays within vmcnt's range (63 operations in flight).
+  static constexpr int STAGES_VM = (63 - OPS_H0) / OPS_STEP + 2;
+  static constexpr int STAGES = STAGES_FIT < 5 ? (STAGES_FIT < STAGES_VM ? STAGES_FIT : STAGES_VM)
+                                               : (5 < STAGES_VM ? 5 : STAGES_VM);
   static constexpr int JUNK_OFF = STAGES * STAGE;            // target of the prologue's padding copies
   static constexpr int RED_OFF = JUNK_OFF + 1024;            // per-token partial sums (head_dim 256)
   static constexpr int RED_BYTES = HD == 256 ? WAVES_N * BM * 4 : 0;
   static constexpr int LDS_BYTES = RED_OFF + RED_BYTES;
-  static constexpr int WCK = W_BYTES / 1024 / NW;            // 1 KB weight copies per wave per stage
-  static constexpr int ACK = A_BYTES / 1024 / NW;            // 1 KB activation copies per wave per stage
-  static constexpr int NCOPY = WCK + ACK + (FMT == FMT_FP4 ? 2 : 0);   // + activation / weight scale copies
-  // Memory operations every wave issues per half-step: FP4 loads one unit per
-  // half and copies a stage in the second half; FP8 does both in the second half.
-  static constexpr int OPS_H0 = FMT == FMT_FP4 ? UNIT_LOADS : 0;
-  static constexpr int OPS_H1 = NCOPY + UNIT_LOADS;
-  static constexpr int OPS_STEP = OPS_H0 + OPS_H1;
   // Waits, as the number of operations that may stay outstanding (vmcnt counts
   // in issue order; the counts below hold whatever the order inside a half).
   //   unit u used in half h: issued in half h - (RING - 1), so the RING - 2 halves
   //   in between were all issued after it (FP8: units are steps, issued in the
   //   second half of step g - (RING - 1)).
-  static constexpr int WAIT_UNIT = FMT == FMT_FP4 ? (RING - 2) / 2 * OPS_STEP : (RING - 2) * OPS_H1;
+  static constexpr int WAIT_UNIT = MX ? (RING - 2) / 2 * OPS_STEP : (RING - 2) * OPS_H1;
   //   stage g+1 (needed at the barrier of step g): issued in the second half of
   //   step g + 1 - STAGES; steps g+2-STAGES .. g-1 and the first half of g follow.
   static constexpr int WAIT_STAGE = (STAGES - 2) * OPS_STEP + OPS_H0;
-  static constexpr int WAIT_BARRIER =
-      FMT == FMT_FP4 ? (WAIT_UNIT < WAIT_STAGE ? WAIT_UNIT : WAIT_STAGE) : WAIT_STAGE;
+  static constexpr int WAIT_BARRIER = MX ? (WAIT_UNIT < WAIT_STAGE ? WAIT_UNIT : WAIT_STAGE) : WAIT_STAGE;
   // prologue: the half-steps before step 0 that issue stage 0 .. STAGES-1 and unit 0 .. RING-2
-  static constexpr int PRO_HALVES = FMT == FMT_FP4 ? (2 * STAGES - 1 > RING - 1 ? 2 * STAGES - 1 : RING - 1)
-                                                   : 2 * (STAGES > RING - 1 ? STAGES : RING - 1);
+  static constexpr int PRO_HALVES = MX ? (2 * STAGES - 1 > RING - 1 ? 2 * STAGES - 1 : RING - 1)
+                                       : 2 * (STAGES > RING - 1 ? STAGES : RING - 1);
   static_assert(A_BYTES == ACK * 1024 * NW && W_BYTES == WCK * 1024 * NW, "whole 1 KB copies per wave");
   static_assert(WLDS >= 0 && WLDS <= TN, "weight groups split between LDS and registers");
-  static_assert(3 * BM + 256 <= AS_BYTES || FMT != FMT_FP4, "overlapping scale-word copies fit");
+  static_assert(3 * BM + 256 <= AS_BYTES || !MX, "overlapping scale-word copies fit");
+  static_assert(ACK % APANELS == 0, "whole activation copies per panel");
+  static_assert(WLDS == 0 || GROUP_BYTES == 2048, "LDS weight groups are copied as two 1 KB halves");
   static_assert(RING % CH == 0 && RING >= 4, "ring holds whole k-steps");
   static_assert(WAIT_UNIT < 64 && WAIT_STAGE < 64, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024 && STAGES >= 3, "LDS");
@@ -120,9 +129,9 @@ struct Tile {
 
 struct Params {
   const uint8_t* a_codes;
-  const void* a_scales;       // FP4: u8 [M][K/32]; FP8: f32 [M]
+  const void* a_scales;       // FP4 / MXFP8: E8M0 u8 [M][K/32]; FP8: f32 [M]
   const uint8_t* w_codes;     // blob + header
-  const void* w_scales;       // FP4: E8M0 groups; FP8: f32 [Np]
+  const void* w_scales;       // FP4 / MXFP8: E8M0 records; FP8: f32 [Np]
   uint16_t* out;              // bf16 output, or null when only the quantized output is wanted
   uint8_t* q_codes;           // FP4 quantization of the output for the next GEMM, or null
   uint8_t* q_scales;
@@ -190,7 +199,7 @@ __device__ inline void store_tile(const Params& p, int row, bool row_ok, int col
     g[6 + d] = t[1];
   }
   const int c0 = col0 + 8 * h, c1 = col0 + 16 + 8 * h;
-  if ((T::FMT == FMT_FP8 || p.out != nullptr) && row_ok) {
+  if ((T::FMT != FMT_FP4 || p.out != nullptr) && row_ok) {
     uint16_t* o = p.out + (size_t)row * p.ldo;
     if (c0 < ncols) *reinterpret_cast<v4i*>(o + c0) = v4i{(int)g[0], (int)g[1], (int)g[2], (int)g[3]};
     if (c1 < ncols) *reinterpret_cast<v4i*>(o + c1) = v4i{(int)g[4], (int)g[5], (int)g[6], (int)g[7]};
@@ -226,8 +235,10 @@ __device__ inline float silu(float x) {
 
 // ---------------------------------------------------------------- operands
 // Activation fragments of one unit (TM token tiles): lane L holds token row
-// wm*WM + 32*tm + L%32, K chunk 32*(L/32) of the unit (FP4: 16 bytes at logical
-// chunk 2J + L/32 of the 64-byte row; FP8: 32 bytes, chunks 2*(L/32), +1).
+// wm*WM + 32*tm + L%32 (FP4: the 16 bytes of K chunk 32*(L/32), logical chunk
+// 2J + L/32 of the 64-byte row; FP8: two 16-byte runs, logical chunks L/32 and
+// 2 + L/32 of the row, in the 8-bit operand order of the MFMA; MXFP8: the same
+// two runs of code panel J).
 template <class T>
 struct AFrag {
   v4i a[T::TM][T::FRAG_LOADS];
@@ -252,8 +263,11 @@ __device__ __forceinline__ void load_act(AFrag<T>& f, const uint8_t* stage, int 
     if constexpr (T::FMT == FMT_FP4) {
       f.a[tm][0] = *reinterpret_cast<const v4i*>(row + 16 * ((2 * J + h) ^ swz(r)));
     } else {
-      f.a[tm][0] = *reinterpret_cast<const v4i*>(row + 16 * ((2 * h) ^ swz(r)));
-      f.a[tm][1] = *reinterpret_cast<const v4i*>(row + 16 * ((2 * h + 1) ^ swz(r)));
+      // 8-bit operands: the MFMA takes k = 16h .. 16h+15 in its first four registers
+      // and k = 32 + 16h .. in the other four (logical chunks h and 2 + h)
+      const uint8_t* prow = row + J * T::BM * kRowBytes;      // MXFP8: unit J's panel (FP8: J = 0)
+      f.a[tm][0] = *reinterpret_cast<const v4i*>(prow + 16 * (h ^ swz(r)));
+      f.a[tm][1] = *reinterpret_cast<const v4i*>(prow + 16 * ((2 + h) ^ swz(r)));
     }
   }
 }
@@ -264,7 +278,7 @@ struct WUnit {
   v4i w[T::TND > 0 ? T::TND : 1][T::FRAG_LOADS];
 };
 
-// Scale words of one k-step (FP4): a weight record's 16-bit word per lane holds the
+// Scale words of one k-step (FP4, MXFP8): a weight record's 16-bit word per lane holds the
 // bytes of units J = 0, 1; two row groups share a register (group tn in bytes
 // 2*(tn%2) + J, picked by op_sel).  A token's 4 scale bytes are its blocks 0..3 of
 // the step, and this lane's units J = 0, 1 take blocks 2J + h (selector byte 0x0C
@@ -277,7 +291,7 @@ struct Scales {
 
 template <class T>
 __device__ __forceinline__ void load_scales(Scales<T>& sc, const uint8_t* stage, int wn, int wm, int lane) {
-  if constexpr (T::FMT == FMT_FP4) {
+  if constexpr (T::MX) {
     const int l32 = lane & 31;
 #pragma unroll
     for (int t2 = 0; t2 < T::TN / 2; ++t2) {
@@ -293,14 +307,14 @@ __device__ __forceinline__ void load_scales(Scales<T>& sc, const uint8_t* stage,
 
 template <class T>
 __device__ __forceinline__ void select_scales(Scales<T>& sc, int lane) {
-  if constexpr (T::FMT == FMT_FP4) {
+  if constexpr (T::MX) {
     const uint32_t sel = (lane & 32) ? 0x0C0C0301u : 0x0C0C0200u;
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) sc.a[tm] = __builtin_amdgcn_perm(0u, sc.a[tm], sel);
   }
 }
 
-// MFMAs of unit J (FP4 op_sel byte) over token tiles [TM0, TM1); ZERO starts the
+// MFMAs of unit J (op_sel byte of the block scales) over token tiles [TM0, TM1); ZERO starts the
 // sums from 0 (first step of a tile) instead of the accumulators.
 template <class T>
 __device__ __forceinline__ v8i operand(const v4i (&x)[T::FRAG_LOADS]) {
@@ -334,6 +348,9 @@ __device__ __forceinline__ void mfma_part(v16f (&acc)[T::TN][T::TM], const WUnit
       if constexpr (T::FMT == FMT_FP4)
         acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             w, operand<T>(f.a[tm]), c, 4, 4, 2 * (tn & 1) + J, (int)sc.w[tn / 2], J, (int)sc.a[tm]);
+      else if constexpr (T::FMT == FMT_MX8)
+        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            w, operand<T>(f.a[tm]), c, 0, 0, 2 * (tn & 1) + J, (int)sc.w[tn / 2], J, (int)sc.a[tm]);
       else
         acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, operand<T>(f.a[tm]), c, 0, 0, 0,
                                                                       0x7F7F7F7F, 0, 0x7F7F7F7F);
@@ -430,6 +447,23 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
     // squares through LDS (both add the same two numbers, so both get the same sum).
     constexpr int D = T::HD;
     static_assert(D == T::WN || D == T::BN, "a head is one wave or one workgroup wide");
+    if constexpr (T::FMT == FMT_FP8) {
+      // the row / column scales first: the norm is taken over the scaled values
+#pragma unroll
+      for (int tm = 0; tm < T::TM; ++tm) {
+        const int row = m0w + 32 * tm + l32;
+        const float sa = reinterpret_cast<const float*>(p.a_scales)[row < p.M ? row : p.M - 1];
+#pragma unroll
+        for (int tn = 0; tn < T::TN; ++tn)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const v4f sw = *reinterpret_cast<const v4f*>(
+                reinterpret_cast<const float*>(p.w_scales) + n0w + 32 * tn + 8 * g + 4 * h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[tn][tm][4 * g + i] *= sa * sw[i];
+          }
+      }
+    }
     const int head = D == T::WN ? n0w / D : (n0w - wn * T::WN) / D;
     const int part = head / p.n_heads;          // 0 = Q, 1 = K, 2 = V, 3 = padding past N
     if (part >= 3) return;                      // uniform over the workgroup when D == BN
@@ -624,9 +658,10 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
     }
   };
   // Activation cursor: tile and k-step of the next stage.  Activation copy c of
-  // wave w = 16 token rows of the K panel (contiguous in the panel-major layout),
+  // wave w = 16 token rows of a K panel (contiguous in the panel-major layout),
   // lane L fetching the logical chunk that the swizzle places at slot L%4 of row
-  // 16(w*ACK + c) + L/4.  FP4 scale copies, 4 bytes per lane: wave w copies the
+  // 16(w*ACKP + c') + L/4, c' = c mod ACKP in panel c / ACKP (MXFP8 copies two
+  // 64-element panels per k-step).  Block-scale copies, 4 bytes per lane: wave w copies the
   // tile's activation scale words from byte w*BM and weight scale records from
   // byte 256w (the activation copies overlap and write the same bytes).  Rows
   // past M read other data; their results are never stored.
@@ -639,7 +674,7 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
     tile_of(i, n0, m0);
     // the swizzle of row 16k + L/4 depends on L only, so copy c of the wave is copy 0
     // moved by c * 1 KB
-    const int rr = 16 * (wave * T::ACK) + (lane >> 2);
+    const int rr = 16 * (wave * T::ACKP) + (lane >> 2);
     a_off = (uint32_t)(m0 + rr) * kRowBytes + 16u * ((lane & 3) ^ swz(rr));
     // weight copy q of the workgroup = half (q % 2) of LDS group q / 2 = group g of
     // row band wn', in the stage's weight area in that order
@@ -649,7 +684,7 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
       const int band = grp / (T::WLDS > 0 ? T::WLDS : 1), g = grp % (T::WLDS > 0 ? T::WLDS : 1);
       w_off[c] = (uint32_t)(n0 / 32 + band * T::TN + g) * wgroup + 1024u * (q & 1) + 16u * lane;
     }
-    if constexpr (T::FMT == FMT_FP4) {
+    if constexpr (T::MX) {
       as_off = (uint32_t)m0 * 4u + (uint32_t)(wave * T::BM) + 4u * lane;
       ws_off = (uint32_t)(n0 / 32) * 128u + 256u * wave + 4u * lane;
     }
@@ -660,9 +695,12 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
     for (int c = 0; c < T::WCK; ++c)
       copy_to_lds<16>(w_rsrc, w_off[c], ac_ks * T::GROUP_BYTES, base + (wave * T::WCK + c) * 1024);
 #pragma unroll
-    for (int c = 0; c < T::ACK; ++c)
-      copy_to_lds<16>(a_rsrc, a_off, ac_ks * a_panel + c * 1024, base + T::A_OFF + (wave * T::ACK + c) * 1024);
-    if constexpr (T::FMT == FMT_FP4) {
+    for (int c = 0; c < T::ACK; ++c) {
+      const int panel = c / T::ACKP, cc = c % T::ACKP;
+      copy_to_lds<16>(a_rsrc, a_off, (ac_ks * T::APANELS + panel) * a_panel + cc * 1024,
+                      base + T::A_OFF + panel * T::BM * kRowBytes + (wave * T::ACKP + cc) * 1024);
+    }
+    if constexpr (T::MX) {
       copy_to_lds<4>(as_rsrc, as_off, ac_ks * as_step, base + T::AS_OFF + wave * T::BM);
       copy_to_lds<4>(ws_rsrc, ws_off, ac_ks * ws_step, base + T::WS_OFF + 256 * wave);
     }
@@ -694,7 +732,7 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
   static_for<0, PRO>([&](auto k_c) __attribute__((always_inline)) {
     constexpr int h = decltype(k_c)::value - PRO;           // half-step index, negative
     constexpr int J = h & 1, g = h >> 1;                     // k-step g (floor), second half if J
-    if constexpr (T::FMT == FMT_FP4 || J == 1) {
+    if constexpr (T::MX || J == 1) {
       if constexpr (J == 1) {
         if constexpr (g + S >= 0) {
           copy_stage(((g + S) % S) * T::STAGE);
@@ -703,7 +741,7 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
           pad(std::integral_constant<int, T::NCOPY>{});
         }
       }
-      constexpr int u = T::FMT == FMT_FP4 ? h + T::RING - 1 : g + T::RING - 1;
+      constexpr int u = T::MX ? h + T::RING - 1 : g + T::RING - 1;
       if constexpr (u >= 0) {
         load_unit<T>(ring[u % T::RING], w_rsrc, wbase, wc_u, (int)wgroup);
         advance_w();
@@ -718,7 +756,7 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
     int n = 0;
     for (int h = -2 * S + 2; h < 0; ++h) {
       const bool second = (h & 1) != 0;
-      n += T::FMT == FMT_FP4 ? (second ? T::OPS_H1 : T::OPS_H0) : (second ? T::OPS_H1 : 0);
+      n += T::MX ? (second ? T::OPS_H1 : T::OPS_H0) : (second ? T::OPS_H1 : 0);
     }
     return n < 63 ? n : 63;
   }();
@@ -743,7 +781,7 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
     constexpr int SI = decltype(si_c)::value;
     constexpr bool ZERO = decltype(zero_c)::value;
     const int nxt = cur + T::STAGE == S * T::STAGE ? 0 : cur + T::STAGE;
-    if constexpr (T::FMT == FMT_FP4) {
+    if constexpr (T::MX) {
       constexpr int u0 = (2 * SI) % T::RING, u1 = u0 + 1;
       constexpr int l0 = (u0 + T::RING - 1) % T::RING, l1 = u0;
       wait_vmcnt<T::WAIT_UNIT>();                  // unit u0 has landed
@@ -834,21 +872,19 @@ hipError_t launch(Params& p, hipStream_t stream) {
 
 // Token-tile height 192 or 256 (TM = 3 or 4 per wave), whichever gives the fewest
 // rounds of tiles over the CUs, weighted by the tile's work plus a fixed cost of
-// about half a token tile (FP8 always 192: with 256 its operand registers spill);
-// weight ring of 8 units when the k-steps come in groups of 4, else 4.
+// about half a token tile (FP8 and MXFP8 always 192: with 256 their operand
+// registers spill); FP4 weight ring of 8 units when the k-steps come in groups of
+// 4, else 4 (FP8 and MXFP8: 4).
 template <int FMT, int EPI, int HD = 0, int WLDS = wlds_for(FMT)>
 hipError_t launch_cfg(Params& p, hipStream_t stream) {
-  constexpr int CH = FMT == FMT_FP4 ? 2 : 1;
-  const int nks = p.K / (64 * CH);
-  const int cus = cu_count();
-  const long tn = padded_rows(p.N) / 256;
-  const long r3 = ((p.M + 191) / 192 * tn + cus - 1) / cus, r4 = ((p.M + 255) / 256 * tn + cus - 1) / cus;
-  const bool tm3 = FMT == FMT_FP8 || r3 * 7 < r4 * 9;
-  if constexpr (FMT == FMT_FP8) {
-    (void)tm3;
-    (void)nks;
+  if constexpr (FMT != FMT_FP4) {
     return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
   } else {
+    const int nks = p.K / 128;
+    const int cus = cu_count();
+    const long tn = padded_rows(p.N) / 256;
+    const long r3 = ((p.M + 191) / 192 * tn + cus - 1) / cus, r4 = ((p.M + 255) / 256 * tn + cus - 1) / cus;
+    const bool tm3 = r3 * 7 < r4 * 9;
     if (nks % 4 != 0) {
       if (tm3) return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
       return launch<Tile<FMT, EPI, 4, 4, WLDS, HD>>(p, stream);
@@ -858,8 +894,28 @@ hipError_t launch_cfg(Params& p, hipStream_t stream) {
   }
 }
 
-Params make_params(const uint8_t* a_codes, const void* a_scales, const uint8_t* blob, int fmt, int M, int N,
-                   int K, uint16_t* out, int ldo) {
+template <int FMT>
+hipError_t launch_epi(Params& p, int epi, const RmsArgs* rms, hipStream_t stream) {
+  switch (epi) {
+    case EPI_IDENTITY:
+      return launch_cfg<FMT, EPI_IDENTITY>(p, stream);
+    case EPI_GATED_SILU:
+      return launch_cfg<FMT, EPI_GATED_SILU>(p, stream);
+    default:
+      p.gamma_q = rms->gamma_q;
+      p.gamma_k = rms->gamma_k;
+      p.eps = rms->eps;
+      p.n_heads = rms->n_heads;
+      if (rms->head_dim == 128) return launch_cfg<FMT, EPI_QK_RMSNORM, 128>(p, stream);
+      return launch_cfg<FMT, EPI_QK_RMSNORM, 256>(p, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, const uint8_t* blob, int M, int N,
+                       int K, int epi, const RmsArgs* rms, uint16_t* out, int ldo, uint8_t* q_codes,
+                       uint8_t* q_scales, hipStream_t stream) {
   const int Np = padded_rows(N);
   Params p{};
   p.a_codes = a_codes;
@@ -867,45 +923,19 @@ Params make_params(const uint8_t* a_codes, const void* a_scales, const uint8_t* 
   p.w_codes = blob + kHeaderBytes;
   p.w_scales = blob + blob_scales_offset(fmt, Np, K);
   p.out = out;
+  p.q_codes = q_codes;
+  p.q_scales = q_scales;
   p.M = M;
   p.N = N;
   p.K = K;
   p.ldo = ldo;
   p.a_bytes = (uint32_t)((size_t)M * (fmt == FMT_FP4 ? K / 2 : K));
   p.w_bytes = (uint32_t)blob_code_bytes(fmt, Np, K);
-  p.as_bytes = (uint32_t)((size_t)M * (fmt == FMT_FP4 ? K / 32 : 4));
+  p.as_bytes = (uint32_t)((size_t)M * (fmt == FMT_FP8 ? 4 : K / 32));
   p.ws_bytes = (uint32_t)blob_scale_bytes(fmt, Np, K);
-  return p;
-}
-
-}  // namespace
-
-hipError_t launch_gemm_fp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* blob, int M, int N,
-                           int K, int epi, const RmsArgs* rms, uint16_t* out, int ldo, uint8_t* q_codes,
-                           uint8_t* q_scales, hipStream_t stream) {
-  Params p = make_params(a_codes, a_scales, blob, FMT_FP4, M, N, K, out, ldo);
-  p.q_codes = q_codes;
-  p.q_scales = q_scales;
-  switch (epi) {
-    case EPI_IDENTITY:
-      return launch_cfg<FMT_FP4, EPI_IDENTITY>(p, stream);
-    case EPI_GATED_SILU:
-      return launch_cfg<FMT_FP4, EPI_GATED_SILU>(p, stream);
-    default:
-      p.gamma_q = rms->gamma_q;
-      p.gamma_k = rms->gamma_k;
-      p.eps = rms->eps;
-      p.n_heads = rms->n_heads;
-      if (rms->head_dim == 128) return launch_cfg<FMT_FP4, EPI_QK_RMSNORM, 128>(p, stream);
-      return launch_cfg<FMT_FP4, EPI_QK_RMSNORM, 256>(p, stream);
-  }
-}
-
-hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scales, const uint8_t* blob, int M, int N,
-                           int K, int epi, uint16_t* out, int ldo, hipStream_t stream) {
-  Params p = make_params(a_codes, a_scales, blob, FMT_FP8, M, N, K, out, ldo);
-  if (epi == EPI_GATED_SILU) return launch_cfg<FMT_FP8, EPI_GATED_SILU>(p, stream);
-  return launch_cfg<FMT_FP8, EPI_IDENTITY>(p, stream);
+  if (fmt == FMT_FP4) return launch_epi<FMT_FP4>(p, epi, rms, stream);
+  if (fmt == FMT_MX8) return launch_epi<FMT_MX8>(p, epi, rms, stream);
+  return launch_epi<FMT_FP8>(p, epi, rms, stream);
 }
 
 }  // namespace ditq

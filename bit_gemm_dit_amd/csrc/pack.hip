@@ -1,7 +1,7 @@
 // Weight packer (gfx950): bf16 W [N, K] -> packed blob (layout in include/ditq.h).
 //
 // The codes are pre-shuffled into the MFMA operand layout: one 1 KB (FP4) or 2 KB
-// (FP8) fragment holds, lane by lane, exactly the registers of one 32x32x64 MFMA
+// (FP8, MXFP8) fragment holds, lane by lane, exactly the registers of one 32x32x64 MFMA
 // operand, so the GEMM copies tiles to LDS and reads fragments with contiguous,
 // conflict-free 16-byte accesses.  For gated-SiLU the rows are permuted so that
 // gate row j and up row j + N/2 sit in the same lane of adjacent 32-row groups:
@@ -61,9 +61,61 @@ __global__ __launch_bounds__(256) void pack_fp4_kernel(const uint16_t* __restric
   sc[((size_t)(c / 2) * (Np / 32) + g) * 128 + 2 * L + (c & 1)] = (uint8_t)byte;
 }
 
+// 8-bit fragments (FP8, MXFP8) hold the K order of the 32x32x64 MFMA's 8-bit
+// operands: lane L's bytes 0..15 are k = 64c + 16h + (0..15) and bytes 16..31 are
+// k = 64c + 32 + 16h + (0..15), h = L/32.  So the 32-element block 64c + 32j is
+// split over the j-th 16-byte halves of both lane groups (whose scale the lanes of
+// group j supply).
+
+// MXFP8: one thread per (fragment, lane), as FP4; the two 16-element runs of a
+// lane belong to blocks 2c and 2c + 1, and each block's maximum is shared with the
+// partner lane L ^ 32 (same row) that holds the block's other run.
+__global__ __launch_bounds__(256) void pack_mx8_kernel(const uint16_t* __restrict__ w, int N, int K,
+                                                       int ldw, int epi, int Np,
+                                                       uint8_t* __restrict__ blob) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t kc = (uint32_t)K / 64;
+  const uint32_t total = (uint32_t)Np / 32 * kc * 64;
+  if (t == 0) write_header(blob, FMT_MX8, epi, N, K, Np);
+  if (t >= total) return;                                  // whole waves: total is a multiple of 64
+  const uint32_t L = t & 63, frag = t >> 6, h = L >> 5;
+  const uint32_t c = frag % kc, g = frag / kc;
+  const int p = (int)(32 * g + (L & 31));
+  const int src = packed_row_source(epi, N, p);            // the same for L and L ^ 32
+  v4i a = {0, 0, 0, 0}, b = a, d = a, e = a;
+  if (src >= 0) {
+    const uint16_t* wr = w + (size_t)src * ldw + 64 * c + 16 * h;
+    a = reinterpret_cast<const v4i*>(wr)[0];
+    b = reinterpret_cast<const v4i*>(wr)[1];
+    d = reinterpret_cast<const v4i*>(wr + 32)[0];
+    e = reinterpret_cast<const v4i*>(wr + 32)[1];
+  }
+  uint32_t m0 = max(absmax8(a), absmax8(b)), m1 = max(absmax8(d), absmax8(e));
+  m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 32));
+  m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 32));
+  const uint32_t byte0 = src >= 0 ? mx8_scale_byte(m0) : 0, byte1 = src >= 0 ? mx8_scale_byte(m1) : 0;
+  v4i lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+  if (src >= 0) {
+    lo.x = (int)mx8_encode4((uint32_t)a.x, (uint32_t)a.y, byte0);
+    lo.y = (int)mx8_encode4((uint32_t)a.z, (uint32_t)a.w, byte0);
+    lo.z = (int)mx8_encode4((uint32_t)b.x, (uint32_t)b.y, byte0);
+    lo.w = (int)mx8_encode4((uint32_t)b.z, (uint32_t)b.w, byte0);
+    hi.x = (int)mx8_encode4((uint32_t)d.x, (uint32_t)d.y, byte1);
+    hi.y = (int)mx8_encode4((uint32_t)d.z, (uint32_t)d.w, byte1);
+    hi.z = (int)mx8_encode4((uint32_t)e.x, (uint32_t)e.y, byte1);
+    hi.w = (int)mx8_encode4((uint32_t)e.z, (uint32_t)e.w, byte1);
+  }
+  uint8_t* dst = blob + kHeaderBytes + (size_t)frag * 2048 + 32 * L;
+  *reinterpret_cast<v4i*>(dst) = lo;
+  *reinterpret_cast<v4i*>(dst + 16) = hi;
+  // scale record (s = c / 2, g), byte 2L + (c % 2): block 2c + L/32, i.e. this lane group's block
+  uint8_t* sc = blob + blob_scales_offset(FMT_MX8, Np, K);
+  sc[((size_t)(c / 2) * (Np / 32) + g) * 128 + 2 * L + (c & 1)] = (uint8_t)(h ? byte1 : byte0);
+}
+
 // FP8: one wave per packed row.  Pass 1 finds the row's amax (-> s_w), pass 2
-// encodes 32-element pieces; piece q of the row lands in fragment (g, q/2), lane
-// p%32 + 32*(q%2).
+// encodes 16-element runs; run r (k = 16r ..) lands in fragment (g, r/4), lane
+// p%32 + 32*(r%2), byte 16*((r/2)%2) (the 8-bit fragment order above).
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const uint16_t* __restrict__ w, int N, int K,
                                                        int ldw, int epi, int Np,
                                                        uint8_t* __restrict__ blob) {
@@ -75,12 +127,12 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const uint16_t* __restric
   float* sw = reinterpret_cast<float*>(blob + blob_scales_offset(FMT_FP8, Np, K));
   const int g = p / 32, kc = K / 64;
   const int lane_in_frag = p & 31;
+  auto run_dst = [&](int r) {
+    return blob + kHeaderBytes + ((size_t)g * kc + r / 4) * 2048 + 32 * (lane_in_frag + 32 * (r & 1)) +
+           16 * ((r >> 1) & 1);
+  };
   if (src < 0) {
-    for (int q = lane; q < K / 32; q += 64) {
-      uint8_t* d = blob + kHeaderBytes + ((size_t)g * kc + q / 2) * 2048 + 32 * (lane_in_frag + 32 * (q & 1));
-      *reinterpret_cast<v4i*>(d) = v4i{0, 0, 0, 0};
-      *reinterpret_cast<v4i*>(d + 16) = v4i{0, 0, 0, 0};
-    }
+    for (int r = lane; r < K / 16; r += 64) *reinterpret_cast<v4i*>(run_dst(r)) = v4i{0, 0, 0, 0};
     if (lane == 0) sw[p] = 0.0f;
     return;
   }
@@ -91,21 +143,15 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const uint16_t* __restric
   for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
   const float s = fp8_row_scale(m);
   if (lane == 0) sw[p] = s;
-  for (int q = lane; q < K / 32; q += 64) {
-    const v4i* wp = reinterpret_cast<const v4i*>(wr + 32 * q);
-    v4i lo, hi;
-    const v4i a = wp[0], b = wp[1], c = wp[2], d = wp[3];
-    lo.x = (int)fp8_encode4((uint32_t)a.x, (uint32_t)a.y, s);
-    lo.y = (int)fp8_encode4((uint32_t)a.z, (uint32_t)a.w, s);
-    lo.z = (int)fp8_encode4((uint32_t)b.x, (uint32_t)b.y, s);
-    lo.w = (int)fp8_encode4((uint32_t)b.z, (uint32_t)b.w, s);
-    hi.x = (int)fp8_encode4((uint32_t)c.x, (uint32_t)c.y, s);
-    hi.y = (int)fp8_encode4((uint32_t)c.z, (uint32_t)c.w, s);
-    hi.z = (int)fp8_encode4((uint32_t)d.x, (uint32_t)d.y, s);
-    hi.w = (int)fp8_encode4((uint32_t)d.z, (uint32_t)d.w, s);
-    uint8_t* dst = blob + kHeaderBytes + ((size_t)g * kc + q / 2) * 2048 + 32 * (lane_in_frag + 32 * (q & 1));
-    *reinterpret_cast<v4i*>(dst) = lo;
-    *reinterpret_cast<v4i*>(dst + 16) = hi;
+  for (int r = lane; r < K / 16; r += 64) {
+    const v4i* wp = reinterpret_cast<const v4i*>(wr + 16 * r);
+    const v4i a = wp[0], b = wp[1];
+    v4i q;
+    q.x = (int)fp8_encode4((uint32_t)a.x, (uint32_t)a.y, s);
+    q.y = (int)fp8_encode4((uint32_t)a.z, (uint32_t)a.w, s);
+    q.z = (int)fp8_encode4((uint32_t)b.x, (uint32_t)b.y, s);
+    q.w = (int)fp8_encode4((uint32_t)b.z, (uint32_t)b.w, s);
+    *reinterpret_cast<v4i*>(run_dst(r)) = q;
   }
 }
 
@@ -114,10 +160,10 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const uint16_t* __restric
 hipError_t launch_pack(int fmt, int epi, const uint16_t* w, int N, int K, int ldw, uint8_t* blob,
                        hipStream_t stream) {
   const int Np = padded_rows(N);
-  if (fmt == FMT_FP4) {
+  if (fmt == FMT_FP4 || fmt == FMT_MX8) {
     const uint32_t total = (uint32_t)Np / 32 * ((uint32_t)K / 64) * 64;
-    hipLaunchKernelGGL(pack_fp4_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, w, N, K, ldw, epi,
-                       Np, blob);
+    hipLaunchKernelGGL(fmt == FMT_FP4 ? pack_fp4_kernel : pack_mx8_kernel, dim3((total + 255) / 256), dim3(256), 0,
+                       stream, w, N, K, ldw, epi, Np, blob);
   } else {
     hipLaunchKernelGGL(pack_fp8_kernel, dim3((Np + 3) / 4), dim3(256), 0, stream, w, N, K, ldw, epi, Np,
                        blob);

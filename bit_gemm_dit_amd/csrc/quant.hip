@@ -8,11 +8,13 @@
 // 6x faster", paragraph 2.
 // FP8: bf16 [M, K] -> E4M3 codes (K-panel-major) + fp32 row scales [M] (page "WaveSpeedAI
 // X DataCrunch", engine list: FP8 mixed precision).
+// MXFP8: bf16 [M, K] -> E4M3 codes (the FP8 code layout) + E8M0 block-32 scales (the
+// FP4 scale layout), scales computed per call like the FP4 path's.
 //
-// Both kernels are HBM-bound streams: 2 bytes read per element, 0.5 + 1/32 (FP4)
-// or 1 (FP8) byte written.  Outputs are K-panel-major (include/ditq.h): the GEMM
-// then copies each 64-byte-per-token panel slice of a token tile as one
-// contiguous run.
+// All kernels are HBM-bound streams: 2 bytes read per element, 0.5 + 1/32 (FP4),
+// 1 (FP8) or 1 + 1/32 (MXFP8) bytes written.  Outputs are K-panel-major
+// (include/ditq.h): the GEMM then copies each 64-byte-per-token panel slice of a
+// token tile as one contiguous run.
 #include "common.hpp"
 
 namespace ditq {
@@ -43,6 +45,30 @@ __global__ __launch_bounds__(256) void quant_fp4_kernel(const uint16_t* __restri
     const size_t prow = (size_t)(col >> 4) * M + row;              // panel-major row index
     *reinterpret_cast<uint32_t*>(codes + prow * 64 + 4 * (col & 15)) = fp4_encode8(v, byte);
     if ((threadIdx.x & 3) == 0) scales[prow * 4 + ((col >> 2) & 3)] = (uint8_t)byte;
+  }
+}
+
+// MXFP8: the FP4 kernel's thread and quad structure with E4M3 elements.  Chunk
+// `col` (8 elements) of a row sits in 64-element code panel col/8 at byte
+// 8*(col%8) of the token's 64-byte panel row; its block scale goes to 128-element
+// scale panel col/16, byte (col/4)%4 of the token's 4-byte panel row.
+__global__ __launch_bounds__(256) void quant_mx8_kernel(const uint16_t* __restrict__ x, int M, int ldx,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales, uint32_t total,
+                                                        uint32_t per_row) {
+  const uint32_t stride = gridDim.x * 256u;
+  for (uint32_t c = blockIdx.x * 256u + threadIdx.x; c < total; c += stride) {
+    const uint32_t row = c / per_row, col = c - row * per_row;
+    const v4i v = *reinterpret_cast<const v4i*>(x + (size_t)row * ldx + (size_t)col * 8);
+    uint32_t m = absmax8(v);
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kQuadXor1, 0xF, 0xF, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kQuadXor2, 0xF, 0xF, false));
+    const uint32_t byte = mx8_scale_byte(m);
+    uint2 q;
+    q.x = mx8_encode4((uint32_t)v.x, (uint32_t)v.y, byte);
+    q.y = mx8_encode4((uint32_t)v.z, (uint32_t)v.w, byte);
+    *reinterpret_cast<uint2*>(codes + ((size_t)(col >> 3) * M + row) * 64 + 8 * (col & 7)) = q;
+    if ((threadIdx.x & 3) == 0) scales[((size_t)(col >> 4) * M + row) * 4 + ((col >> 2) & 3)] = (uint8_t)byte;
   }
 }
 
@@ -119,6 +145,18 @@ hipError_t launch_quant_fp4(const uint16_t* x, int M, int K, int ldx, uint8_t* c
   const uint32_t cap = 256u * 32u;                        // 256 CUs x 32 blocks of 4 waves
   if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(quant_fp4_kernel, dim3(blocks), dim3(256), 0, stream, x, M, ldx, codes, scales, total,
+                     per_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mx8(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream) {
+  const uint32_t per_row = (uint32_t)K / 8;
+  const uint32_t total = (uint32_t)M * per_row;
+  uint32_t blocks = (total + 255) / 256;
+  const uint32_t cap = 256u * 32u;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(quant_mx8_kernel, dim3(blocks), dim3(256), 0, stream, x, M, ldx, codes, scales, total,
                      per_row);
   return hipGetLastError();
 }

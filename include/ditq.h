@@ -3,8 +3,9 @@
  * on AMD MI355X (gfx950).
  *
  * The layer: bf16 activations are quantized on the fly to a 4-bit float (FP4
- * E2M1, one E8M0 scale per 32 consecutive K elements) or to FP8 E4M3 (one fp32
- * scale per row); they are multiplied with pre-packed low-bit weights on the
+ * E2M1, one E8M0 scale per 32 consecutive K elements), to FP8 E4M3 with one fp32
+ * scale per row, or to MXFP8 (E4M3, one E8M0 scale per 32 K elements); they are
+ * multiplied with pre-packed low-bit weights on the
  * scaled MFMA units; the small op that follows the GEMM (identity, gated-SiLU,
  * per-head QK-RMSNorm) is applied to the fp32 accumulator before the single bf16
  * store.  Sources: page "How fal made Ideogram V4 6x faster" (news.ditty.ir),
@@ -49,7 +50,8 @@ typedef enum {
 
 typedef enum {
   DIT_FMT_FP4_E2M1_MX32 = 1,   /* E2M1 codes + one E8M0 scale per 32 K elements */
-  DIT_FMT_FP8_E4M3_ROWCOL = 2  /* OCP E4M3 codes + fp32 per-row / per-column scales */
+  DIT_FMT_FP8_E4M3_ROWCOL = 2, /* OCP E4M3 codes + fp32 per-row / per-column scales */
+  DIT_FMT_FP8_E4M3_MX32 = 3    /* OCP E4M3 codes + one E8M0 scale per 32 K elements (MXFP8) */
 } dit_fmt;
 
 typedef enum {
@@ -80,11 +82,13 @@ typedef struct {
  * Pure arithmetic, no device access; 0 means "unsupported arguments". */
 
 /* Bytes of the packed weight blob written by dit_pack_weights.  Rows are padded
- * to Np = ceil(N / 256) * 256.  FP4: 256 + Np*K/2 + Np*K/32.  FP8: 256 + Np*K + 4*Np. */
+ * to Np = ceil(N / 256) * 256.  FP4: 256 + Np*K/2 + Np*K/32.  FP8: 256 + Np*K + 4*Np.
+ * MXFP8: 256 + Np*K + Np*K/32. */
 size_t dit_packed_weight_bytes(dit_fmt fmt, dit_epi epi, int N, int K);
 
 /* Bytes of the activation codes / scales written by dit_quantize_act.
- * FP4: codes M*K/2, scales M*K/32.  FP8: codes M*K, scales 4*M. */
+ * FP4: codes M*K/2, scales M*K/32.  FP8: codes M*K, scales 4*M.  MXFP8: codes M*K,
+ * scales M*K/32. */
 size_t dit_act_code_bytes(dit_fmt fmt, int M, int K);
 size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
 
@@ -97,9 +101,9 @@ size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
  * called with DIT_EPI_GATED_SILU too.  Blobs packed for IDENTITY and QK_RMSNORM
  * are identical and interchangeable.
  *
- * Quantization rule, per weight row: FP4 -- the same rule as dit_quantize_act
- * along K; FP8 -- s_w[n] = fl32(amax_n / 448) (1 if the row is zero), codes
- * RNE_E4M3(fl32(w / s_w[n])).
+ * Quantization rule, per weight row: FP4 and MXFP8 -- the same rule as
+ * dit_quantize_act along K; FP8 -- s_w[n] = fl32(amax_n / 448) (1 if the row is
+ * zero), codes RNE_E4M3(fl32(w / s_w[n])).
  *
  * Blob layout (little-endian; the GEMM relies on it, tests decode it):
  *   header, 256 bytes: u32 magic 0x51544944 ("DITQ"), u32 layout version 2,
@@ -122,8 +126,13 @@ size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
  *     picked with op_sel), so one K step of 256 packed rows is 1 KB contiguous.
  *   FP8 codes: 2048-byte fragments (g, c) at 256 + (g*K/64 + c)*2048; byte
  *     32*L + b holds the E4M3 code of packed row 32g + L%32 at
- *     k = 64c + 32*(L/32) + b.
+ *     k = 64c + 32*(b/16) + 16*(L/32) + b%16 (the 8-bit operand order of the
+ *     32x32x64 MFMA: each lane holds two 16-element runs, and the 32-element
+ *     block 64c + 32j is the j-th run of both lane groups).
  *   FP8 scales: fp32 [Np] at the scales offset, in packed row order.
+ *   MXFP8 codes: the FP8 code layout.  MXFP8 scales: the FP4 scale layout (128-byte
+ *     records (s, g), byte 2*L + j = the E8M0 scale of packed row 32g + L%32 for
+ *     the K block 4s + 2j + L/32).
  *
  * Supported: K % 256 == 0; N % 64 == 0 (GATED_SILU: N % 128 == 0); ldw >= K,
  * ldw % 8 == 0; w_bf16 and packed 16-byte aligned.  W must be finite. */
@@ -151,9 +160,16 @@ dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N,
  *   RNE_E4M3(fl32(x / s)), both divisions IEEE fp32.  Codes K-panel-major with
  *   64-element panels: byte (s*M + m)*64 + k%64, s = k / 64, holds token m's code
  *   at k; scales fp32 [M].
+ * MXFP8 (FP8 in the block-scaled structure of the FP4 path):
+ *   per row and per 32-element K block: amax = max |x|;
+ *   scale byte = clamp(floor(log2 amax) - 8 + 127, 0, 254), 0 if amax == 0 (the
+ *   8 is the exponent of E4M3's largest magnitude, 448 = 1.75 * 2^8);
+ *   code = RNE_E4M3(min(|x| / 2^(byte-127), 448)) with the sign of x.
+ *   Codes in the FP8 layout (64-element panels); scales in the FP4 layout
+ *   (byte (s*M + m)*4 + (k%128)/32, s = k / 128).
  *
  * Supported: K % 256 == 0, ldx >= K, ldx % 8 == 0, pointers 16-byte aligned
- * (FP4 scales: any alignment).  x must be finite. */
+ * (FP4 and MXFP8 scales: any alignment).  x must be finite. */
 dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int ldx,
                             void* codes, void* scales, void* stream);
 
@@ -196,11 +212,31 @@ dit_status dit_gemm_q4_epilogue_q4(const void* a_codes, const void* a_scales, co
 /* ---------------------------------------------------------------- fused GEMM + epilogue, FP8
  * out = epi((A W^T) * s_a[m] * s_w[n]) with A the E4M3 codes (K-panel-major) and
  * fp32 row scales [M] from dit_quantize_act, W an FP8 blob.  epi is IDENTITY or
- * GATED_SILU (QK_RMSNORM returns DIT_EUNSUPPORTED).  Same shape rules as the FP4
- * entry point (a_scales 4-byte aligned). */
+ * GATED_SILU (QK_RMSNORM, which needs its parameters, returns DIT_EUNSUPPORTED
+ * here; dit_gemm_epilogue takes them).  Same shape rules as the FP4 entry point
+ * (a_scales 4-byte aligned). */
 dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, const void* w_packed,
                                 int M, int N, int K, dit_epi epi,
                                 void* out_bf16, int ldo, void* stream);
+
+/* ---------------------------------------------------------------- fused GEMM + epilogue, any format
+ * The GEMM + epilogue of the entry points above for every format and epilogue:
+ *   fmt = DIT_FMT_FP4_E2M1_MX32: exactly dit_gemm_q4_epilogue;
+ *   fmt = DIT_FMT_FP8_E4M3_ROWCOL: dit_gemm_q8_epilogue (a_scales: fp32 [M]),
+ *     plus QK_RMSNORM, applied to (A W^T) * s_a[m] * s_w[n];
+ *   fmt = DIT_FMT_FP8_E4M3_MX32: out = epi(A W^T), A and W MXFP8 (E4M3 codes with
+ *     E8M0 block scales applied inside the product, as for FP4), every epilogue.
+ * FP8 as the safer precision beside the 4-bit format: page "WaveSpeedAI X
+ * DataCrunch: FLUX real-time image inference on B200", engine list; page on
+ * FLUX.1-dev inference optimization with LoRA (aitime.ge), FP8 quantization as
+ * the best speed / memory trade-off.  The epilogues: page "How fal made Ideogram
+ * V4 6x faster", paragraphs 3-4.
+ * A and W must come from dit_quantize_act / dit_pack_weights with the same fmt
+ * (W packed for the same epi family).  Arguments, shapes, alignment and error
+ * codes as dit_gemm_q4_epilogue (FP8 row scales: 4-byte aligned). */
+dit_status dit_gemm_epilogue(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed,
+                             int M, int N, int K, dit_epi epi, const dit_rmsnorm_params* rms,
+                             void* out_bf16, int ldo, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* dit_status_str(dit_status status);

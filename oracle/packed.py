@@ -24,7 +24,8 @@ Layout (all offsets in bytes, little-endian):
   E8M0 scale of packed row 32g + L%32 for the 32-element K block 4s + 2j + L//32.
 * FP8 codes: 2048-byte fragments, fragment (g, c) at codes_offset +
   (g * K/64 + c) * 2048; byte 32*L + b holds the E4M3 code of packed row
-  32g + L%32 at k = 64c + 32(L//32) + b.
+  32g + L%32 at k = 64c + 32(b//16) + 16(L//32) + b%16 (two 16-element runs
+  per lane).
 * FP8 scales: float32 [Np] at scales_offset, in packed row order.
 * MXFP8 codes: as FP8 codes (2048-byte fragments, one E4M3 byte per element).
 * MXFP8 scales: as FP4 scales (128-byte records (s, g), byte 2*L + j = E8M0 scale
@@ -90,9 +91,10 @@ def decode(blob: np.ndarray, fmt: int, epi: int, N: int, K: int):
         rows = np.empty((Np, K), dtype=np.uint8)
         for L in range(64):
             r = np.arange(G) * 32 + L % 32
-            col0 = (L // 32) * 32
             for c in range(K // 64):
-                rows[r, c * 64 + col0:c * 64 + col0 + 32] = frag[:, c, L, :]
+                for run in range(2):                                         # bytes 16*run .. 16*run + 15
+                    k0 = c * 64 + 32 * run + 16 * (L // 32)
+                    rows[r, k0:k0 + 16] = frag[:, c, L, 16 * run:16 * run + 16]
     else:
         raise ValueError("unknown format")
     if fmt == FMT_FP8:

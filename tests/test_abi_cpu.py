@@ -43,8 +43,13 @@ def test_size_queries():
     assert ditq.dit_packed_weight_bytes(2, 0, 12288, 3072) == 256 + 12288 * 3072 + 12288 * 4
     assert ditq.dit_packed_weight_bytes(1, 0, 64, 128) == 0          # K % 256
     assert ditq.dit_packed_weight_bytes(1, 1, 64, 256) == 0          # gated needs N % 128
-    assert ditq.dit_packed_weight_bytes(2, 2, 384, 256) == 0         # FP8 has no RMSNorm epilogue
-    assert ditq.dit_packed_weight_bytes(3, 0, 64, 256) == 0
+    assert ditq.dit_packed_weight_bytes(2, 2, 384, 256) == 256 + 512 * 256 + 512 * 4   # = the identity blob
+    assert ditq.dit_packed_weight_bytes(3, 0, 64, 256) == 256 + 256 * 256 + 256 * 8    # MXFP8
+    assert ditq.dit_packed_weight_bytes(3, 1, 16384, 3072) == 256 + 16384 * 3072 + 16384 * 96
+    assert ditq.dit_act_code_bytes(3, 4608, 3072) == 4608 * 3072
+    assert ditq.dit_act_scale_bytes(3, 4608, 3072) == 4608 * 96
+    assert ditq.dit_packed_weight_bytes(4, 0, 64, 256) == 0          # no such format
+    assert ditq.dit_act_code_bytes(4, 64, 256) == 0
     assert ditq.dit_act_code_bytes(1, 0, 256) == 0
 
 
@@ -109,24 +114,58 @@ def test_gemm_q4_quantized_output_validation():
 def test_other_entry_points_validation():
     lib = ditq._lib
     assert lib.dit_quantize_act(1, None, 4, 256, 256, B, C, None) == EINVAL
-    assert lib.dit_quantize_act(3, A, 4, 256, 256, B, C, None) == EINVAL
+    assert lib.dit_quantize_act(4, A, 4, 256, 256, B, C, None) == EINVAL
+    assert lib.dit_quantize_act(3, A, 4, 256, 256, None, C, None) == EINVAL
+    assert lib.dit_quantize_act(3, A, 4, 256, 256, B + 8, C, None) == EALIGN       # MXFP8 codes need 16 B
     assert lib.dit_quantize_act(1, A, 4, 300, 304, B, C, None) == EUNSUP
     assert lib.dit_quantize_act(1, A, 4, 256, 250, B, C, None) == EALIGN
     assert lib.dit_quantize_act(1, A + 2, 4, 256, 256, B, C, None) == EALIGN
     assert lib.dit_quantize_act(2, A, 4, 256, 256, B, C + 2, None) == EALIGN
     assert lib.dit_pack_weights(1, 0, A, 64, 256, 256, None, None) == EINVAL
     assert lib.dit_pack_weights(1, 1, A, 64, 256, 256, B, None) == EUNSUP
-    assert lib.dit_pack_weights(2, 2, A, 384, 256, 256, B, None) == EUNSUP
+    assert lib.dit_pack_weights(3, 1, A, 64, 256, 256, B, None) == EUNSUP
     assert lib.dit_pack_weights(1, 0, A, 64, 256, 264, B + 1, None) == EALIGN
     assert lib.dit_gemm_q8_epilogue(A, B, C, 4, 512, 256, 2, D, 512, None) == EUNSUP
     assert lib.dit_gemm_q8_epilogue(A, B + 2, C, 4, 512, 256, 0, D, 512, None) == EALIGN
     assert lib.dit_gemm_q8_epilogue(A, None, C, 4, 512, 256, 0, D, 512, None) == EINVAL
     if not _has_gpu():
         assert lib.dit_quantize_act(1, A, 4, 256, 256, B, C, None) == EDEVICE
+        assert lib.dit_quantize_act(3, A, 4, 256, 256, B, C + 1, None) == EDEVICE    # MXFP8 scales: any alignment
         assert lib.dit_pack_weights(2, 1, A, 128, 256, 256, B, None) == EDEVICE
+        assert lib.dit_pack_weights(2, 2, A, 384, 256, 256, B, None) == EDEVICE      # FP8 for QK-RMSNorm
+        assert lib.dit_pack_weights(3, 1, A, 128, 256, 256, B, None) == EDEVICE
         assert lib.dit_gemm_q8_epilogue(A, B, C, 4, 512, 256, 1, D, 256, None) == EDEVICE
 
 
 def _has_gpu():
     import torch
     return torch.cuda.device_count() > 0
+
+
+def _any(fmt=3, a=A, s=B, w=C, M=64, N=512, K=256, epi=1, rms=None, out=D, ldo=256):
+    return ditq._lib.dit_gemm_epilogue(fmt, a, s, w, M, N, K, epi, ctypes.byref(rms) if rms else None, out, ldo,
+                                       None)
+
+
+def test_gemm_any_format_validation():
+    assert _any(fmt=0) == EINVAL
+    assert _any(fmt=4) == EINVAL
+    assert _any(out=None) == EINVAL
+    assert _any(a=None) == EINVAL
+    assert _any(epi=2) == EINVAL                                     # RMSNorm without params
+    assert _any(fmt=2, epi=2) == EINVAL
+    r = ditq.RmsNormParams(128, 1, A, B, 1e-6)
+    assert _any(epi=0, rms=r, ldo=512) == EINVAL                     # params without RMSNorm
+    assert _any(fmt=2, epi=2, rms=ditq.RmsNormParams(64, 2, A, B, 1e-6), N=384, ldo=384) == EUNSUP
+    assert _any(K=128) == EUNSUP
+    assert _any(fmt=2, N=576) == EUNSUP                              # gated needs N % 128
+    assert _any(s=B + 4) == EALIGN                                   # MXFP8 scales: 16 B
+    assert _any(fmt=2, s=B + 4) != EALIGN                            # FP8 row scales: 4 B is enough
+    assert _any(fmt=2, s=B + 2) == EALIGN
+    assert _any(ldo=255) == EALIGN
+    if not _has_gpu():
+        for fmt in (1, 2, 3):
+            assert _any(fmt=fmt) == EDEVICE
+            assert _any(fmt=fmt, epi=0, ldo=512) == EDEVICE
+            assert _any(fmt=fmt, epi=2, rms=r, N=384, ldo=384) == EDEVICE
+            assert _any(fmt=fmt, epi=2, rms=ditq.RmsNormParams(256, 1, A, B, 1e-6), N=768, ldo=768) == EDEVICE

@@ -14,7 +14,7 @@ from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-FMT = {"fp4": 1, "fp8": 2}
+FMT = {"fp4": 1, "fp8": 2, "mx8": 3}
 EPI = {"identity": 0, "gated_silu": 1, "qk_rmsnorm": 2}
 
 
@@ -27,8 +27,11 @@ def ditq():
     return bit_gemm_dit_amd
 
 
-def run_layer(ditq, d, fmt, epi, ldo=None, stream=None, guard=0):
-    """Pack W, quantize x, run the fused GEMM through the C ABI; returns bf16 bits [M, width]."""
+def run_layer(ditq, d, fmt, epi, ldo=None, stream=None, guard=0, generic=False):
+    """Pack W, quantize x, run the fused GEMM through the C ABI; returns bf16 bits [M, width].
+
+    FP4 goes through dit_gemm_q4_epilogue and FP8 without RMSNorm through
+    dit_gemm_q8_epilogue, unless `generic`; everything else through dit_gemm_epilogue."""
     import torch
     from tests.gpu_util import to_dev_bf16, to_host_bits
     M, K = d["x"].shape
@@ -55,10 +58,13 @@ def run_layer(ditq, d, fmt, epi, ldo=None, stream=None, guard=0):
         gk = torch.from_numpy(d["gamma_k"]).cuda()
         keep = [gq, gk]
         rms = ditq.RmsNormParams(d["head_dim"], d["n_heads"], gq.data_ptr(), gk.data_ptr(), d["eps"])
-    if f == 1:
+    if f == 1 and not generic:
         ditq.dit_gemm_q4_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, e, rms, optr, ldo, st)
-    else:
+    elif f == 2 and e != 2 and not generic:
         ditq.dit_gemm_q8_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, e, optr, ldo, st)
+    else:
+        ditq.dit_gemm_epilogue(f, codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, e, rms, optr, ldo,
+                               st)
     torch.cuda.synchronize()
     del keep
     o = out.cpu().numpy().view(np.uint16)
@@ -89,6 +95,15 @@ SMALL = [
     ("fp8_cfg_pair", "fp8", "identity", 300, 768, 512, None),
     ("fp8_cfg_pair", "fp8", "gated_silu", 129, 1024, 768, None),
     ("fp8_cfg_pair", "fp8", "identity", 1, 320, 256, None),
+    ("qkv_rmsnorm_hd128", "fp8", "qk_rmsnorm", 300, None, 512, 2),
+    ("qkv_rmsnorm_hd128", "fp8", "qk_rmsnorm", 1, None, 256, 1),
+    ("qkv_rmsnorm_hd256", "fp8", "qk_rmsnorm", 70, None, 768, 3),
+    ("mlp_gated_silu", "mx8", "identity", 300, 768, 512, None),
+    ("mlp_gated_silu", "mx8", "gated_silu", 129, 1024, 768, None),
+    ("mlp_gated_silu", "mx8", "gated_silu", 200, 1024, 1024, None),
+    ("mlp_gated_silu", "mx8", "identity", 1, 320, 256, None),
+    ("qkv_rmsnorm_hd128", "mx8", "qk_rmsnorm", 257, None, 512, 2),
+    ("qkv_rmsnorm_hd256", "mx8", "qk_rmsnorm", 65, None, 512, 1),
 ]
 
 
@@ -121,19 +136,36 @@ def test_ldo_stream_and_determinism(ditq):
     compare_bf16(g1, oracle_rows(d, "fp4", "gated_silu"), "ldo")
 
 
-FULL = [("qkv_rmsnorm_hd128", "qk_rmsnorm"), ("mlp_gated_silu", "gated_silu"),
-        ("qkv_rmsnorm_hd256", "qk_rmsnorm"), ("fp8_cfg_pair", "identity"), ("fp8_cfg_pair", "gated_silu")]
+FULL = [("qkv_rmsnorm_hd128", "qk_rmsnorm", None), ("mlp_gated_silu", "gated_silu", None),
+        ("qkv_rmsnorm_hd256", "qk_rmsnorm", None), ("fp8_cfg_pair", "identity", None),
+        ("fp8_cfg_pair", "gated_silu", None), ("qkv_rmsnorm_hd128", "qk_rmsnorm", "fp8"),
+        ("qkv_rmsnorm_hd256", "qk_rmsnorm", "fp8"), ("mlp_gated_silu", "gated_silu", "mx8"),
+        ("qkv_rmsnorm_hd128", "qk_rmsnorm", "mx8"), ("fp8_cfg_pair", "identity", "mx8")]
 
 
-@pytest.mark.parametrize("name,epi", FULL, ids=[f"{a}-{b}" for a, b in FULL])
-def test_full_size_sampled_rows(ditq, name, epi):
+@pytest.mark.parametrize("name,epi,fmt", FULL, ids=[f"{a}-{b}-{c or WORKLOADS[a].fmt}" for a, b, c in FULL])
+def test_full_size_sampled_rows(ditq, name, epi, fmt):
     from tests.gpu_util import compare_bf16
     wl = WORKLOADS[name]
+    fmt = fmt or wl.fmt
     d = make_inputs(name, seed=0)
-    print(f"case full {name} {epi}", flush=True)
-    g = run_layer(ditq, d, wl.fmt, epi)
+    print(f"case full {name} {epi} {fmt}", flush=True)
+    g = run_layer(ditq, d, fmt, epi)
     rng = np.random.default_rng(1)
     rows = np.unique(np.concatenate([[0, 1, 31, 32, 255, 256, wl.M - 1], rng.choice(wl.M, 40, replace=False)]))
-    y = oracle_rows(d, wl.fmt, epi, rows=rows)
+    y = oracle_rows(d, fmt, epi, rows=rows)
     rep = compare_bf16(g[rows], y, f"{name}/{epi}")
     print(f"{name}/{epi}: literal max err / row-RMS = {rep['literal_max_err_over_rowrms']:.4g}")
+
+
+@pytest.mark.parametrize("kind,fmt,epi,M,N,K,H", [("mlp_gated_silu", "fp4", "gated_silu", 200, 1024, 512, None),
+                                                  ("qkv_rmsnorm_hd128", "fp4", "qk_rmsnorm", 70, None, 256, 2),
+                                                  ("fp8_cfg_pair", "fp8", "identity", 130, 512, 512, None),
+                                                  ("fp8_cfg_pair", "fp8", "gated_silu", 64, 512, 256, None)])
+def test_generic_entry_matches_format_entries(ditq, kind, fmt, epi, M, N, K, H):
+    """dit_gemm_epilogue with the FP4 / FP8 formats writes exactly what the
+    format-specific entry points write."""
+    d = make_inputs(kind, seed=3, M=M, N=N, K=K, n_heads=H)
+    a = run_layer(ditq, d, fmt, epi, guard=16)
+    b = run_layer(ditq, d, fmt, epi, guard=16, generic=True)
+    np.testing.assert_array_equal(a, b)

@@ -71,3 +71,27 @@ def test_fp8_pack_bitexact(ditq, N, K, epi):
     np.testing.assert_array_equal(s.view(np.uint32), rs.view(np.uint32))
     np.testing.assert_array_equal(c, rc)
     assert not pad["codes"].any()
+
+
+@pytest.mark.parametrize("N,K,epi", [(320, 256, 0), (256, 512, 1), (384, 768, 2), (16384, 3072, 1)])
+def test_mx8_pack_bitexact(ditq, N, K, epi):
+    d = make_inputs("mlp_gated_silu", seed=N + 1, M=1, N=N, K=K)
+    d["w"][3, :] = 0                                                   # an all-zero row
+    d["w"][5, 64:96] = 0x0001                                          # a block of subnormals: byte 0
+    blob = _pack(ditq, d["w"], 3, epi)
+    hdr = packed.read_header(blob)
+    assert (hdr["magic"], hdr["fmt"], hdr["epi"], hdr["N"], hdr["K"]) == (packed.MAGIC, 3, epi, N, K)
+    assert hdr["total"] == blob.size
+    c, s, pad = packed.decode(blob, 3, epi, N, K)
+    rc, rs = quant.quantize_mx8(d["w"])
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
+    assert not pad["codes"].any() and not pad["scales"].any()
+
+
+def test_fp8_pack_for_rmsnorm_is_the_identity_blob(ditq):
+    d = make_inputs("fp8_cfg_pair", seed=9, M=1, N=384, K=256)
+    a = _pack(ditq, d["w"], 2, 0)
+    b = _pack(ditq, d["w"], 2, 2)
+    assert packed.read_header(b)["epi"] == 2
+    np.testing.assert_array_equal(a[256:], b[256:])

@@ -130,3 +130,64 @@ def test_fp8_quantizer_full_size_workload(ditq):
     rc, rs = quant.quantize_fp8(d["x"])
     np.testing.assert_array_equal(s.view(np.uint32), rs.view(np.uint32))
     np.testing.assert_array_equal(c, rc)
+
+
+def _run_mx8(ditq, bits, ldx=None):
+    import torch
+    from tests.gpu_util import act_codes_to_rowmajor, act_scales_to_rowmajor, to_dev_bf16
+    M, K = bits.shape
+    ldx = ldx or K
+    buf = np.zeros((M, ldx), dtype=np.uint16)
+    buf[:, :K] = bits
+    x = to_dev_bf16(buf)
+    codes = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+    ditq.dit_quantize_act(ditq.FMT_MX8, x.data_ptr(), M, K, ldx, codes.data_ptr(), scales.data_ptr(),
+                          torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return (act_codes_to_rowmajor(codes.cpu().numpy(), M, K, 2),
+            act_scales_to_rowmajor(scales.cpu().numpy(), M, K))
+
+
+@pytest.mark.parametrize("M,K,ldx", [(1, 256, 256), (63, 3072, 3072), (300, 512, 520), (7, 4096, 4104)])
+def test_mx8_quantizer_bitexact(ditq, M, K, ldx):
+    rng = np.random.default_rng(M * 11 + K)
+    bits = _special_rows(rng, M, K)
+    c, s = _run_mx8(ditq, bits, ldx)
+    rc, rs = quant.quantize_mx8(bits)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
+
+
+def test_mx8_quantizer_every_bf16_value(ditq):
+    """Every finite bf16 value, each under several block maxima: byte 0 (maxima
+    with exponent field <= 8, where products reach fp32's subnormal range), the
+    first non-zero bytes, ordinary and the largest maxima."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = allb[np.isfinite(formats.bf16_to_f64(allb))]
+    rng = np.random.default_rng(1)
+    rows = []
+    for top in (0x0000, 0x0400, 0x0480, 0x04FF, 0x3F80, 0x43E0, 0x4278, 0x7F7F):
+        v = rng.permutation(fin)
+        v = np.concatenate([v, v[: (-len(v)) % 31]])
+        blk = v.reshape(-1, 31)
+        mag = blk & 0x7FFF
+        keep = mag.max(axis=1) <= (top & 0x7FFF) if top else np.ones(len(blk), bool)
+        b = np.concatenate([np.full((len(blk), 1), top, np.uint16), blk], axis=1)
+        b = np.where(keep[:, None], b, np.concatenate([np.full((len(blk), 1), 0x7F7F, np.uint16), blk], axis=1))
+        rows.append(b.reshape(-1))
+    flat = np.concatenate(rows)
+    flat = np.concatenate([flat, np.zeros((-len(flat)) % 3072, np.uint16)])
+    bits = flat.reshape(-1, 3072)
+    c, s = _run_mx8(ditq, bits)
+    rc, rs = quant.quantize_mx8(bits)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
+
+
+def test_mx8_quantizer_full_size_workload(ditq):
+    d = make_inputs("mlp_gated_silu", seed=0)
+    c, s = _run_mx8(ditq, d["x"])
+    rc, rs = quant.quantize_mx8(d["x"])
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)

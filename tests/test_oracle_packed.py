@@ -41,8 +41,9 @@ def _write_blob(codes, scales, fmt, epi, N, K):
         else:
             for k in range(K):
                 c, within = k // 64, k % 64
-                L = lane_lo + 32 * (within // 32)
-                blob[256 + (g * (K // 64) + c) * 2048 + 32 * L + within % 32] = codes[n, k]
+                L = lane_lo + 32 * ((within % 32) // 16)
+                byte = 16 * (within // 32) + within % 16
+                blob[256 + (g * (K // 64) + c) * 2048 + 32 * L + byte] = codes[n, k]
             if fmt == packed.FMT_MX8:
                 for blk in range(K // 32):
                     s, r = blk // 4, blk % 4
