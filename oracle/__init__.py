@@ -12,7 +12,8 @@ What it computes (plain, slow, obviously correct; float64 for floating point):
   per-row (activation) / per-column (weight) scales, and MXFP8 (E4M3 with an
   E8M0 scale per 32-element K block).
 * ``gemm``     -- decode codes and scales, multiply in float64.
-* ``epilogue`` -- identity, gated-SiLU and per-head QK-RMSNorm in float64.
+* ``epilogue`` -- identity, gated-SiLU, per-head QK-RMSNorm, GELU (tanh form)
+  and the gated residual update, in float64.
 * ``packed``   -- decoder of the packed weight blob, written from the layout
   documented in ``include/ditq.h`` (used to check the packer bit-exactly).
 

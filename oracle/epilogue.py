@@ -9,7 +9,15 @@ Page "How fal made Ideogram V4 6x faster" (news.ditty.ir):
   mathematics is the same as for any head size, so the oracle has no schedule);
 * paragraph 4 -- gated-SiLU: C = A @ B, output = SiLU(C[:, :N//2]) * C[:, N//2:].
 
-Readings where the pages are silent: SiLU(x) = x / (1 + exp(-x)); RMSNorm is the
+Two more small ops of a DiT block in the same place: the GELU of an MLP (page on
+Google's on-device diffusion work (laaro.com), fused GELU kernels; FLUX-style MLPs
+use its tanh form), and the gated residual update of adaLN-style blocks, the
+small op after the attention-output and MLP-down projections.
+
+Readings where the pages are silent: GELU-tanh(x) = 0.5 x (1 + tanh(sqrt(2/pi)
+(x + 0.044715 x^3))); the gated residual is out[m, n] = residual[m, n] +
+gate[m // rows_per_gate, n] * C[m, n], one gate row per sample of rows_per_gate
+tokens, residual in bf16, gate in fp32; SiLU(x) = x / (1 + exp(-x)); RMSNorm is the
 textbook y = x / sqrt(mean_d(x^2) + eps) * gamma[d], with the mean over the head
 dimension, eps inside the square root, one gamma per head-dimension element shared
 by all heads, separate gammas for the Q and K heads, and the GEMM columns ordered
@@ -18,7 +26,11 @@ the un-rounded accumulator: the fused kernel never rounds C before the small op.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
+
+from . import formats
 
 
 def identity(acc: np.ndarray) -> np.ndarray:
@@ -29,6 +41,27 @@ def silu(x: np.ndarray) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     with np.errstate(over="ignore"):
         return x / (1.0 + np.exp(-x))           # -> -0.0 for very negative x, never NaN
+
+
+GELU_TANH_C = 0.044715
+SQRT_2_OVER_PI = math.sqrt(2.0 / math.pi)
+
+
+def gelu_tanh(x: np.ndarray) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        return 0.5 * x * (1.0 + np.tanh(SQRT_2_OVER_PI * (x + GELU_TANH_C * x ** 3)))
+
+
+def gate_residual(acc: np.ndarray, residual_bits, gate, rows_per_gate: int, row_ids=None) -> np.ndarray:
+    """residual + gate * acc for the accumulator rows ``row_ids`` (all rows if None):
+    row m takes residual row m (bf16 bits, [M, N]) and gate row m // rows_per_gate
+    (fp32, [ceil(M / rows_per_gate), N])."""
+    acc = np.asarray(acc, dtype=np.float64)
+    ids = np.arange(acc.shape[0]) if row_ids is None else np.asarray(row_ids)
+    res = formats.bf16_to_f64(np.asarray(residual_bits, dtype=np.uint16)[ids])
+    g = np.asarray(gate, dtype=np.float32).astype(np.float64)[ids // rows_per_gate]
+    return res + g * acc
 
 
 def gated_silu(acc: np.ndarray) -> np.ndarray:
@@ -61,4 +94,8 @@ def apply(epi: str, acc: np.ndarray, **kw) -> np.ndarray:
         return gated_silu(acc)
     if epi == "qk_rmsnorm":
         return qk_rmsnorm(acc, kw["n_heads"], kw["head_dim"], kw["gamma_q"], kw["gamma_k"], kw["eps"])
+    if epi == "gelu_tanh":
+        return gelu_tanh(acc)
+    if epi == "gate_residual":
+        return gate_residual(acc, kw["residual"], kw["gate"], kw["rows_per_gate"], kw.get("row_ids"))
     raise ValueError(epi)

@@ -34,4 +34,6 @@ def accumulate(a, w, fmt: str, rows=None) -> np.ndarray:
 def forward(x_bits, w_bits, fmt: str, epi: str, rows=None, **epi_kw) -> np.ndarray:
     """float64 output of the layer (before the bf16 store) for all rows or the given rows."""
     a, w = quantize_operands(x_bits, w_bits, fmt)
+    if epi == "gate_residual":
+        epi_kw = dict(epi_kw, row_ids=rows)
     return epilogue.apply(epi, accumulate(a, w, fmt, rows=rows), **epi_kw)

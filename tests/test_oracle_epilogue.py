@@ -76,3 +76,40 @@ def test_rmsnorm_head_is_local_and_per_head():
     acc[0, D:2 * D] = 100.0                    # second Q head much larger: must not affect the first
     y = epilogue.qk_rmsnorm(acc, H, D, np.ones(D), np.ones(D), 0.0)
     np.testing.assert_allclose(y[0, :2 * D], 1.0, rtol=1e-15)
+
+
+def test_gelu_tanh_closed_forms_and_library():
+    import torch
+    x = np.concatenate([np.linspace(-12, 12, 2401), [-1e4, -50.0, 50.0, 1e4, 1e30, -1e30]])
+    g = epilogue.gelu_tanh(x)
+    assert epilogue.gelu_tanh(np.array([0.0]))[0] == 0.0
+    # x * Phi-like form: g(x) - g(-x) = x for the tanh form too (tanh is odd)
+    np.testing.assert_allclose(g - epilogue.gelu_tanh(-x), x, rtol=1e-15, atol=1e-12)
+    # torch's tanh-approximated GELU in float64 on the CPU
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    # (1 + tanh u) cancels for very negative x in both, so the tails agree only to ~1e-15 absolute
+    np.testing.assert_allclose(g, ref, rtol=1e-14, atol=1e-15)
+    # within the tanh approximation's known distance of the exact GELU x * Phi(x)
+    from scipy.special import erf
+    exact = 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+    small = np.abs(x) < 20
+    assert np.max(np.abs(g[small] - exact[small])) < 1e-3
+    assert g[-1] == 0.0 and g[-3] == 1e4 and g[-4] == 50.0
+
+
+def test_gate_residual_against_elementwise_loops():
+    rng = np.random.default_rng(3)
+    from workloads import f32_to_bf16_bits
+    M, N, rpg = 7, 5, 3
+    acc = rng.standard_normal((M, N))
+    res = f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    gate = rng.standard_normal(((M + rpg - 1) // rpg, N)).astype(np.float32)
+    y = epilogue.gate_residual(acc, res, gate, rpg)
+    rv = (res.astype(np.uint32) << 16).view(np.float32)
+    for m in range(M):
+        for n in range(N):
+            assert y[m, n] == float(rv[m, n]) + float(gate[m // rpg, n]) * acc[m, n]
+    rows = np.array([6, 0, 4])
+    np.testing.assert_array_equal(epilogue.gate_residual(acc[rows], res, gate, rpg, row_ids=rows), y[rows])
+    np.testing.assert_array_equal(epilogue.gate_residual(acc, res, np.zeros_like(gate), rpg), rv.astype(np.float64))
+    np.testing.assert_array_equal(epilogue.gate_residual(acc, np.zeros_like(res), np.ones_like(gate), rpg), acc)

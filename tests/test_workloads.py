@@ -32,3 +32,12 @@ def test_workload_table():
     assert WORKLOADS["mlp_gated_silu"].flops == 2 * 4608 * 16384 * 3072
     assert WORKLOADS["qkv_rmsnorm_hd256"].N == 3 * 16 * 256
     assert WORKLOADS["qkv_rmsnorm_hd128"].N == 3 * 24 * 128
+
+
+def test_gate_residual_inputs():
+    d = make_inputs("mlp_down_gate_residual", seed=1, M=50, N=128, K=256, rows_per_gate=20)
+    assert d["residual"].shape == (50, 128) and d["gate"].shape == (3, 128) and d["rows_per_gate"] == 20
+    assert d["gate"].dtype == np.float32 and 0.3 < float(np.std(d["gate"])) < 0.7
+    e = make_inputs("mlp_gated_silu", seed=1, M=8, N=128, K=256)
+    assert e["residual"] is None and e["gate"] is None
+    assert WORKLOADS["mlp_down_gate_residual"].flops == 2 * 9216 * 3072 * 12288

@@ -14,10 +14,16 @@ Workloads (shapes are GEMM M x N x K, N = full GEMM width):
 * ``qkv_rmsnorm_hd256`` 4096 x 12288 x 4096, FP4, per-head QK-RMSNorm, 16 heads of 256.
 * ``fp8_cfg_pair``      9216 x 12288 x 3072, FP8 E4M3, identity and gated-SiLU;
   9216 = 2 x 4608 tokens (the conditional and unconditional halves of a CFG pair).
+* ``mlp_gelu_tanh``     4608 x 12288 x 3072, FP4, GELU (tanh form): a FLUX-style
+  MLP up-projection (hidden 3072, ratio 4).
+* ``mlp_down_gate_residual`` 9216 x 3072 x 12288, FP4, gated residual update: the
+  MLP down-projection of a CFG pair, out = residual + gate[sample] * C, one gate
+  row per sample of 4608 tokens.
 
 Value distributions: activations ~ N(0, 1) with 1 % of the K channels (the same
 channels for every row) scaled by 20; weights ~ N(0, 1/sqrt(K)) (standard
-deviation 1/sqrt(K)); RMSNorm gammas ~ U(0.5, 1.5); eps = 1e-6.
+deviation 1/sqrt(K)); RMSNorm gammas ~ U(0.5, 1.5); eps = 1e-6; residual ~ N(0, 1)
+(bf16, [M, N]); gates ~ N(0, 0.5^2) (fp32, one row of N per sample).
 
 The diffusion-transformer shapes follow the DiT layers the pages accelerate
 (FLUX-dev: hidden 3072, 24 heads of 128; page "WaveSpeedAI X DataCrunch: FLUX
@@ -37,6 +43,8 @@ FP8 = "fp8"
 IDENTITY = "identity"
 GATED_SILU = "gated_silu"
 QK_RMSNORM = "qk_rmsnorm"
+GELU_TANH = "gelu_tanh"
+GATE_RESIDUAL = "gate_residual"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -51,6 +59,7 @@ class Workload:
     n_heads: int = 0
     head_dim: int = 0
     eps: float = 1e-6
+    rows_per_gate: int = 0       # tokens per sample of the gated residual (0: no gate)
 
     @property
     def flops(self) -> int:
@@ -66,8 +75,12 @@ WORKLOADS = {
     "qkv_rmsnorm_hd256": Workload("qkv_rmsnorm_hd256", FP4, (QK_RMSNORM,), 4096, 12288, 4096, True,
                                   n_heads=16, head_dim=256),
     "fp8_cfg_pair": Workload("fp8_cfg_pair", FP8, (IDENTITY, GATED_SILU), 9216, 12288, 3072, True),
+    "mlp_gelu_tanh": Workload("mlp_gelu_tanh", FP4, (GELU_TANH,), 4608, 12288, 3072, True),
+    "mlp_down_gate_residual": Workload("mlp_down_gate_residual", FP4, (GATE_RESIDUAL,), 9216, 3072, 12288, True,
+                                       rows_per_gate=4608),
 }
-ORDER = ["tiny_gated_silu", "qkv_rmsnorm_hd128", "mlp_gated_silu", "qkv_rmsnorm_hd256", "fp8_cfg_pair"]
+ORDER = ["tiny_gated_silu", "qkv_rmsnorm_hd128", "mlp_gated_silu", "qkv_rmsnorm_hd256", "fp8_cfg_pair",
+         "mlp_gelu_tanh", "mlp_down_gate_residual"]
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -89,16 +102,20 @@ def outlier_channels(rng: np.random.Generator, K: int) -> np.ndarray:
 
 
 def make_inputs(wl: Workload | str, seed: int = 0, M: int | None = None, N: int | None = None,
-                K: int | None = None, n_heads: int | None = None) -> dict:
+                K: int | None = None, n_heads: int | None = None, rows_per_gate: int | None = None) -> dict:
     """Draw the inputs of one workload.
 
     Draw order (one PCG64 generator per call): outlier channel indices, the
     activation matrix [M, K], the weight matrix [N, K] (rows in gate-then-up
-    order for gated-SiLU), then gamma_q and gamma_k.  M, N, K and n_heads may be
-    overridden to get smaller problems of the same kind for parity tests.
+    order for gated-SiLU), then gamma_q and gamma_k, then (gated residual) the
+    residual [M, N] and the gates [ceil(M / rows_per_gate), N].  M, N, K,
+    n_heads and rows_per_gate may be overridden to get smaller problems of the
+    same kind for parity tests.
 
     Returns a dict with ``x`` (uint16 bf16 bits [M, K]), ``w`` (uint16 bf16 bits
-    [N, K]), ``gamma_q`` / ``gamma_k`` (float32 [head_dim] or None), ``eps``.
+    [N, K]), ``gamma_q`` / ``gamma_k`` (float32 [head_dim] or None), ``eps``,
+    ``residual`` (uint16 bf16 bits [M, N] or None), ``gate`` (float32 or None),
+    ``rows_per_gate``.
     """
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
@@ -117,6 +134,11 @@ def make_inputs(wl: Workload | str, seed: int = 0, M: int | None = None, N: int 
     if wl.head_dim:
         gq = rng.uniform(0.5, 1.5, wl.head_dim).astype(np.float32)
         gk = rng.uniform(0.5, 1.5, wl.head_dim).astype(np.float32)
+    rpg = wl.rows_per_gate if rows_per_gate is None else rows_per_gate
+    res = gate = None
+    if rpg:
+        res = f32_to_bf16_bits(rng.standard_normal((M, N), dtype=np.float32))
+        gate = (rng.standard_normal(((M + rpg - 1) // rpg, N), dtype=np.float32) * np.float32(0.5))
     return {
         "x": f32_to_bf16_bits(x),
         "w": f32_to_bf16_bits(w),
@@ -124,5 +146,8 @@ def make_inputs(wl: Workload | str, seed: int = 0, M: int | None = None, N: int 
         "gamma_k": gk,
         "eps": wl.eps,
         "outlier_channels": chans,
+        "residual": res,
+        "gate": gate,
+        "rows_per_gate": rpg,
         "M": M, "N": N, "K": K, "n_heads": H, "head_dim": wl.head_dim,
     }
