@@ -203,8 +203,9 @@ def time_other_configs(ditq, torch, args):
              ("fp8_cfg_pair", "identity", None), ("fp8_cfg_pair", "gated_silu", None),
              ("qkv_rmsnorm_hd128", "qk_rmsnorm", "fp8"), ("qkv_rmsnorm_hd256", "qk_rmsnorm", "fp8"),
              ("mlp_gated_silu", "gated_silu", "mx8"), ("qkv_rmsnorm_hd128", "qk_rmsnorm", "mx8"),
-             ("fp8_cfg_pair", "identity", "mx8")]
-    epis = {"identity": 0, "gated_silu": 1, "qk_rmsnorm": 2}
+             ("fp8_cfg_pair", "identity", "mx8"), ("mlp_gelu_tanh", "gelu_tanh", None),
+             ("mlp_down_gate_residual", "gate_residual", None)]
+    epis = {"identity": 0, "gated_silu": 1, "qk_rmsnorm": 2, "gelu_tanh": 3, "gate_residual": 4}
     fmts = {"fp4": ditq.FMT_FP4, "fp8": ditq.FMT_FP8, "mx8": ditq.FMT_MX8}
     for name, epi_name, fmt_name in plans:
         wl = WORKLOADS[name]
@@ -224,7 +225,18 @@ def time_other_configs(ditq, torch, args):
             keep = [gq, gk]
             rms = ditq.rmsnorm_params(gq, gk, wl.n_heads, wl.eps)
         codes, scales = ditq.quantize_act(x, fmt)
-        o = ditq.gemm(codes, scales, blob, wl.N, wl.K, fmt, epi, rms=rms)
+        if epi == 4:
+            res = torch.from_numpy(d["residual"].view("int16")).cuda().view(torch.bfloat16)
+            gate = torch.from_numpy(d["gate"]).cuda()
+            keep = [res, gate]
+
+            def run_gemm(out=None):
+                return ditq.gemm_gate_residual(codes, scales, blob, wl.N, wl.K, fmt, res, gate, wl.rows_per_gate,
+                                               out=out)
+        else:
+            def run_gemm(out=None):
+                return ditq.gemm(codes, scales, blob, wl.N, wl.K, fmt, epi, rms=rms, out=out)
+        o = run_gemm()
         # flush the Infinity Cache between launches by touching a 512 MB buffer
         flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
         times_g, times_q = [], []
@@ -235,7 +247,7 @@ def time_other_configs(ditq, torch, args):
             ditq.dit_quantize_act(fmt, x.data_ptr(), wl.M, wl.K, wl.K, codes.data_ptr(), scales.data_ptr(),
                                   torch.cuda.current_stream().cuda_stream)
             e[1].record()
-            ditq.gemm(codes, scales, blob, wl.N, wl.K, fmt, epi, rms=rms, out=o)
+            run_gemm(out=o)
             e[2].record()
             torch.cuda.synchronize()
             times_q.append(e[0].elapsed_time(e[1]))

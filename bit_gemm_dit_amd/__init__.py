@@ -14,11 +14,11 @@ import ctypes
 import os
 
 __all__ = [
-    "FMT_FP4", "FMT_FP8", "FMT_MX8", "EPI_IDENTITY", "EPI_GATED_SILU", "EPI_QK_RMSNORM", "DitError",
-    "RmsNormParams",
+    "FMT_FP4", "FMT_FP8", "FMT_MX8", "EPI_IDENTITY", "EPI_GATED_SILU", "EPI_QK_RMSNORM", "EPI_GELU_TANH",
+    "EPI_GATE_RESIDUAL", "DitError", "RmsNormParams", "GateResidualParams",
     "dit_packed_weight_bytes", "dit_act_code_bytes", "dit_act_scale_bytes", "dit_pack_weights",
     "dit_quantize_act", "dit_gemm_q4_epilogue", "dit_gemm_q4_epilogue_q4", "dit_gemm_q8_epilogue",
-    "dit_gemm_epilogue",
+    "dit_gemm_epilogue", "dit_gemm_gate_residual", "gemm_gate_residual",
     "dit_status_str", "dit_last_error", "pack_weights", "quantize_act", "gemm", "gemm_q4out", "linear",
     "library_path", "EXPORTED",
 ]
@@ -29,6 +29,8 @@ FMT_MX8 = 3
 EPI_IDENTITY = 0
 EPI_GATED_SILU = 1
 EPI_QK_RMSNORM = 2
+EPI_GELU_TANH = 3
+EPI_GATE_RESIDUAL = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libditq.so")
@@ -53,6 +55,12 @@ class RmsNormParams(ctypes.Structure):
                 ("gamma_k", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
+class GateResidualParams(ctypes.Structure):
+    """dit_gate_residual_params: residual (device bf16), ldr, gate (device fp32), rows_per_gate."""
+    _fields_ = [("residual", ctypes.c_void_p), ("ldr", ctypes.c_int), ("gate", ctypes.c_void_p),
+                ("rows_per_gate", ctypes.c_int)]
+
+
 _i, _p, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
 _SIGS = {
     "dit_packed_weight_bytes": (_sz, [_i, _i, _i, _i]),
@@ -65,6 +73,7 @@ _SIGS = {
                                      _p]),
     "dit_gemm_q8_epilogue": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _i, _p]),
     "dit_gemm_epilogue": (_i, [_i, _p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams), _p, _i, _p]),
+    "dit_gemm_gate_residual": (_i, [_i, _p, _p, _p, _i, _i, _i, ctypes.POINTER(GateResidualParams), _p, _i, _p]),
     "dit_status_str": (ctypes.c_char_p, [_i]),
     "dit_last_error": (ctypes.c_char_p, []),
 }
@@ -138,6 +147,12 @@ def dit_gemm_epilogue(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, out, 
     rp = ctypes.byref(rms) if rms is not None else None
     _check(_lib.dit_gemm_epilogue(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rp, out, ldo, stream),
            "dit_gemm_epilogue")
+
+
+def dit_gemm_gate_residual(fmt, a_codes, a_scales, w_packed, M, N, K, gr, out, ldo, stream=None) -> None:
+    gp = ctypes.byref(gr) if gr is not None else None
+    _check(_lib.dit_gemm_gate_residual(fmt, a_codes, a_scales, w_packed, M, N, K, gp, out, ldo, stream),
+           "dit_gemm_gate_residual")
 
 
 # ---------------------------------------------------------------- torch helpers
@@ -222,6 +237,20 @@ def gemm_q4out(codes, scales, blob, N: int, K: int, epi: int, rms: RmsNormParams
                             out.data_ptr() if out is not None else None, _ld(out) if out is not None else 0,
                             q_codes.data_ptr(), q_scales.data_ptr(), _stream())
     return (q_codes, q_scales, out) if with_bf16 else (q_codes, q_scales)
+
+
+def gemm_gate_residual(codes, scales, blob, N: int, K: int, fmt: int, residual, gate, rows_per_gate: int,
+                       out=None):
+    """out = residual + gate[row // rows_per_gate] * (A W^T), bf16 [M, N]; `out` may be
+    `residual` itself (an in-place update of the residual stream)."""
+    import torch
+    M = codes.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=codes.device)
+    gr = GateResidualParams(residual.data_ptr(), _ld(residual), gate.data_ptr(), rows_per_gate)
+    dit_gemm_gate_residual(fmt, codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, gr,
+                           out.data_ptr(), _ld(out), _stream())
+    return out
 
 
 def linear(x, blob, N: int, fmt: int, epi: int, rms: RmsNormParams | None = None, out=None):

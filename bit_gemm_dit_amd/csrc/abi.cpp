@@ -25,7 +25,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 bool valid_fmt(int f) {
   return f == DIT_FMT_FP4_E2M1_MX32 || f == DIT_FMT_FP8_E4M3_ROWCOL || f == DIT_FMT_FP8_E4M3_MX32;
 }
-bool valid_epi(int e) { return e == DIT_EPI_IDENTITY || e == DIT_EPI_GATED_SILU || e == DIT_EPI_QK_RMSNORM; }
+bool valid_epi(int e) {
+  return e == DIT_EPI_IDENTITY || e == DIT_EPI_GATED_SILU || e == DIT_EPI_QK_RMSNORM || e == DIT_EPI_GELU_TANH ||
+         e == DIT_EPI_GATE_RESIDUAL;
+}
 
 // Shapes the kernels implement.  K: whole 256-element k-steps (FP4 scale groups);
 // N: whole 64-row weight groups (128 for gated-SiLU so each 64-row packed group
@@ -130,14 +133,24 @@ namespace {
 // Checks and launch shared by every GEMM entry point.  out_codes set: the FP4
 // quantization of the output is written too (FP4 only), and out_bf16 may be null.
 dit_status gemm_any(int fmt, const void* a_codes, const void* a_scales, const void* w_packed, int M, int N, int K,
-                    dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo, void* out_codes,
-                    void* out_scales, void* stream) {
+                    dit_epi epi, const dit_rmsnorm_params* rms, const dit_gate_residual_params* gr,
+                    void* out_bf16, int ldo, void* out_codes, void* out_scales, void* stream) {
   const bool quantized = out_codes != nullptr;
   if (!valid_fmt(fmt) || !a_codes || !a_scales || !w_packed || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi))
     return DIT_EINVAL;
   if (!quantized && !out_bf16) return DIT_EINVAL;
   if (quantized && !out_scales) return DIT_EINVAL;
   if ((epi == DIT_EPI_QK_RMSNORM) != (rms != nullptr)) return DIT_EINVAL;
+  if ((epi == DIT_EPI_GATE_RESIDUAL) != (gr != nullptr)) return DIT_EINVAL;
+  if (gr) {
+    if (!gr->residual || !gr->gate || gr->rows_per_gate <= 0 || !out_bf16) return DIT_EINVAL;
+    // the residual may be the output itself (an in-place update), but no other overlap
+    const uintptr_t r0 = reinterpret_cast<uintptr_t>(gr->residual), o0 = reinterpret_cast<uintptr_t>(out_bf16);
+    const uintptr_t r1 = r0 + 2 * ((size_t)(M - 1) * (size_t)gr->ldr + N);
+    const uintptr_t o1 = o0 + 2 * ((size_t)(M - 1) * (size_t)ldo + N);
+    const bool same = r0 == o0 && gr->ldr == ldo;
+    if (!same && r0 < o1 && o0 < r1) return DIT_EINVAL;
+  }
   if (rms) {
     if (!rms->gamma_q || !rms->gamma_k || rms->n_heads <= 0 || !(rms->eps > 0.0f)) return DIT_EINVAL;
     if ((long long)N != 3LL * rms->n_heads * rms->head_dim) return DIT_EINVAL;
@@ -152,14 +165,19 @@ dit_status gemm_any(int fmt, const void* a_codes, const void* a_scales, const vo
   if (out_bf16 && (!aligned16(out_bf16) || ldo < width || ldo % 8 != 0)) return DIT_EALIGN;
   if (quantized && (!aligned16(out_codes) || !aligned16(out_scales))) return DIT_EALIGN;
   if (rms && (!aligned16(rms->gamma_q) || !aligned16(rms->gamma_k))) return DIT_EALIGN;
+  if (gr && (!aligned16(gr->residual) || !aligned16(gr->gate) || gr->ldr < N || gr->ldr % 8 != 0))
+    return DIT_EALIGN;
   if (dit_status s = check_device()) return s;
   (void)hipGetLastError();
   ditq::RmsArgs r{};
   if (rms) r = ditq::RmsArgs{rms->head_dim, rms->n_heads, rms->gamma_q, rms->gamma_k, rms->eps};
+  ditq::ResidualArgs g{};
+  if (gr) g = ditq::ResidualArgs{static_cast<const uint16_t*>(gr->residual), gr->ldr, gr->gate, gr->rows_per_gate};
   return launched(ditq::launch_gemm(fmt, static_cast<const uint8_t*>(a_codes), a_scales,
                                     static_cast<const uint8_t*>(w_packed), M, N, K, epi, rms ? &r : nullptr,
-                                    static_cast<uint16_t*>(out_bf16), ldo, static_cast<uint8_t*>(out_codes),
-                                    static_cast<uint8_t*>(out_scales), static_cast<hipStream_t>(stream)));
+                                    gr ? &g : nullptr, static_cast<uint16_t*>(out_bf16), ldo,
+                                    static_cast<uint8_t*>(out_codes), static_cast<uint8_t*>(out_scales),
+                                    static_cast<hipStream_t>(stream)));
 }
 }  // namespace
 
@@ -167,32 +185,42 @@ dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const
                                 int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
                                 void* stream) {
   if (!out_bf16) return DIT_EINVAL;
-  return gemm_any(FMT_FP4, a_codes, a_scales, w_packed, M, N, K, epi, rms, out_bf16, ldo, nullptr, nullptr,
-                  stream);
+  return gemm_any(FMT_FP4, a_codes, a_scales, w_packed, M, N, K, epi, rms, nullptr, out_bf16, ldo, nullptr,
+                  nullptr, stream);
 }
 
 dit_status dit_gemm_q4_epilogue_q4(const void* a_codes, const void* a_scales, const void* w_packed, int M, int N,
                                    int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
                                    void* out_codes, void* out_scales, void* stream) {
   if (!out_codes || !out_scales) return DIT_EINVAL;
-  return gemm_any(FMT_FP4, a_codes, a_scales, w_packed, M, N, K, epi, rms, out_bf16, ldo, out_codes, out_scales,
-                  stream);
+  return gemm_any(FMT_FP4, a_codes, a_scales, w_packed, M, N, K, epi, rms, nullptr, out_bf16, ldo, out_codes,
+                  out_scales, stream);
 }
 
 dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, const void* w_packed, int M, int N,
                                 int K, dit_epi epi, void* out_bf16, int ldo, void* stream) {
   if (!a_codes || !a_scales || !w_packed || !out_bf16 || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi))
     return DIT_EINVAL;
-  if (epi == DIT_EPI_QK_RMSNORM) return DIT_EUNSUPPORTED;     // no RMSNorm parameters here
-  return gemm_any(FMT_FP8, a_codes, a_scales, w_packed, M, N, K, epi, nullptr, out_bf16, ldo, nullptr, nullptr,
-                  stream);
+  // no parameters for RMSNorm or the gated residual here
+  if (epi == DIT_EPI_QK_RMSNORM || epi == DIT_EPI_GATE_RESIDUAL) return DIT_EUNSUPPORTED;
+  return gemm_any(FMT_FP8, a_codes, a_scales, w_packed, M, N, K, epi, nullptr, nullptr, out_bf16, ldo, nullptr,
+                  nullptr, stream);
 }
 
 dit_status dit_gemm_epilogue(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed, int M,
                              int N, int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
                              void* stream) {
   if (!out_bf16) return DIT_EINVAL;
-  return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, out_bf16, ldo, nullptr, nullptr, stream);
+  return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, nullptr, out_bf16, ldo, nullptr, nullptr,
+                  stream);
+}
+
+dit_status dit_gemm_gate_residual(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed,
+                                  int M, int N, int K, const dit_gate_residual_params* gr, void* out_bf16, int ldo,
+                                  void* stream) {
+  if (!gr || !out_bf16) return DIT_EINVAL;
+  return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, DIT_EPI_GATE_RESIDUAL, nullptr, gr, out_bf16, ldo,
+                  nullptr, nullptr, stream);
 }
 
 const char* dit_last_error(void) { return g_last_error; }

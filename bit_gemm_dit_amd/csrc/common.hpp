@@ -22,7 +22,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 enum { FMT_FP4 = 1, FMT_FP8 = 2, FMT_MX8 = 3 };
-enum { EPI_IDENTITY = 0, EPI_GATED_SILU = 1, EPI_QK_RMSNORM = 2 };
+enum { EPI_IDENTITY = 0, EPI_GATED_SILU = 1, EPI_QK_RMSNORM = 2, EPI_GELU_TANH = 3, EPI_GATE_RESIDUAL = 4 };
 
 // ---------------------------------------------------------------- blob layout
 constexpr uint32_t kBlobMagic = 0x51544944u;   // "DITQ"
@@ -172,6 +172,12 @@ struct RmsArgs {
   const float* gamma_k;
   float eps;
 };
+struct ResidualArgs {
+  const uint16_t* residual;   // bf16 [M][ldr]; may be the output itself
+  int ldr;
+  const float* gate;          // fp32 [ceil(M / rows_per_gate)][N]
+  int rows_per_gate;
+};
 
 hipError_t launch_quant_fp4(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
                             hipStream_t stream);
@@ -182,11 +188,11 @@ hipError_t launch_quant_mx8(const uint16_t* x, int M, int K, int ldx, uint8_t* c
 hipError_t launch_pack(int fmt, int epi, const uint16_t* w, int N, int K, int ldw, uint8_t* blob,
                        hipStream_t stream);
 // Fused GEMM + epilogue in any format.  a_scales: FP4 / MXFP8 E8M0 bytes, FP8 fp32
-// row scales.  rms: non-null exactly for EPI_QK_RMSNORM.  q_codes / q_scales
-// (FP4 only): optional FP4 quantization of the output (null: none); out may be
-// null when q_codes is set.
+// row scales.  rms: non-null exactly for EPI_QK_RMSNORM; gr: exactly for
+// EPI_GATE_RESIDUAL.  q_codes / q_scales (FP4 only): optional FP4 quantization of
+// the output (null: none); out may be null when q_codes is set.
 hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, const uint8_t* blob, int M, int N,
-                       int K, int epi, const RmsArgs* rms, uint16_t* out, int ldo, uint8_t* q_codes,
-                       uint8_t* q_scales, hipStream_t stream);
+                       int K, int epi, const RmsArgs* rms, const ResidualArgs* gr, uint16_t* out, int ldo,
+                       uint8_t* q_codes, uint8_t* q_scales, hipStream_t stream);
 
 }  // namespace ditq

@@ -5,7 +5,10 @@
 // after the GEMM runs on the fp32 accumulators in registers and the result is
 // written to HBM once as bf16 ("epilogue fusion": page "How fal made Ideogram V4 6x
 // faster", paragraph 3; gated-SiLU with interleaved columns: paragraph 4; FP8 as the
-// second precision: page "WaveSpeedAI X DataCrunch", engine list).
+// second precision: page "WaveSpeedAI X DataCrunch", engine list).  The other small
+// ops of a DiT block fuse the same way: the MLP's GELU (tanh form; fused GELU:
+// page on Google's on-device diffusion work, laaro.com) and the gated residual
+// update out = residual + gate * C of adaLN-style blocks.
 //
 // Mapping to CDNA4:
 // * MFMA operand A = a 32-row weight fragment, operand B = 32 tokens, so the
@@ -137,6 +140,9 @@ struct Params {
   uint8_t* q_scales;
   int M, N, K, ldo;
   int tiles_m, tiles_n, tiles;
+  const uint16_t* residual;   // gated residual: bf16 [M][ldr] (may be `out`), gate fp32 [..][N]
+  const float* gate;
+  int ldr, rows_per_gate;
   uint32_t a_bytes, w_bytes, as_bytes, ws_bytes;
   const float* gamma_q;
   const float* gamma_k;
@@ -232,6 +238,15 @@ __device__ inline float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+
+// GELU, tanh form: 0.5 x (1 + tanh(u)) = x / (1 + e^(-2u)), u = sqrt(2/pi) (x +
+// 0.044715 x^3), with the hardware exp2 and reciprocal.  Saturates to x and -0
+// without NaN (an infinite e^(-2u) gives x * 0).
+__device__ inline float gelu_tanh(float x) {
+  const float t = x * (1.0f + 0.044715f * x * x);                  // u / sqrt(2/pi)
+  const float e = __builtin_amdgcn_exp2f(-2.3022081981443250f * t);  // e^(-2u) = 2^(-2 sqrt(2/pi) log2(e) t)
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // ---------------------------------------------------------------- operands
 // Activation fragments of one unit (TM token tiles): lane L holds token row
@@ -385,7 +400,7 @@ template <class T>
 __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::TM], int n0w, int m0w, int lane,
                                          int wn, int wm, uint8_t* lds) {
   const int h = lane >> 5, l32 = lane & 31;
-  if constexpr (T::EPI == EPI_IDENTITY || T::EPI == EPI_GATED_SILU) {
+  if constexpr (T::EPI != EPI_QK_RMSNORM) {
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) {
       __builtin_amdgcn_sched_barrier(0);     // one token tile at a time keeps register use low
@@ -393,7 +408,7 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
       const bool ok = row < p.M;
       float sa = 1.0f;
       if constexpr (T::FMT == FMT_FP8) sa = reinterpret_cast<const float*>(p.a_scales)[ok ? row : p.M - 1];
-      if constexpr (T::EPI == EPI_IDENTITY) {
+      if constexpr (T::EPI != EPI_GATED_SILU) {
 #pragma unroll
         for (int tn = 0; tn < T::TN; ++tn) {
           __builtin_amdgcn_sched_barrier(0);   // one result tile at a time
@@ -407,6 +422,28 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
                   reinterpret_cast<const float*>(p.w_scales) + n0w + 32 * tn + 8 * g + 4 * h);
 #pragma unroll
               for (int i = 0; i < 4; ++i) v[4 * g + i] *= sa * sw[i];
+            }
+          }
+          if constexpr (T::EPI == EPI_GELU_TANH) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v[r] = gelu_tanh(v[r]);
+          }
+          if constexpr (T::EPI == EPI_GATE_RESIDUAL) {
+            // this lane's 16 columns are 4 runs of 4 (n0 + 8g + 4h + i): the residual
+            // as four 8-byte reads, the gate row of the token's sample as four 16-byte
+            // reads; rows past M read row M - 1 and are not stored
+            const int rr = ok ? row : p.M - 1;
+            const int col = n0w + 32 * tn + 4 * h;
+            const uint16_t* rp = p.residual + (size_t)rr * p.ldr + col;
+            const float* gp = p.gate + (size_t)(rr / p.rows_per_gate) * p.N + col;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const uint2 rv = *reinterpret_cast<const uint2*>(rp + 8 * g);
+              const v4f gv = *reinterpret_cast<const v4f*>(gp + 8 * g);
+              v[4 * g + 0] = __builtin_fmaf(gv[0], v[4 * g + 0], bf16_lo(rv.x));
+              v[4 * g + 1] = __builtin_fmaf(gv[1], v[4 * g + 1], bf16_hi(rv.x));
+              v[4 * g + 2] = __builtin_fmaf(gv[2], v[4 * g + 2], bf16_lo(rv.y));
+              v[4 * g + 3] = __builtin_fmaf(gv[3], v[4 * g + 3], bf16_hi(rv.y));
             }
           }
           store_tile<T>(p, row, ok, n0w + 32 * tn, p.N, h, v);
@@ -901,6 +938,10 @@ hipError_t launch_epi(Params& p, int epi, const RmsArgs* rms, hipStream_t stream
       return launch_cfg<FMT, EPI_IDENTITY>(p, stream);
     case EPI_GATED_SILU:
       return launch_cfg<FMT, EPI_GATED_SILU>(p, stream);
+    case EPI_GELU_TANH:
+      return launch_cfg<FMT, EPI_GELU_TANH>(p, stream);
+    case EPI_GATE_RESIDUAL:
+      return launch_cfg<FMT, EPI_GATE_RESIDUAL>(p, stream);
     default:
       p.gamma_q = rms->gamma_q;
       p.gamma_k = rms->gamma_k;
@@ -914,8 +955,8 @@ hipError_t launch_epi(Params& p, int epi, const RmsArgs* rms, hipStream_t stream
 }  // namespace
 
 hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, const uint8_t* blob, int M, int N,
-                       int K, int epi, const RmsArgs* rms, uint16_t* out, int ldo, uint8_t* q_codes,
-                       uint8_t* q_scales, hipStream_t stream) {
+                       int K, int epi, const RmsArgs* rms, const ResidualArgs* gr, uint16_t* out, int ldo,
+                       uint8_t* q_codes, uint8_t* q_scales, hipStream_t stream) {
   const int Np = padded_rows(N);
   Params p{};
   p.a_codes = a_codes;
@@ -933,6 +974,12 @@ hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, co
   p.w_bytes = (uint32_t)blob_code_bytes(fmt, Np, K);
   p.as_bytes = (uint32_t)((size_t)M * (fmt == FMT_FP8 ? 4 : K / 32));
   p.ws_bytes = (uint32_t)blob_scale_bytes(fmt, Np, K);
+  if (gr) {
+    p.residual = gr->residual;
+    p.ldr = gr->ldr;
+    p.gate = gr->gate;
+    p.rows_per_gate = gr->rows_per_gate;
+  }
   if (fmt == FMT_FP4) return launch_epi<FMT_FP4>(p, epi, rms, stream);
   if (fmt == FMT_MX8) return launch_epi<FMT_MX8>(p, epi, rms, stream);
   return launch_epi<FMT_FP8>(p, epi, rms, stream);

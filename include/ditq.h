@@ -57,7 +57,9 @@ typedef enum {
 typedef enum {
   DIT_EPI_IDENTITY = 0,        /* out = bf16(C) */
   DIT_EPI_GATED_SILU = 1,      /* out[:, j] = bf16(SiLU(C[:, j]) * C[:, j + N/2]), j < N/2 */
-  DIT_EPI_QK_RMSNORM = 2       /* per-head RMSNorm on the Q and K heads of C = [Q | K | V] */
+  DIT_EPI_QK_RMSNORM = 2,      /* per-head RMSNorm on the Q and K heads of C = [Q | K | V] */
+  DIT_EPI_GELU_TANH = 3,       /* out = bf16(0.5 C (1 + tanh(sqrt(2/pi) (C + 0.044715 C^3)))) */
+  DIT_EPI_GATE_RESIDUAL = 4    /* out = bf16(residual + gate[sample] * C): dit_gemm_gate_residual */
 } dit_epi;
 
 /* Parameters of DIT_EPI_QK_RMSNORM (page "How fal made Ideogram V4 6x faster",
@@ -77,6 +79,22 @@ typedef struct {
   const float* gamma_k;  /* device, [head_dim] */
   float eps;             /* > 0, e.g. 1e-6 */
 } dit_rmsnorm_params;
+
+/* Parameters of DIT_EPI_GATE_RESIDUAL, the residual update of adaLN-style DiT
+ * blocks after the attention-output and MLP-down projections (the small op after
+ * a big GEMM, fused so the result goes to HBM once: page "How fal made Ideogram
+ * V4 6x faster", paragraphs 2-3):
+ *     out[m][n] = bf16_RNE(residual[m][n] + gate[m / rows_per_gate][n] * C[m][n])
+ * computed as one fp32 fused multiply-add; rows_per_gate tokens share a gate row
+ * (one sample of a batch).  The residual may be the output itself (same pointer
+ * and leading dimension) for an in-place update of the residual stream; any other
+ * overlap of residual and output is DIT_EINVAL. */
+typedef struct {
+  const void* residual;  /* device, bf16 [M][ldr] */
+  int ldr;               /* >= N, a multiple of 8 */
+  const float* gate;     /* device, fp32 [ceil(M / rows_per_gate)][N] */
+  int rows_per_gate;     /* > 0 */
+} dit_gate_residual_params;
 
 /* ---------------------------------------------------------------- size queries
  * Pure arithmetic, no device access; 0 means "unsupported arguments". */
@@ -98,8 +116,8 @@ size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
  * dit_packed_weight_bytes bytes, 256-byte aligned recommended).  Run once per
  * weight, offline.  `epi` selects the row order: DIT_EPI_GATED_SILU interleaves
  * the gate rows (0 .. N/2-1) with the up rows (N/2 .. N-1); the GEMM must then be
- * called with DIT_EPI_GATED_SILU too.  Blobs packed for IDENTITY and QK_RMSNORM
- * are identical and interchangeable.
+ * called with DIT_EPI_GATED_SILU too.  Blobs packed for every other epilogue are
+ * identical (bar the epi field of the header) and interchangeable.
  *
  * Quantization rule, per weight row: FP4 and MXFP8 -- the same rule as
  * dit_quantize_act along K; FP8 -- s_w[n] = fl32(amax_n / 448) (1 if the row is
@@ -181,7 +199,8 @@ dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int l
  * [M][ldo]; the output width is N/2 for GATED_SILU and N otherwise.
  * `rms` must be non-NULL exactly when epi == DIT_EPI_QK_RMSNORM (host pointer to
  * the struct; the gammas inside are device pointers), with
- * N == 3 * n_heads * head_dim and head_dim in {128, 256}.
+ * N == 3 * n_heads * head_dim and head_dim in {128, 256}.  DIT_EPI_GATE_RESIDUAL
+ * needs its parameters, which dit_gemm_gate_residual takes (here: DIT_EINVAL).
  * Supported: M >= 1 (any), K % 256 == 0, N % 64 == 0 (GATED_SILU: N % 128 == 0),
  * ldo >= output width, ldo % 8 == 0, pointers 16-byte aligned. */
 dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const void* w_packed,
@@ -211,9 +230,10 @@ dit_status dit_gemm_q4_epilogue_q4(const void* a_codes, const void* a_scales, co
 
 /* ---------------------------------------------------------------- fused GEMM + epilogue, FP8
  * out = epi((A W^T) * s_a[m] * s_w[n]) with A the E4M3 codes (K-panel-major) and
- * fp32 row scales [M] from dit_quantize_act, W an FP8 blob.  epi is IDENTITY or
- * GATED_SILU (QK_RMSNORM, which needs its parameters, returns DIT_EUNSUPPORTED
- * here; dit_gemm_epilogue takes them).  Same shape rules as the FP4 entry point
+ * fp32 row scales [M] from dit_quantize_act, W an FP8 blob.  epi is IDENTITY,
+ * GATED_SILU or GELU_TANH (QK_RMSNORM and GATE_RESIDUAL, which need parameters,
+ * return DIT_EUNSUPPORTED here; dit_gemm_epilogue and dit_gemm_gate_residual take
+ * them).  Same shape rules as the FP4 entry point
  * (a_scales 4-byte aligned). */
 dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, const void* w_packed,
                                 int M, int N, int K, dit_epi epi,
@@ -237,6 +257,18 @@ dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, cons
 dit_status dit_gemm_epilogue(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed,
                              int M, int N, int K, dit_epi epi, const dit_rmsnorm_params* rms,
                              void* out_bf16, int ldo, void* stream);
+
+/* ---------------------------------------------------------------- fused GEMM + gated residual
+ * out = bf16(residual + gate[m / rows_per_gate] * C) with C = A W^T in any format
+ * (FP8 row/column: C includes s_a[m] * s_w[n]), the DIT_EPI_GATE_RESIDUAL
+ * epilogue (parameters above).  Width N, weights packed for any epi but
+ * GATED_SILU.  Arguments, shapes and errors as dit_gemm_epilogue; residual and
+ * gate 16-byte aligned, ldr >= N and ldr % 8 == 0 (else DIT_EALIGN); gr NULL or a
+ * NULL member, rows_per_gate <= 0, or a partial overlap of residual and output:
+ * DIT_EINVAL. */
+dit_status dit_gemm_gate_residual(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed,
+                                  int M, int N, int K, const dit_gate_residual_params* gr,
+                                  void* out_bf16, int ldo, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* dit_status_str(dit_status status);

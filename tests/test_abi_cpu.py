@@ -169,3 +169,39 @@ def test_gemm_any_format_validation():
             assert _any(fmt=fmt, epi=0, ldo=512) == EDEVICE
             assert _any(fmt=fmt, epi=2, rms=r, N=384, ldo=384) == EDEVICE
             assert _any(fmt=fmt, epi=2, rms=ditq.RmsNormParams(256, 1, A, B, 1e-6), N=768, ldo=768) == EDEVICE
+
+
+def _gr(fmt=1, a=A, s=B, w=C, M=64, N=512, K=256, gr="default", out=D, ldo=512):
+    if gr == "default":
+        gr = ditq.GateResidualParams(E, 512, F, 32)
+    return ditq._lib.dit_gemm_gate_residual(fmt, a, s, w, M, N, K, ctypes.byref(gr) if gr else None, out, ldo,
+                                            None)
+
+
+def test_gate_residual_validation():
+    P = ditq.GateResidualParams
+    assert _gr(gr=None) == EINVAL
+    assert _gr(out=None) == EINVAL
+    assert _gr(gr=P(None, 512, F, 32)) == EINVAL
+    assert _gr(gr=P(E, 512, None, 32)) == EINVAL
+    assert _gr(gr=P(E, 512, F, 0)) == EINVAL
+    assert _gr(gr=P(D + 1024, 512, F, 32)) == EINVAL                 # partial overlap with the output
+    assert _gr(fmt=4) == EINVAL
+    assert _gr(K=128) == EUNSUP
+    assert _gr(gr=P(E + 8, 512, F, 32)) == EALIGN
+    assert _gr(gr=P(E, 500, F, 32)) == EALIGN                         # ldr < N
+    assert _gr(gr=P(E, 516, F, 32)) == EALIGN                         # ldr % 8
+    assert _gr(gr=P(E, 512, F + 4, 32)) == EALIGN
+    # the other entry points have no gated-residual parameters
+    assert _q4(epi=4, ldo=512) == EINVAL
+    assert ditq._lib.dit_gemm_q8_epilogue(A, B, C, 4, 512, 256, 4, D, 512, None) == EUNSUP
+    assert _any(epi=4, ldo=512) == EINVAL
+    assert ditq.dit_packed_weight_bytes(1, 4, 512, 256) == ditq.dit_packed_weight_bytes(1, 0, 512, 256)
+    assert ditq.dit_packed_weight_bytes(3, 3, 512, 256) == ditq.dit_packed_weight_bytes(3, 0, 512, 256)
+    if not _has_gpu():
+        for fmt in (1, 2, 3):
+            assert _gr(fmt=fmt) == EDEVICE
+            assert _gr(fmt=fmt, gr=P(D, 512, F, 7), out=D) == EDEVICE     # in place
+            assert _any(fmt=fmt, epi=3, ldo=512) == EDEVICE               # GELU-tanh
+        assert _q4(epi=3, ldo=512) == EDEVICE
+        assert ditq._lib.dit_gemm_q8_epilogue(A, B, C, 4, 512, 256, 3, D, 512, None) == EDEVICE

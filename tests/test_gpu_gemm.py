@@ -15,7 +15,7 @@ from workloads import WORKLOADS, make_inputs
 pytestmark = pytest.mark.gpu
 
 FMT = {"fp4": 1, "fp8": 2, "mx8": 3}
-EPI = {"identity": 0, "gated_silu": 1, "qk_rmsnorm": 2}
+EPI = {"identity": 0, "gated_silu": 1, "qk_rmsnorm": 2, "gelu_tanh": 3, "gate_residual": 4}
 
 
 @pytest.fixture(scope="module")
@@ -78,7 +78,47 @@ def oracle_rows(d, fmt, epi, rows=None):
     kw = {}
     if epi == "qk_rmsnorm":
         kw = dict(n_heads=d["n_heads"], head_dim=d["head_dim"], gamma_q=d["gamma_q"], gamma_k=d["gamma_k"], eps=d["eps"])
+    if epi == "gate_residual":
+        kw = dict(residual=d["residual"], gate=d["gate"], rows_per_gate=d["rows_per_gate"])
     return layer.forward(d["x"], d["w"], fmt, epi, rows=rows, **kw)
+
+
+def run_gate_residual(ditq, d, fmt, in_place=False, ldo=None, guard=0):
+    """The gated-residual GEMM through dit_gemm_gate_residual; returns bf16 bits [M, N].
+    in_place: the output is the residual buffer itself."""
+    import torch
+    from tests.gpu_util import to_dev_bf16
+    M, K = d["x"].shape
+    N = d["w"].shape[0]
+    f = FMT[fmt]
+    st = torch.cuda.current_stream().cuda_stream
+    x, w = to_dev_bf16(d["x"]), to_dev_bf16(d["w"])
+    blob = torch.empty(ditq.dit_packed_weight_bytes(f, 4, N, K), dtype=torch.uint8, device="cuda")
+    ditq.dit_pack_weights(f, 4, w.data_ptr(), N, K, K, blob.data_ptr(), st)
+    codes = torch.empty(ditq.dit_act_code_bytes(f, M, K), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(ditq.dit_act_scale_bytes(f, M, K), dtype=torch.uint8, device="cuda")
+    ditq.dit_quantize_act(f, x.data_ptr(), M, K, K, codes.data_ptr(), scales.data_ptr(), st)
+    res = to_dev_bf16(d["residual"])
+    gate = torch.from_numpy(d["gate"]).cuda()
+    gr = ditq.GateResidualParams(res.data_ptr(), N, gate.data_ptr(), d["rows_per_gate"])
+    if in_place:
+        ditq.dit_gemm_gate_residual(f, codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, gr,
+                                    res.data_ptr(), N, st)
+        torch.cuda.synchronize()
+        return res.view(torch.int16).cpu().numpy().view(np.uint16)
+    ldo = ldo or N
+    out = torch.full((guard + M * ldo + guard,), -12345, dtype=torch.int16, device="cuda")
+    ditq.dit_gemm_gate_residual(f, codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, gr,
+                                out.data_ptr() + 2 * guard, ldo, st)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().view(np.uint16)
+    poison = np.uint16(-12345 & 0xFFFF)
+    assert np.all(o[:guard] == poison) and np.all(o[guard + M * ldo:] == poison)
+    body = o[guard:guard + M * ldo].reshape(M, ldo)
+    assert np.all(body[:, N:] == poison), "write past the output width"
+    res_after = res.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(res_after, d["residual"])             # the residual is only read
+    return body[:, :N].copy()
 
 
 SMALL = [
@@ -104,6 +144,10 @@ SMALL = [
     ("mlp_gated_silu", "mx8", "identity", 1, 320, 256, None),
     ("qkv_rmsnorm_hd128", "mx8", "qk_rmsnorm", 257, None, 512, 2),
     ("qkv_rmsnorm_hd256", "mx8", "qk_rmsnorm", 65, None, 512, 1),
+    ("mlp_gelu_tanh", "fp4", "gelu_tanh", 300, 768, 512, None),
+    ("mlp_gelu_tanh", "fp4", "gelu_tanh", 1, 256, 256, None),
+    ("mlp_gelu_tanh", "fp8", "gelu_tanh", 129, 512, 768, None),
+    ("mlp_gelu_tanh", "mx8", "gelu_tanh", 70, 1024, 256, None),
 ]
 
 
@@ -140,7 +184,8 @@ FULL = [("qkv_rmsnorm_hd128", "qk_rmsnorm", None), ("mlp_gated_silu", "gated_sil
         ("qkv_rmsnorm_hd256", "qk_rmsnorm", None), ("fp8_cfg_pair", "identity", None),
         ("fp8_cfg_pair", "gated_silu", None), ("qkv_rmsnorm_hd128", "qk_rmsnorm", "fp8"),
         ("qkv_rmsnorm_hd256", "qk_rmsnorm", "fp8"), ("mlp_gated_silu", "gated_silu", "mx8"),
-        ("qkv_rmsnorm_hd128", "qk_rmsnorm", "mx8"), ("fp8_cfg_pair", "identity", "mx8")]
+        ("qkv_rmsnorm_hd128", "qk_rmsnorm", "mx8"), ("fp8_cfg_pair", "identity", "mx8"),
+        ("mlp_gelu_tanh", "gelu_tanh", None)]
 
 
 @pytest.mark.parametrize("name,epi,fmt", FULL, ids=[f"{a}-{b}-{c or WORKLOADS[a].fmt}" for a, b, c in FULL])
@@ -169,3 +214,38 @@ def test_generic_entry_matches_format_entries(ditq, kind, fmt, epi, M, N, K, H):
     a = run_layer(ditq, d, fmt, epi, guard=16)
     b = run_layer(ditq, d, fmt, epi, guard=16, generic=True)
     np.testing.assert_array_equal(a, b)
+
+
+GR = [  # fmt, M, N, K, rows_per_gate, in_place
+    ("fp4", 300, 512, 512, 100, False),
+    ("fp4", 257, 768, 256, 129, True),
+    ("fp4", 1, 256, 256, 1, False),
+    ("fp8", 257, 512, 768, 129, False),
+    ("fp8", 64, 256, 256, 7, True),
+    ("mx8", 200, 768, 512, 64, False),
+    ("mx8", 70, 256, 1024, 1000, True),
+]
+
+
+@pytest.mark.parametrize("fmt,M,N,K,rpg,in_place", GR, ids=[f"{g[0]}-M{g[1]}-rpg{g[4]}-{'inplace' if g[5] else 'out'}"
+                                                             for g in GR])
+def test_gate_residual_all_elements(ditq, fmt, M, N, K, rpg, in_place):
+    from tests.gpu_util import compare_bf16
+    d = make_inputs("mlp_down_gate_residual", seed=M + rpg, M=M, N=N, K=K, rows_per_gate=rpg)
+    print(f"case gate_residual {fmt} M={M} N={N} K={K} rpg={rpg} in_place={in_place}", flush=True)
+    g = run_gate_residual(ditq, d, fmt, in_place=in_place, guard=0 if in_place else 32,
+                          ldo=None if in_place else N + 8)
+    compare_bf16(g, oracle_rows(d, fmt, "gate_residual"), f"gate_residual/{fmt}")
+
+
+def test_gate_residual_full_size_sampled_rows(ditq):
+    """The CFG-pair MLP down-projection, updating the residual stream in place."""
+    from tests.gpu_util import compare_bf16
+    wl = WORKLOADS["mlp_down_gate_residual"]
+    d = make_inputs(wl.name, seed=0)
+    print("case full mlp_down_gate_residual", flush=True)
+    g = run_gate_residual(ditq, d, "fp4", in_place=True)
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, 1, 4607, 4608, 4609, wl.M - 1], rng.choice(wl.M, 40, replace=False)]))
+    rep = compare_bf16(g[rows], oracle_rows(d, "fp4", "gate_residual", rows=rows), "mlp_down_gate_residual")
+    print(f"mlp_down_gate_residual: literal max err / row-RMS = {rep['literal_max_err_over_rowrms']:.4g}")

@@ -15,7 +15,7 @@ from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-EPI = {"identity": 0, "gated_silu": 1, "qk_rmsnorm": 2}
+EPI = {"identity": 0, "gated_silu": 1, "qk_rmsnorm": 2, "gelu_tanh": 3}
 
 
 @pytest.fixture(scope="module")
@@ -90,6 +90,7 @@ SMALL = [
     ("mlp_gated_silu", "identity", 1, 768, 256, None),
     ("qkv_rmsnorm_hd128", "qk_rmsnorm", 257, None, 256, 2),
     ("qkv_rmsnorm_hd256", "qk_rmsnorm", 65, None, 512, 1),
+    ("mlp_gelu_tanh", "gelu_tanh", 130, 768, 512, None),
 ]
 
 
