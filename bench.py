@@ -32,7 +32,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused FP4 GEMM+epilogue TFLOP/s and % of MI355X FP4 MFMA peak, M=4608 K=3072"
-PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "mx8": 5000.0}   # MI355X dense MFMA peaks (MXFP8 runs at the FP8 rate)
+# MI355X dense MFMA peaks of the instruction each format's products run on (MXFP8 at
+# the FP8 rate; NVFP4 is dequantized in registers onto the f16 MFMA)
+PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "mx8": 5000.0, "nv4": 2500.0}
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_fp4_mlp_gated_silu.txt")
 GEMM_SRC = os.path.join(ROOT, "bit_gemm_dit_amd", "csrc", "gemm.hip")
@@ -204,9 +206,9 @@ def time_other_configs(ditq, torch, args):
              ("qkv_rmsnorm_hd128", "qk_rmsnorm", "fp8"), ("qkv_rmsnorm_hd256", "qk_rmsnorm", "fp8"),
              ("mlp_gated_silu", "gated_silu", "mx8"), ("qkv_rmsnorm_hd128", "qk_rmsnorm", "mx8"),
              ("fp8_cfg_pair", "identity", "mx8"), ("mlp_gelu_tanh", "gelu_tanh", None),
-             ("mlp_down_gate_residual", "gate_residual", None)]
+             ("mlp_down_gate_residual", "gate_residual", None), ("mlp_gated_silu", "gated_silu", "nv4")]
     epis = {"identity": 0, "gated_silu": 1, "qk_rmsnorm": 2, "gelu_tanh": 3, "gate_residual": 4}
-    fmts = {"fp4": ditq.FMT_FP4, "fp8": ditq.FMT_FP8, "mx8": ditq.FMT_MX8}
+    fmts = {"fp4": ditq.FMT_FP4, "fp8": ditq.FMT_FP8, "mx8": ditq.FMT_MX8, "nv4": ditq.FMT_NV4}
     for name, epi_name, fmt_name in plans:
         wl = WORKLOADS[name]
         d = make_inputs(name, seed=0)
@@ -257,7 +259,7 @@ def time_other_configs(ditq, torch, args):
         g = times_g[len(times_g) // 2]
         q = times_q[len(times_q) // 2]
         qbytes = wl.M * wl.K * 2 + {1: wl.M * wl.K // 2 + wl.M * wl.K // 32, 2: wl.M * wl.K + 4 * wl.M,
-                                    3: wl.M * wl.K + wl.M * wl.K // 32}[fmt]
+                                    3: wl.M * wl.K + wl.M * wl.K // 32, 4: wl.M * wl.K // 2 + wl.M * wl.K // 16}[fmt]
         key = f"{name}/{epi_name}" + ("" if fmt_name == wl.fmt else f"/{fmt_name}")
         out[key] = {
             "gemm_us": round(g * 1e3, 2),

@@ -14,7 +14,7 @@ import ctypes
 import os
 
 __all__ = [
-    "FMT_FP4", "FMT_FP8", "FMT_MX8", "EPI_IDENTITY", "EPI_GATED_SILU", "EPI_QK_RMSNORM", "EPI_GELU_TANH",
+    "FMT_FP4", "FMT_FP8", "FMT_MX8", "FMT_NV4", "EPI_IDENTITY", "EPI_GATED_SILU", "EPI_QK_RMSNORM", "EPI_GELU_TANH",
     "EPI_GATE_RESIDUAL", "DitError", "RmsNormParams", "GateResidualParams",
     "dit_packed_weight_bytes", "dit_act_code_bytes", "dit_act_scale_bytes", "dit_pack_weights",
     "dit_quantize_act", "dit_gemm_q4_epilogue", "dit_gemm_q4_epilogue_q4", "dit_gemm_q8_epilogue",
@@ -26,6 +26,7 @@ __all__ = [
 FMT_FP4 = 1
 FMT_FP8 = 2
 FMT_MX8 = 3
+FMT_NV4 = 4
 EPI_IDENTITY = 0
 EPI_GATED_SILU = 1
 EPI_QK_RMSNORM = 2
@@ -193,6 +194,10 @@ def quantize_act(x, fmt: int):
     elif fmt == FMT_MX8:
         codes = torch.empty((K // 64, M, 64), dtype=torch.uint8, device=x.device)
         scales = torch.empty((K // 128, M, 4), dtype=torch.uint8, device=x.device)
+    elif fmt == FMT_NV4:
+        # block scales [K/128][M][8], then a 16-byte tail holding the tensor scale
+        codes = torch.empty((K // 128, M, 64), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((sb,), dtype=torch.uint8, device=x.device)
     else:
         codes = torch.empty((K // 64, M, 64), dtype=torch.uint8, device=x.device)
         scales = torch.empty((M,), dtype=torch.float32, device=x.device)

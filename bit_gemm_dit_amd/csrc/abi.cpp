@@ -19,11 +19,13 @@ namespace {
 using ditq::FMT_FP4;
 using ditq::FMT_FP8;
 using ditq::FMT_MX8;
+using ditq::FMT_NV4;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool valid_fmt(int f) {
-  return f == DIT_FMT_FP4_E2M1_MX32 || f == DIT_FMT_FP8_E4M3_ROWCOL || f == DIT_FMT_FP8_E4M3_MX32;
+  return f == DIT_FMT_FP4_E2M1_MX32 || f == DIT_FMT_FP8_E4M3_ROWCOL || f == DIT_FMT_FP8_E4M3_MX32 ||
+         f == DIT_FMT_FP4_E2M1_NV16;
 }
 bool valid_epi(int e) {
   return e == DIT_EPI_IDENTITY || e == DIT_EPI_GATED_SILU || e == DIT_EPI_QK_RMSNORM || e == DIT_EPI_GELU_TANH ||
@@ -38,11 +40,11 @@ bool shape_ok(int fmt, int epi, int N, int K) {
   if (K % 256 != 0 || N % 64 != 0) return false;
   if (epi == DIT_EPI_GATED_SILU && N % 128 != 0) return false;
   const size_t Np = (size_t)ditq::padded_rows(N);
-  const size_t code_bytes = fmt == FMT_FP4 ? Np * K / 2 : Np * K;
+  const size_t code_bytes = ditq::is_fp4_codes(fmt) ? Np * K / 2 : Np * K;
   return code_bytes < (1ull << 31);
 }
 bool rows_ok(int fmt, int M, int K) {
-  const size_t row = fmt == FMT_FP4 ? (size_t)K / 2 : (size_t)K;
+  const size_t row = ditq::is_fp4_codes(fmt) ? (size_t)K / 2 : (size_t)K;
   return ((size_t)M + 256) * row < (1ull << 31);
 }
 
@@ -90,12 +92,14 @@ size_t dit_packed_weight_bytes(dit_fmt fmt, dit_epi epi, int N, int K) {
 
 size_t dit_act_code_bytes(dit_fmt fmt, int M, int K) {
   if (!valid_fmt(fmt) || M <= 0 || K <= 0 || K % 256 != 0) return 0;
-  return fmt == DIT_FMT_FP4_E2M1_MX32 ? (size_t)M * K / 2 : (size_t)M * K;
+  return ditq::is_fp4_codes(fmt) ? (size_t)M * K / 2 : (size_t)M * K;
 }
 
 size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K) {
   if (!valid_fmt(fmt) || M <= 0 || K <= 0 || K % 256 != 0) return 0;
-  return fmt == DIT_FMT_FP8_E4M3_ROWCOL ? (size_t)M * 4 : (size_t)M * K / 32;
+  if (fmt == DIT_FMT_FP8_E4M3_ROWCOL) return (size_t)M * 4;
+  if (fmt == DIT_FMT_FP4_E2M1_NV16) return ditq::nv4_act_tail(M, K) + 16;
+  return (size_t)M * K / 32;
 }
 
 dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N, int K, int ldw, void* packed,
@@ -115,6 +119,7 @@ dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int l
   if (K % 256 != 0 || !rows_ok(fmt, M, K)) return DIT_EUNSUPPORTED;
   if (!aligned16(x_bf16) || !aligned16(codes) || ldx < K || ldx % 8 != 0) return DIT_EALIGN;
   if (fmt == DIT_FMT_FP8_E4M3_ROWCOL && !aligned(scales, 4)) return DIT_EALIGN;
+  if (fmt == DIT_FMT_FP4_E2M1_NV16 && !aligned16(scales)) return DIT_EALIGN;
   if (dit_status s = check_device()) return s;
   (void)hipGetLastError();
   const auto x = static_cast<const uint16_t*>(x_bf16);
@@ -124,6 +129,9 @@ dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int l
                                            static_cast<uint8_t*>(scales), st));
   if (fmt == DIT_FMT_FP8_E4M3_MX32)
     return launched(ditq::launch_quant_mx8(x, M, K, ldx, static_cast<uint8_t*>(codes),
+                                           static_cast<uint8_t*>(scales), st));
+  if (fmt == DIT_FMT_FP4_E2M1_NV16)
+    return launched(ditq::launch_quant_nv4(x, M, K, ldx, static_cast<uint8_t*>(codes),
                                            static_cast<uint8_t*>(scales), st));
   return launched(
       ditq::launch_quant_fp8(x, M, K, ldx, static_cast<uint8_t*>(codes), static_cast<float*>(scales), st));

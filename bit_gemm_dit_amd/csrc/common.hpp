@@ -21,7 +21,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-enum { FMT_FP4 = 1, FMT_FP8 = 2, FMT_MX8 = 3 };
+enum { FMT_FP4 = 1, FMT_FP8 = 2, FMT_MX8 = 3, FMT_NV4 = 4 };
 enum { EPI_IDENTITY = 0, EPI_GATED_SILU = 1, EPI_QK_RMSNORM = 2, EPI_GELU_TANH = 3, EPI_GATE_RESIDUAL = 4 };
 
 // ---------------------------------------------------------------- blob layout
@@ -31,12 +31,19 @@ constexpr int kHeaderBytes = 256;
 constexpr int kRowPad = 256;                   // packed rows are padded to a multiple of this
 
 __host__ __device__ inline int padded_rows(int N) { return (N + kRowPad - 1) / kRowPad * kRowPad; }
+constexpr int kNvTensorScaleOff = 56;          // NVFP4 blob: fp32 tensor scale in the header
+constexpr int kNvAmaxOff = 60;                 // ... and the packer's tensor-maximum slot
+
+__host__ __device__ constexpr bool is_fp4_codes(int fmt) { return fmt == FMT_FP4 || fmt == FMT_NV4; }
 __host__ __device__ inline size_t blob_code_bytes(int fmt, int Np, int K) {
-  return fmt == FMT_FP4 ? (size_t)Np * K / 2 : (size_t)Np * K;
+  return is_fp4_codes(fmt) ? (size_t)Np * K / 2 : (size_t)Np * K;
 }
 __host__ __device__ inline size_t blob_scale_bytes(int fmt, int Np, int K) {
-  return fmt == FMT_FP8 ? (size_t)Np * 4 : (size_t)Np * K / 32;
+  return fmt == FMT_FP8 ? (size_t)Np * 4 : fmt == FMT_NV4 ? (size_t)Np * K / 16 : (size_t)Np * K / 32;
 }
+// NVFP4 activation scales: M*K/16 block scale bytes, then a 16-byte tail holding the
+// tensor-maximum slot (u32) and the fp32 tensor scale.
+__host__ __device__ inline size_t nv4_act_tail(int M, int K) { return (size_t)M * K / 16; }
 __host__ __device__ inline size_t blob_scales_offset(int fmt, int Np, int K) {
   return kHeaderBytes + blob_code_bytes(fmt, Np, K);
 }
@@ -156,6 +163,38 @@ __device__ inline uint32_t mx8_encode4(uint32_t w0, uint32_t w1, uint32_t byte) 
   return (uint32_t)r;
 }
 
+// ---------------------------------------------------------------- NVFP4 encoding
+// Two levels of scaling (every step IEEE fp32): s_t = fl32(amax_tensor / 2688) (1 for
+// a zero tensor); per 16-element block s_b = RNE_E4M3(min(fl32(amax_b / fl32(6 s_t)),
+// 448)); elements RNE_E2M1(fl32(x / fl32(dec(s_b) s_t))), saturating at 6.
+__device__ inline float nv4_tensor_scale(uint32_t amax_bits) {
+  return amax_bits == 0 ? 1.0f : __uint_as_float(amax_bits << 16) / 2688.0f;
+}
+// E4M3 code of a non-negative block ratio d (round to nearest even, saturating).
+__device__ inline uint32_t nv4_scale_code(float d) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(d, 448.0f), 0.0f, 0, false) & 0xFFu;
+}
+// Eight bf16 values (one uint4) -> eight E2M1 codes (one dword, element 2j in the low
+// nibble of byte j), divided by `denom` = fl32(dec(s_b) * s_t).  The division is the
+// IEEE fp32 one; the conversion (scale 1) rounds to nearest even, saturates at 6 and
+// keeps the sign.  denom = 0 (an all-zero block scale) gives signed zeros.
+__device__ inline uint32_t nv4_encode8(v4i v, float denom) {
+  float y[8];
+  const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
+    y[2 * i] = denom == 0.0f ? lo * 0.0f : lo / denom;
+    y[2 * i + 1] = denom == 0.0f ? hi * 0.0f : hi / denom;
+  }
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[0], y[1], 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[2], y[3], 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[4], y[5], 1.0f, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6], y[7], 1.0f, 3);
+  return r;
+}
+
 // ---------------------------------------------------------------- buffer resources
 // Raw buffer descriptors: loads past num_records bytes return zeros, which
 // clips ragged tiles without branches.
@@ -185,6 +224,12 @@ hipError_t launch_quant_fp8(const uint16_t* x, int M, int K, int ldx, uint8_t* c
                             hipStream_t stream);
 hipError_t launch_quant_mx8(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
                             hipStream_t stream);
+// scales: M*K/16 block scale bytes plus the 16-byte tail (nv4_act_tail)
+hipError_t launch_quant_nv4(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream);
+// Largest bf16 magnitude (bit pattern) of x [R][ld] (first `cols` columns), merged into
+// *slot with an atomic maximum; the slot must hold 0 (or a smaller maximum) before.
+hipError_t launch_amax_bf16(const uint16_t* x, int R, int cols, int ld, uint32_t* slot, hipStream_t stream);
 hipError_t launch_pack(int fmt, int epi, const uint16_t* w, int N, int K, int ldw, uint8_t* blob,
                        hipStream_t stream);
 // Fused GEMM + epilogue in any format.  a_scales: FP4 / MXFP8 E8M0 bytes, FP8 fp32

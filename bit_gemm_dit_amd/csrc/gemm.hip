@@ -22,6 +22,13 @@
 //   64-K step).  MXFP8: the same with E4M3 operands (8 VGPRs) and E8M0 block
 //   scales, in the FP4 path's k-step of two 64-K units.  FP8: E4M3 operands and
 //   unit block scales; the fp32 row/column scales are applied in the epilogue.
+// * NVFP4 (E2M1 with E4M3 scales per 16 K and an fp32 tensor scale): the block-scaled
+//   MFMA takes only power-of-two scales per 32 K, so the FP4 fragments are
+//   dequantized in registers instead: E2M1 -> f16 (exact), times the E4M3 block
+//   scale as a packed f16 multiply (exact: at most 6 significant bits, within f16's
+//   range), into v_mfma_f32_32x32x16_f16 (four per 64-K unit); the two tensor scales
+//   multiply the accumulator in the epilogue.  Same loads, stages and lane layouts as
+//   FP4, at the f16 MFMA rate.
 // * A workgroup of 4 waves (one per SIMD) computes a 256 (features) x BM (tokens)
 //   tile; wave (wn, wm) owns 128 features x BM/2 tokens (4 x TM result tiles of
 //   32 x 32, TM = 3 or 4, up to 256 accumulators).
@@ -70,8 +77,10 @@ struct Tile {
   static constexpr bool MX = FMT != FMT_FP8;                   // E8M0 block scales applied by the MFMA
   static constexpr int CH = MX ? 2 : 1;                        // units per k-step
   static constexpr int KSTEP = 64 * CH;
-  static constexpr int FRAG = FMT == FMT_FP4 ? 1024 : 2048;    // bytes of one 32x64 operand fragment
+  static constexpr bool NV = FMT == FMT_NV4;                   // E4M3 block-16 scales, dequantized in registers
+  static constexpr int FRAG = is_fp4_codes(FMT) ? 1024 : 2048; // bytes of one 32x64 operand fragment
   static constexpr int FRAG_LOADS = FRAG / 1024;               // 16-byte loads per lane per fragment
+  static constexpr int MFMA_PER_UNIT = NV ? 4 : 1;             // MFMAs per result tile and 64-K unit
   static constexpr int APANELS = FMT == FMT_MX8 ? 2 : 1;       // 64-byte activation code panels per k-step
   static constexpr int TND = TN - WLDS;                        // weight groups loaded into registers
   static constexpr int UNIT_LOADS = TND * FRAG_LOADS;
@@ -83,9 +92,10 @@ struct Tile {
   static constexpr int A_OFF = W_BYTES;
   static constexpr int A_BYTES = BM * kRowBytes * APANELS;
   static constexpr int AS_OFF = A_OFF + A_BYTES;
-  static constexpr int AS_BYTES = MX ? (3 * BM + 256 + 255) / 256 * 256 : 0;
+  // scale bytes per token / per 32-row group and 128-K step: E8M0 4 / 128, NVFP4 8 / 256
+  static constexpr int AS_BYTES = NV ? (6 * BM + 1024 + 255) / 256 * 256 : MX ? (3 * BM + 256 + 255) / 256 * 256 : 0;
   static constexpr int WS_OFF = AS_OFF + AS_BYTES;
-  static constexpr int WS_BYTES = MX ? BN / 32 * 128 : 0;
+  static constexpr int WS_BYTES = NV ? BN / 32 * 256 : MX ? BN / 32 * 128 : 0;
   static constexpr int STAGE = (WS_OFF + WS_BYTES + 255) / 256 * 256;
   static constexpr int STAGES_FIT = (160 * 1024 - 1024 - (HD == 256 ? WAVES_N * BM * 4 : 0)) / STAGE;
   static constexpr int WCK = W_BYTES / 1024 / NW;            // 1 KB weight copies per wave per stage
@@ -121,7 +131,9 @@ struct Tile {
                                        : 2 * (STAGES > RING - 1 ? STAGES : RING - 1);
   static_assert(A_BYTES == ACK * 1024 * NW && W_BYTES == WCK * 1024 * NW, "whole 1 KB copies per wave");
   static_assert(WLDS >= 0 && WLDS <= TN, "weight groups split between LDS and registers");
-  static_assert(3 * BM + 256 <= AS_BYTES || !MX, "overlapping scale-word copies fit");
+  static_assert(NV ? 6 * BM + 1024 <= AS_BYTES && 8 * BM <= 6 * BM + 1024 && WS_BYTES == 2048
+                   : 3 * BM + 256 <= AS_BYTES || !MX,
+                "overlapping scale copies fit and cover the tile");
   static_assert(ACK % APANELS == 0, "whole activation copies per panel");
   static_assert(WLDS == 0 || GROUP_BYTES == 2048, "LDS weight groups are copied as two 1 KB halves");
   static_assert(RING % CH == 0 && RING >= 4, "ring holds whole k-steps");
@@ -148,6 +160,8 @@ struct Params {
   const float* gamma_k;
   float eps;
   int n_heads;
+  const float* a_tscale;      // NVFP4 tensor scales (device)
+  const float* w_tscale;
 };
 
 // Activation LDS rows are 64 bytes = 4 chunks of 16 bytes; chunk c of row r is
@@ -275,7 +289,7 @@ __device__ __forceinline__ void load_act(AFrag<T>& f, const uint8_t* stage, int 
   for (int tm = 0; tm < T::TM; ++tm) {
     const int r = wm * T::WM + 32 * tm + l32;
     const uint8_t* row = stage + r * kRowBytes;
-    if constexpr (T::FMT == FMT_FP4) {
+    if constexpr (is_fp4_codes(T::FMT)) {
       f.a[tm][0] = *reinterpret_cast<const v4i*>(row + 16 * ((2 * J + h) ^ swz(r)));
     } else {
       // 8-bit operands: the MFMA takes k = 16h .. 16h+15 in its first four registers
@@ -298,15 +312,30 @@ struct WUnit {
 // 2*(tn%2) + J, picked by op_sel).  A token's 4 scale bytes are its blocks 0..3 of
 // the step, and this lane's units J = 0, 1 take blocks 2J + h (selector byte 0x0C
 // gives a zero byte).
+// NVFP4: a weight word holds the lane's four E4M3 bytes of the k-step (unit J, block
+// b at byte 2J + b); an activation word the token's four bytes for this lane group.
 template <class T>
 struct Scales {
-  uint32_t w[T::TN / 2];
+  uint32_t w[T::NV ? T::TN : T::TN / 2];
   uint32_t a[T::TM];
 };
 
 template <class T>
 __device__ __forceinline__ void load_scales(Scales<T>& sc, const uint8_t* stage, int wn, int wm, int lane) {
-  if constexpr (T::MX) {
+  if constexpr (T::NV) {
+    const int l32 = lane & 31;
+    // the token's 8 bytes are blocks 0..7 of the step; this lane group takes blocks
+    // 4J + 2h + b, i.e. bytes (2h, 2h+1, 4+2h, 5+2h)
+    const uint32_t sel = (lane & 32) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int tn = 0; tn < T::TN; ++tn)
+      sc.w[tn] = *reinterpret_cast<const uint32_t*>(stage + T::WS_OFF + (wn * T::TN + tn) * 256 + 4 * lane);
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm) {
+      const uint2 v = *reinterpret_cast<const uint2*>(stage + T::AS_OFF + 8 * (wm * T::WM + 32 * tm + l32));
+      sc.a[tm] = __builtin_amdgcn_perm(v.y, v.x, sel);
+    }
+  } else if constexpr (T::MX) {
     const int l32 = lane & 31;
 #pragma unroll
     for (int t2 = 0; t2 < T::TN / 2; ++t2) {
@@ -322,7 +351,7 @@ __device__ __forceinline__ void load_scales(Scales<T>& sc, const uint8_t* stage,
 
 template <class T>
 __device__ __forceinline__ void select_scales(Scales<T>& sc, int lane) {
-  if constexpr (T::MX) {
+  if constexpr (T::MX && !T::NV) {
     const uint32_t sel = (lane & 32) ? 0x0C0C0301u : 0x0C0C0200u;
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) sc.a[tm] = __builtin_amdgcn_perm(0u, sc.a[tm], sel);
@@ -347,9 +376,47 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// NVFP4: eight E2M1 codes (one dword) times an f16 block scale -> eight f16 (exact).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8 nv4_dequant8(uint32_t codes, _Float16 s) {
+  const f16x2 ss = {s, s};
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+__device__ __forceinline__ _Float16 nv4_scale(uint32_t word, int byte) {
+  return (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)(word >> (8 * byte)), 0);
+}
+
 template <class T, int J, int TM0, int TM1, bool ZERO>
 __device__ __forceinline__ void mfma_part(v16f (&acc)[T::TN][T::TM], const WUnit<T>& wu, const AFrag<T>& f,
                                           const Scales<T>& sc) {
+  if constexpr (T::NV) {
+    // Sub-step i takes dword i of every fragment (codes 8i .. 8i+7 of the lane, block
+    // i/2): A and B lanes pair element by element, so any lane-local K order shared
+    // by both operands gives the same dot product.
+    static_for<0, 4>([&](auto i_c) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_c)::value, b = i / 2;
+      f16x8 wv[T::TN], av[T::TM];
+#pragma unroll
+      for (int tn = 0; tn < T::TN; ++tn) {
+        const v4i x = tn < T::WLDS ? f.w[tn < T::WLDS ? tn : 0][0] : wu.w[tn >= T::WLDS ? tn - T::WLDS : 0][0];
+        wv[tn] = nv4_dequant8((uint32_t)x[i], nv4_scale(sc.w[tn], 2 * J + b));
+      }
+#pragma unroll
+      for (int tm = TM0; tm < TM1; ++tm) av[tm] = nv4_dequant8((uint32_t)f.a[tm][0][i], nv4_scale(sc.a[tm], 2 * J + b));
+#pragma unroll
+      for (int tn = 0; tn < T::TN; ++tn)
+#pragma unroll
+        for (int tm = TM0; tm < TM1; ++tm)
+          acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[tn], av[tm], (ZERO && i == 0) ? v16f{} : acc[tn][tm],
+                                                                0, 0, 0);
+    });
+    return;
+  }
   static_for<0, T::TN>([&](auto tn_c) __attribute__((always_inline)) {
     constexpr int tn = decltype(tn_c)::value;
     v8i w;
@@ -400,6 +467,16 @@ template <class T>
 __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::TM], int n0w, int m0w, int lane,
                                          int wn, int wm, uint8_t* lds) {
   const int h = lane >> 5, l32 = lane & 31;
+  if constexpr (T::NV) {
+    // the two tensor scales, before any small op
+    const float ts = *p.a_tscale * *p.w_tscale;
+#pragma unroll
+    for (int tn = 0; tn < T::TN; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < T::TM; ++tm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tn][tm][r] *= ts;
+  }
   if constexpr (T::EPI != EPI_QK_RMSNORM) {
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) {
@@ -676,8 +753,9 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
   const auto w_rsrc = make_rsrc(p.w_codes, p.w_bytes);
   [[maybe_unused]] const auto as_rsrc = make_rsrc(p.a_scales, p.as_bytes);
   [[maybe_unused]] const auto ws_rsrc = make_rsrc(p.w_scales, p.ws_bytes);
-  [[maybe_unused]] const uint32_t as_step = (uint32_t)p.M * 4u;  // one K panel of activation scale words
-  [[maybe_unused]] const uint32_t ws_step = (uint32_t)(padded_rows(p.N) / 32) * 128u;
+  // one 128-K panel of activation scale rows / of weight scale records
+  [[maybe_unused]] const uint32_t as_step = (uint32_t)p.M * (T::NV ? 8u : 4u);
+  [[maybe_unused]] const uint32_t ws_step = (uint32_t)(padded_rows(p.N) / 32) * (T::NV ? 256u : 128u);
 
   // Weight cursor: tile and unit that the next weight loads fetch.  Lane L of
   // fragment (group g, unit u) sits at g * wgroup + u * FRAG + L * FRAG/64.
@@ -721,7 +799,13 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
       const int band = grp / (T::WLDS > 0 ? T::WLDS : 1), g = grp % (T::WLDS > 0 ? T::WLDS : 1);
       w_off[c] = (uint32_t)(n0 / 32 + band * T::TN + g) * wgroup + 1024u * (q & 1) + 16u * lane;
     }
-    if constexpr (T::MX) {
+    if constexpr (T::NV) {
+      // 16 bytes per lane: wave w copies 1 KB of activation scale rows from byte 2w*BM
+      // (overlapping, together the tile's 8*BM bytes) and weight records from byte
+      // 1 KB*(w%2) (waves 2, 3 repeat waves 0, 1)
+      as_off = (uint32_t)m0 * 8u + (uint32_t)(2 * wave * T::BM) + 16u * lane;
+      ws_off = (uint32_t)(n0 / 32) * 256u + 1024u * (wave & 1) + 16u * lane;
+    } else if constexpr (T::MX) {
       as_off = (uint32_t)m0 * 4u + (uint32_t)(wave * T::BM) + 4u * lane;
       ws_off = (uint32_t)(n0 / 32) * 128u + 256u * wave + 4u * lane;
     }
@@ -737,7 +821,10 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
       copy_to_lds<16>(a_rsrc, a_off, (ac_ks * T::APANELS + panel) * a_panel + cc * 1024,
                       base + T::A_OFF + panel * T::BM * kRowBytes + (wave * T::ACKP + cc) * 1024);
     }
-    if constexpr (T::MX) {
+    if constexpr (T::NV) {
+      copy_to_lds<16>(as_rsrc, as_off, ac_ks * as_step, base + T::AS_OFF + 2 * wave * T::BM);
+      copy_to_lds<16>(ws_rsrc, ws_off, ac_ks * ws_step, base + T::WS_OFF + 1024 * (wave & 1));
+    } else if constexpr (T::MX) {
       copy_to_lds<4>(as_rsrc, as_off, ac_ks * as_step, base + T::AS_OFF + wave * T::BM);
       copy_to_lds<4>(ws_rsrc, ws_off, ac_ks * ws_step, base + T::WS_OFF + 256 * wave);
     }
@@ -826,7 +913,7 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
       load_act<T, 1>(fb, lds + cur, wn, wm, lane);
       load_unit<T>(ring[l0], w_rsrc, wbase, wc_u, (int)wgroup);
       mfma_part<T, 0, 0, T::TM, ZERO>(acc, ring[u0], fa, sc);
-      spread_vmem<T::TN * T::TM, T::UNIT_LOADS>();
+      spread_vmem<T::TN * T::TM * T::MFMA_PER_UNIT, T::UNIT_LOADS>();
       pin_accumulators<T>(acc);
       __builtin_amdgcn_sched_barrier(0);
       advance_w();
@@ -838,7 +925,7 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
       load_scales<T>(sn, lds + nxt, wn, wm, lane);
       load_act<T, 0>(fa, lds + nxt, wn, wm, lane);
       mfma_part<T, 1, 0, T::TM, false>(acc, ring[u1], fb, sc);
-      spread_vmem<T::TN * T::TM, T::NCOPY + T::UNIT_LOADS>();
+      spread_vmem<T::TN * T::TM * T::MFMA_PER_UNIT, T::NCOPY + T::UNIT_LOADS>();
       pin_accumulators<T>(acc);
       __builtin_amdgcn_sched_barrier(0);
       advance_w();
@@ -914,7 +1001,9 @@ hipError_t launch(Params& p, hipStream_t stream) {
 // 4, else 4 (FP8 and MXFP8: 4).
 template <int FMT, int EPI, int HD = 0, int WLDS = wlds_for(FMT)>
 hipError_t launch_cfg(Params& p, hipStream_t stream) {
-  if constexpr (FMT != FMT_FP4) {
+  if constexpr (FMT == FMT_NV4) {
+    return launch<Tile<FMT, EPI, 3, 4, 2, HD>>(p, stream);
+  } else if constexpr (FMT != FMT_FP4) {
     return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
   } else {
     const int nks = p.K / 128;
@@ -970,9 +1059,13 @@ hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, co
   p.N = N;
   p.K = K;
   p.ldo = ldo;
-  p.a_bytes = (uint32_t)((size_t)M * (fmt == FMT_FP4 ? K / 2 : K));
+  p.a_bytes = (uint32_t)((size_t)M * (is_fp4_codes(fmt) ? K / 2 : K));
   p.w_bytes = (uint32_t)blob_code_bytes(fmt, Np, K);
-  p.as_bytes = (uint32_t)((size_t)M * (fmt == FMT_FP8 ? 4 : K / 32));
+  p.as_bytes = (uint32_t)((size_t)M * (fmt == FMT_FP8 ? 4 : fmt == FMT_NV4 ? K / 16 : K / 32));
+  if (fmt == FMT_NV4) {
+    p.a_tscale = reinterpret_cast<const float*>(static_cast<const uint8_t*>(a_scales) + nv4_act_tail(M, K) + 4);
+    p.w_tscale = reinterpret_cast<const float*>(blob + kNvTensorScaleOff);
+  }
   p.ws_bytes = (uint32_t)blob_scale_bytes(fmt, Np, K);
   if (gr) {
     p.residual = gr->residual;
@@ -981,6 +1074,7 @@ hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, co
     p.rows_per_gate = gr->rows_per_gate;
   }
   if (fmt == FMT_FP4) return launch_epi<FMT_FP4>(p, epi, rms, stream);
+  if (fmt == FMT_NV4) return launch_epi<FMT_NV4>(p, epi, rms, stream);
   if (fmt == FMT_MX8) return launch_epi<FMT_MX8>(p, epi, rms, stream);
   return launch_epi<FMT_FP8>(p, epi, rms, stream);
 }

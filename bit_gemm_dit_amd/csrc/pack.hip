@@ -113,6 +113,50 @@ __global__ __launch_bounds__(256) void pack_mx8_kernel(const uint16_t* __restric
   sc[((size_t)(c / 2) * (Np / 32) + g) * 128 + 2 * L + (c & 1)] = (uint8_t)(h ? byte1 : byte0);
 }
 
+// NVFP4: the header (and a cleared tensor-maximum slot) first, in a launch of its own,
+// so that the tensor maximum can be merged into the slot before the codes are packed.
+__global__ void nv4_header_kernel(uint8_t* blob, int epi, int N, int K, int Np) {
+  write_header(blob, FMT_NV4, epi, N, K, Np);       // zeroes the slot and the tensor scale
+}
+
+// NVFP4 codes: one thread per (fragment, lane) as FP4; the lane's 32 elements are two
+// 16-element blocks (4c + 2h and 4c + 2h + 1 of the row, h = L/32), each with its own
+// E4M3 scale.  Scale record (s = c/2, g): 256 bytes, byte 4L + 2(c%2) + b.
+__global__ __launch_bounds__(256) void pack_nv4_kernel(const uint16_t* __restrict__ w, int N, int K,
+                                                       int ldw, int epi, int Np,
+                                                       uint8_t* __restrict__ blob) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t kc = (uint32_t)K / 64;
+  const uint32_t total = (uint32_t)Np / 32 * kc * 64;
+  const float st = nv4_tensor_scale(*reinterpret_cast<const uint32_t*>(blob + kNvAmaxOff));
+  const float six_st = 6.0f * st;
+  if (t == 0) *reinterpret_cast<float*>(blob + kNvTensorScaleOff) = st;
+  if (t >= total) return;
+  const uint32_t L = t & 63, frag = t >> 6;
+  const uint32_t c = frag % kc, g = frag / kc;
+  const int p = (int)(32 * g + (L & 31));
+  const int src = packed_row_source(epi, N, p);
+  v4i out = {0, 0, 0, 0};
+  uint32_t sb0 = 0, sb1 = 0;
+  if (src >= 0) {
+    const v4i* wp = reinterpret_cast<const v4i*>(w + (size_t)src * ldw + 64 * c + 32 * (L >> 5));
+    const v4i v0 = wp[0], v1 = wp[1], v2 = wp[2], v3 = wp[3];
+    sb0 = nv4_scale_code(__uint_as_float(max(absmax8(v0), absmax8(v1)) << 16) / six_st);
+    sb1 = nv4_scale_code(__uint_as_float(max(absmax8(v2), absmax8(v3)) << 16) / six_st);
+    const float d0 = __builtin_amdgcn_cvt_f32_fp8((int)sb0, 0) * st;
+    const float d1 = __builtin_amdgcn_cvt_f32_fp8((int)sb1, 0) * st;
+    out.x = (int)nv4_encode8(v0, d0);
+    out.y = (int)nv4_encode8(v1, d0);
+    out.z = (int)nv4_encode8(v2, d1);
+    out.w = (int)nv4_encode8(v3, d1);
+  }
+  *reinterpret_cast<v4i*>(blob + kHeaderBytes + (size_t)frag * 1024 + 16 * L) = out;
+  uint8_t* sc = blob + blob_scales_offset(FMT_NV4, Np, K) + ((size_t)(c / 2) * (Np / 32) + g) * 256 + 4 * L +
+                2 * (c & 1);
+  sc[0] = (uint8_t)sb0;
+  sc[1] = (uint8_t)sb1;
+}
+
 // FP8: one wave per packed row.  Pass 1 finds the row's amax (-> s_w), pass 2
 // encodes 16-element runs; run r (k = 16r ..) lands in fragment (g, r/4), lane
 // p%32 + 32*(r%2), byte 16*((r/2)%2) (the 8-bit fragment order above).
@@ -160,7 +204,16 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const uint16_t* __restric
 hipError_t launch_pack(int fmt, int epi, const uint16_t* w, int N, int K, int ldw, uint8_t* blob,
                        hipStream_t stream) {
   const int Np = padded_rows(N);
-  if (fmt == FMT_FP4 || fmt == FMT_MX8) {
+  if (fmt == FMT_NV4) {
+    // header + cleared slot, the tensor maximum of W (logical rows; padding rows are
+    // zero), then the codes and scales
+    hipLaunchKernelGGL(nv4_header_kernel, dim3(1), dim3(1), 0, stream, blob, epi, N, K, Np);
+    if (hipError_t e = launch_amax_bf16(w, N, K, ldw, reinterpret_cast<uint32_t*>(blob + kNvAmaxOff), stream))
+      return e;
+    const uint32_t total = (uint32_t)Np / 32 * ((uint32_t)K / 64) * 64;
+    hipLaunchKernelGGL(pack_nv4_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, w, N, K, ldw, epi, Np,
+                       blob);
+  } else if (fmt == FMT_FP4 || fmt == FMT_MX8) {
     const uint32_t total = (uint32_t)Np / 32 * ((uint32_t)K / 64) * 64;
     hipLaunchKernelGGL(fmt == FMT_FP4 ? pack_fp4_kernel : pack_mx8_kernel, dim3((total + 255) / 256), dim3(256), 0,
                        stream, w, N, K, ldw, epi, Np, blob);

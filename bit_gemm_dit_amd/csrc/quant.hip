@@ -10,6 +10,10 @@
 // X DataCrunch", engine list: FP8 mixed precision).
 // MXFP8: bf16 [M, K] -> E4M3 codes (the FP8 code layout) + E8M0 block-32 scales (the
 // FP4 scale layout), scales computed per call like the FP4 path's.
+// NVFP4: bf16 [M, K] -> E2M1 codes (the FP4 code layout) + E4M3 block-16 scales + one
+// fp32 tensor scale (the 4-bit format page "How fal made Ideogram V4 6x faster"
+// names, paragraph 2), in three launches: clear the tensor-maximum slot, an atomic
+// tensor maximum, then the quantizer.
 //
 // All kernels are HBM-bound streams: 2 bytes read per element, 0.5 + 1/32 (FP4),
 // 1 (FP8) or 1 + 1/32 (MXFP8) bytes written.  Outputs are K-panel-major
@@ -69,6 +73,57 @@ __global__ __launch_bounds__(256) void quant_mx8_kernel(const uint16_t* __restri
     q.y = mx8_encode4((uint32_t)v.z, (uint32_t)v.w, byte);
     *reinterpret_cast<uint2*>(codes + ((size_t)(col >> 3) * M + row) * 64 + 8 * (col & 7)) = q;
     if ((threadIdx.x & 3) == 0) scales[((size_t)(col >> 4) * M + row) * 4 + ((col >> 2) & 3)] = (uint8_t)byte;
+  }
+}
+
+// Tensor maximum: one thread per 8 elements, grid-stride over a few hundred
+// workgroups; each workgroup reduces its 256 lanes (waves, then LDS) and merges its
+// maximum with one global atomic maximum (bf16 magnitude bit patterns order like
+// their values, so the unsigned maximum is the maximum).  One atomic per workgroup
+// keeps the contention on the single slot negligible.
+__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int ld, uint32_t total,
+                                                   uint32_t per_row, uint32_t* slot) {
+  __shared__ uint32_t wave_max[4];
+  uint32_t m = 0;
+  const uint32_t stride = gridDim.x * 256u;
+  for (uint32_t c = blockIdx.x * 256u + threadIdx.x; c < total; c += stride) {
+    const uint32_t row = c / per_row, col = c - row * per_row;
+    m = max(m, absmax8(*reinterpret_cast<const v4i*>(x + (size_t)row * ld + (size_t)col * 8)));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+    if (m != 0) atomicMax(slot, m);
+  }
+}
+
+__global__ void clear_slot_kernel(uint32_t* slot) { slot[0] = 0u; }
+
+// NVFP4: the FP4 kernel's structure; a block of 16 is one lane pair (DPP xor 1).
+// Chunk `col` (8 elements) goes to the FP4 code position; its block (col/2) scale to
+// byte (col/2) % 8 of the token's 8-byte row of 128-element panel col/16.
+__global__ __launch_bounds__(256) void quant_nv4_kernel(const uint16_t* __restrict__ x, int M, int ldx,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales, uint32_t total,
+                                                        uint32_t per_row, const uint32_t* amax_slot,
+                                                        float* tensor_scale) {
+  const float st = nv4_tensor_scale(*amax_slot);
+  const float six_st = 6.0f * st;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = st;
+  const uint32_t stride = gridDim.x * 256u;
+  for (uint32_t c = blockIdx.x * 256u + threadIdx.x; c < total; c += stride) {
+    const uint32_t row = c / per_row, col = c - row * per_row;
+    const v4i v = *reinterpret_cast<const v4i*>(x + (size_t)row * ldx + (size_t)col * 8);
+    uint32_t m = absmax8(v);
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kQuadXor1, 0xF, 0xF, false));
+    const uint32_t sb = nv4_scale_code(__uint_as_float(m << 16) / six_st);
+    const float denom = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * st;
+    const size_t prow = (size_t)(col >> 4) * M + row;
+    *reinterpret_cast<uint32_t*>(codes + prow * 64 + 4 * (col & 15)) = nv4_encode8(v, denom);
+    if ((threadIdx.x & 1) == 0) scales[prow * 8 + ((col >> 1) & 7)] = (uint8_t)sb;
   }
 }
 
@@ -158,6 +213,31 @@ hipError_t launch_quant_mx8(const uint16_t* x, int M, int K, int ldx, uint8_t* c
   if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(quant_mx8_kernel, dim3(blocks), dim3(256), 0, stream, x, M, ldx, codes, scales, total,
                      per_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_bf16(const uint16_t* x, int R, int cols, int ld, uint32_t* slot, hipStream_t stream) {
+  const uint32_t per_row = (uint32_t)cols / 8;
+  const uint32_t total = (uint32_t)R * per_row;
+  uint32_t blocks = (total + 255) / 256;
+  const uint32_t cap = 512u;                              // two workgroups per CU, grid-stride beyond
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(256), 0, stream, x, ld, total, per_row, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nv4(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream) {
+  uint32_t* slot = reinterpret_cast<uint32_t*>(scales + nv4_act_tail(M, K));
+  hipLaunchKernelGGL(clear_slot_kernel, dim3(1), dim3(1), 0, stream, slot);
+  if (hipError_t e = launch_amax_bf16(x, M, K, ldx, slot, stream)) return e;
+  const uint32_t per_row = (uint32_t)K / 8;
+  const uint32_t total = (uint32_t)M * per_row;
+  uint32_t blocks = (total + 255) / 256;
+  const uint32_t cap = 256u * 32u;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(quant_nv4_kernel, dim3(blocks), dim3(256), 0, stream, x, M, ldx, codes, scales, total,
+                     per_row, slot, reinterpret_cast<float*>(slot + 1));
   return hipGetLastError();
 }
 

@@ -4,7 +4,8 @@
  *
  * The layer: bf16 activations are quantized on the fly to a 4-bit float (FP4
  * E2M1, one E8M0 scale per 32 consecutive K elements), to FP8 E4M3 with one fp32
- * scale per row, or to MXFP8 (E4M3, one E8M0 scale per 32 K elements); they are
+ * scale per row, to MXFP8 (E4M3, one E8M0 scale per 32 K elements), or to NVFP4
+ * (E2M1, one E4M3 scale per 16 K elements and one fp32 scale per tensor); they are
  * multiplied with pre-packed low-bit weights on the
  * scaled MFMA units; the small op that follows the GEMM (identity, gated-SiLU,
  * per-head QK-RMSNorm) is applied to the fp32 accumulator before the single bf16
@@ -51,7 +52,8 @@ typedef enum {
 typedef enum {
   DIT_FMT_FP4_E2M1_MX32 = 1,   /* E2M1 codes + one E8M0 scale per 32 K elements */
   DIT_FMT_FP8_E4M3_ROWCOL = 2, /* OCP E4M3 codes + fp32 per-row / per-column scales */
-  DIT_FMT_FP8_E4M3_MX32 = 3    /* OCP E4M3 codes + one E8M0 scale per 32 K elements (MXFP8) */
+  DIT_FMT_FP8_E4M3_MX32 = 3,   /* OCP E4M3 codes + one E8M0 scale per 32 K elements (MXFP8) */
+  DIT_FMT_FP4_E2M1_NV16 = 4    /* E2M1 codes + one E4M3 scale per 16 K elements + fp32 tensor scale (NVFP4) */
 } dit_fmt;
 
 typedef enum {
@@ -101,12 +103,12 @@ typedef struct {
 
 /* Bytes of the packed weight blob written by dit_pack_weights.  Rows are padded
  * to Np = ceil(N / 256) * 256.  FP4: 256 + Np*K/2 + Np*K/32.  FP8: 256 + Np*K + 4*Np.
- * MXFP8: 256 + Np*K + Np*K/32. */
+ * MXFP8: 256 + Np*K + Np*K/32.  NVFP4: 256 + Np*K/2 + Np*K/16. */
 size_t dit_packed_weight_bytes(dit_fmt fmt, dit_epi epi, int N, int K);
 
 /* Bytes of the activation codes / scales written by dit_quantize_act.
  * FP4: codes M*K/2, scales M*K/32.  FP8: codes M*K, scales 4*M.  MXFP8: codes M*K,
- * scales M*K/32. */
+ * scales M*K/32.  NVFP4: codes M*K/2, scales M*K/16 + 16. */
 size_t dit_act_code_bytes(dit_fmt fmt, int M, int K);
 size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
 
@@ -119,9 +121,9 @@ size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
  * called with DIT_EPI_GATED_SILU too.  Blobs packed for every other epilogue are
  * identical (bar the epi field of the header) and interchangeable.
  *
- * Quantization rule, per weight row: FP4 and MXFP8 -- the same rule as
- * dit_quantize_act along K; FP8 -- s_w[n] = fl32(amax_n / 448) (1 if the row is
- * zero), codes RNE_E4M3(fl32(w / s_w[n])).
+ * Quantization rule, per weight row: FP4, MXFP8 and NVFP4 -- the same rule as
+ * dit_quantize_act along K (NVFP4: with the tensor maximum of W); FP8 -- s_w[n] =
+ * fl32(amax_n / 448) (1 if the row is zero), codes RNE_E4M3(fl32(w / s_w[n])).
  *
  * Blob layout (little-endian; the GEMM relies on it, tests decode it):
  *   header, 256 bytes: u32 magic 0x51544944 ("DITQ"), u32 layout version 2,
@@ -151,6 +153,11 @@ size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
  *   MXFP8 codes: the FP8 code layout.  MXFP8 scales: the FP4 scale layout (128-byte
  *     records (s, g), byte 2*L + j = the E8M0 scale of packed row 32g + L%32 for
  *     the K block 4s + 2j + L/32).
+ *   NVFP4 codes: the FP4 code layout.  NVFP4 scales: 256-byte records (s, g) at
+ *     scales offset + (s*Np/32 + g)*256; byte 4*L + 2*j + b is the E4M3 scale of
+ *     packed row 32g + L%32 for the 16-element K block 8s + 4j + 2*(L/32) + b.  The
+ *     fp32 tensor scale is stored in the header at byte 56 (byte 60 is work space
+ *     of the packer).
  *
  * Supported: K % 256 == 0; N % 64 == 0 (GATED_SILU: N % 128 == 0); ldw >= K,
  * ldw % 8 == 0; w_bf16 and packed 16-byte aligned.  W must be finite. */
@@ -185,6 +192,16 @@ dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N,
  *   code = RNE_E4M3(min(|x| / 2^(byte-127), 448)) with the sign of x.
  *   Codes in the FP8 layout (64-element panels); scales in the FP4 layout
  *   (byte (s*M + m)*4 + (k%128)/32, s = k / 128).
+ * NVFP4 (the 4-bit format of page "How fal made Ideogram V4 6x faster", paragraph
+ * 2, with its two levels of scaling), every step IEEE fp32:
+ *   s_t = fl32(amax_tensor / 2688) (2688 = 6 * 448; 1 for an all-zero tensor);
+ *   per row and 16-element K block: s_b = RNE_E4M3(min(fl32(amax_b / fl32(6 s_t)),
+ *   448)); code = sign(x) | RNE_E2M1(min(|fl32(x / fl32(dec(s_b) s_t))|, 6)),
+ *   magnitude 0 where s_b = 0.
+ *   Codes in the FP4 layout.  Scales: byte (s*M + m)*8 + (k%128)/16, s = k / 128,
+ *   then a 16-byte tail at byte M*K/16: u32 work space, then the fp32 tensor scale
+ *   s_t.  Three kernel launches (the tensor maximum is a grid-wide reduction);
+ *   the scales buffer must be 16-byte aligned.
  *
  * Supported: K % 256 == 0, ldx >= K, ldx % 8 == 0, pointers 16-byte aligned
  * (FP4 and MXFP8 scales: any alignment).  x must be finite. */
@@ -245,7 +262,11 @@ dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, cons
  *   fmt = DIT_FMT_FP8_E4M3_ROWCOL: dit_gemm_q8_epilogue (a_scales: fp32 [M]),
  *     plus QK_RMSNORM, applied to (A W^T) * s_a[m] * s_w[n];
  *   fmt = DIT_FMT_FP8_E4M3_MX32: out = epi(A W^T), A and W MXFP8 (E4M3 codes with
- *     E8M0 block scales applied inside the product, as for FP4), every epilogue.
+ *     E8M0 block scales applied inside the product, as for FP4), every epilogue;
+ *   fmt = DIT_FMT_FP4_E2M1_NV16: out = epi((sum_k A W) * s_t(A) * s_t(W)) with the
+ *     E4M3 block scales inside the sum: the NVFP4 product, exact up to fp32
+ *     accumulation (the elements and block scales are multiplied exactly in
+ *     f16 before an f16 matrix multiply), every epilogue.
  * FP8 as the safer precision beside the 4-bit format: page "WaveSpeedAI X
  * DataCrunch: FLUX real-time image inference on B200", engine list; page on
  * FLUX.1-dev inference optimization with LoRA (aitime.ge), FP8 quantization as

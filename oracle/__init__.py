@@ -9,8 +9,9 @@ What it computes (plain, slow, obviously correct; float64 for floating point):
 * ``formats``  -- decoding of bf16, FP4 E2M1, E8M0 and FP8 E4M3 codes.
 * ``quant``    -- the on-the-fly activation quantizers and the weight quantizer:
   FP4 E2M1 with an E8M0 scale per 32-element K block, FP8 E4M3 with fp32
-  per-row (activation) / per-column (weight) scales, and MXFP8 (E4M3 with an
-  E8M0 scale per 32-element K block).
+  per-row (activation) / per-column (weight) scales, MXFP8 (E4M3 with an
+  E8M0 scale per 32-element K block) and NVFP4 (E2M1 with an E4M3 scale per
+  16-element K block and an fp32 tensor scale).
 * ``gemm``     -- decode codes and scales, multiply in float64.
 * ``epilogue`` -- identity, gated-SiLU, per-head QK-RMSNorm, GELU (tanh form)
   and the gated residual update, in float64.

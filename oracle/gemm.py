@@ -25,6 +25,10 @@ blocks with different scales need not sum exactly in float64; the float64 sum is
 within K * 2**-53 * sum_k |a_k w_k| of the exact value (below 1e-12 relative to
 the sum of magnitudes for K <= 16384), many orders of magnitude under any fp32
 accumulation or bf16 storage error the layer makes.
+
+NVFP4: acc[m, n] = (sum_k e2m1(a) s_b(a) e2m1(w) s_b(w)) * s_t(A) * s_t(W), the
+block-scaled products summed in float64 (the same bound as MXFP8), then the two
+tensor scales.
 """
 from __future__ import annotations
 
@@ -93,4 +97,17 @@ def gemm_mx8(a_codes, a_scales, w_codes, w_scales, rows=None) -> np.ndarray:
         r = sel[i:i + ROW_CHUNK]
         Ad = quant.dequantize_mx8(np.asarray(a_codes)[r], np.asarray(a_scales)[r])
         out[i:i + ROW_CHUNK] = Ad @ Wd.T
+    return out
+
+
+def gemm_nv4(a_codes, a_scales, a_st, w_codes, w_scales, w_st, rows=None) -> np.ndarray:
+    """acc = (dequant(A) @ dequant(W)^T) in float64 with NVFP4 operands (tensor scales included)."""
+    Wd = quant.dequantize_nv4(w_codes, w_scales, 1.0)
+    sel = np.arange(np.asarray(a_codes).shape[0]) if rows is None else np.asarray(rows)
+    out = np.empty((sel.size, Wd.shape[0]), dtype=np.float64)
+    st = float(np.float32(a_st)) * float(np.float32(w_st))
+    for i in range(0, sel.size, ROW_CHUNK):
+        r = sel[i:i + ROW_CHUNK]
+        Ad = quant.dequantize_nv4(np.asarray(a_codes)[r], np.asarray(a_scales)[r], 1.0)
+        out[i:i + ROW_CHUNK] = (Ad @ Wd.T) * st
     return out

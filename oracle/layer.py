@@ -20,6 +20,8 @@ def quantize_operands(x_bits, w_bits, fmt: str):
         return quant.quantize_fp8(x_bits), quant.quantize_fp8(w_bits)
     if fmt == "mx8":
         return quant.quantize_mx8(x_bits), quant.quantize_mx8(w_bits)
+    if fmt == "nv4":
+        return quant.quantize_nv4(x_bits), quant.quantize_nv4(w_bits)
     raise ValueError(fmt)
 
 
@@ -28,6 +30,8 @@ def accumulate(a, w, fmt: str, rows=None) -> np.ndarray:
         return gemm.gemm_fp4(a[0], a[1], w[0], w[1], rows=rows)
     if fmt == "mx8":
         return gemm.gemm_mx8(a[0], a[1], w[0], w[1], rows=rows)
+    if fmt == "nv4":
+        return gemm.gemm_nv4(a[0], a[1], a[2], w[0], w[1], w[2], rows=rows)
     return gemm.gemm_fp8(a[0], a[1], w[0], w[1], rows=rows)
 
 

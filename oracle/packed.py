@@ -30,6 +30,10 @@ Layout (all offsets in bytes, little-endian):
 * MXFP8 codes: as FP8 codes (2048-byte fragments, one E4M3 byte per element).
 * MXFP8 scales: as FP4 scales (128-byte records (s, g), byte 2*L + j = E8M0 scale
   of packed row 32g + L%32 for the K block 4s + 2j + L//32).
+* NVFP4 codes: as FP4 codes.  NVFP4 scales: 256-byte records (s, g) at
+  scales_offset + (s * Np/32 + g) * 256; byte 4*L + 2*j + b is the E4M3 scale of
+  packed row 32g + L%32 for the 16-element K block 8s + 4j + 2(L//32) + b.  The
+  fp32 tensor scale sits in the header at byte 56.
 """
 from __future__ import annotations
 
@@ -37,7 +41,7 @@ import numpy as np
 
 MAGIC = 0x51544944
 HEADER = 256
-FMT_FP4, FMT_FP8, FMT_MX8 = 1, 2, 3
+FMT_FP4, FMT_FP8, FMT_MX8, FMT_NV4 = 1, 2, 3, 4
 EPI_IDENTITY, EPI_GATED_SILU, EPI_QK_RMSNORM = 0, 1, 2
 
 
@@ -71,12 +75,14 @@ def decode(blob: np.ndarray, fmt: int, epi: int, N: int, K: int):
     FP4: codes uint8 [N, K/2] (low nibble = even k), scales uint8 [N, K/32].
     FP8: codes uint8 [N, K], scales float32 [N].
     MXFP8: codes uint8 [N, K], scales uint8 [N, K/32].
+    NVFP4: codes uint8 [N, K/2], scales uint8 [N, K/16] (the tensor scale is
+    ``tensor_scale(blob)``).
     """
     b = np.asarray(blob, dtype=np.uint8)
     Np = padded_rows(N)
     G = Np // 32
     perm = row_perm(epi, N, Np)
-    if fmt == FMT_FP4:
+    if fmt in (FMT_FP4, FMT_NV4):
         cbytes = Np * K // 2
         frag = b[HEADER:HEADER + cbytes].reshape(G, K // 64, 64, 16)        # [g][c][L][b]
         rows = np.empty((Np, K // 2), dtype=np.uint8)
@@ -99,6 +105,16 @@ def decode(blob: np.ndarray, fmt: int, epi: int, N: int, K: int):
         raise ValueError("unknown format")
     if fmt == FMT_FP8:
         sc = b[HEADER + cbytes:HEADER + cbytes + 4 * Np].copy().view(np.float32)
+    elif fmt == FMT_NV4:
+        sbytes = Np * K // 16
+        sg = b[HEADER + cbytes:HEADER + cbytes + sbytes].reshape(K // 128, G, 64, 2, 2)   # [s][g][L][j][b]
+        sc = np.empty((Np, K // 16), dtype=np.uint8)
+        for L in range(64):
+            r = np.arange(G) * 32 + L % 32
+            for s in range(K // 128):
+                for j in range(2):
+                    for bb in range(2):
+                        sc[r, 8 * s + 4 * j + 2 * (L // 32) + bb] = sg[s, :, L, j, bb]
     else:
         sbytes = Np * K // 32
         sg = b[HEADER + cbytes:HEADER + cbytes + sbytes].reshape(K // 128, G, 64, 2)   # [s][g][L][j]
@@ -115,3 +131,8 @@ def decode(blob: np.ndarray, fmt: int, epi: int, N: int, K: int):
     scales[perm[valid]] = sc[valid]
     padding = {"codes": rows[~valid], "scales": sc[~valid]}
     return codes, scales, padding
+
+
+def tensor_scale(blob: np.ndarray) -> np.float32:
+    """The NVFP4 blob's fp32 tensor scale (header byte 56)."""
+    return np.asarray(blob, dtype=np.uint8)[56:60].copy().view(np.float32)[0]

@@ -37,6 +37,17 @@ MXFP8 path (FP8 as the safer precision, pages above; the block structure of the
     v     = x * 2**-(byte - 127)                             (exact)
     code  = RNE_E4M3(v), saturating at 448, sign kept.
 
+NVFP4 path (the format page "How fal made Ideogram V4 6x faster" names in
+paragraph 2: a 4-bit float with two levels of scaling, E4M3 scales per 16
+elements and one fp32 scale per tensor), every step an IEEE fp32 operation:
+
+  s_t   = fl32(amax_tensor / 2688)  (2688 = 6 * 448; s_t = 1 when the tensor is zero)
+  per row and per block of 16 consecutive K elements:
+    d   = fl32(amax_block / fl32(6 * s_t))
+    s_b = RNE_E4M3(min(d, 448))                                 (the stored scale code)
+    q   = sign(x) | RNE_E2M1(min(|fl32(x / fl32(dec(s_b) * s_t))|, 6)),  magnitude 0 when s_b = 0
+  value = E2M1(q) * dec(s_b) * s_t.
+
 Every rounding function below exists twice (a closed-form threshold rule and a
 brute-force nearest-point search); the tests require them to agree on every
 input class.
@@ -255,3 +266,50 @@ def dequantize_mx8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     R, K = c.shape
     vals = formats.e4m3_decode(c).reshape(R, K // MX_BLOCK, MX_BLOCK)
     return (vals * formats.e8m0_decode(scales)[..., None]).reshape(R, K)
+
+
+# ---------------------------------------------------------------- NVFP4 quantizer
+NV_BLOCK = 16
+NV_TENSOR_DIV = 2688.0        # 6 * 448: the tensor maximum maps to the largest code times the largest scale
+
+
+def nv4_tensor_scale(amax_f32) -> np.float32:
+    """s_t = fl32(amax / 2688), 1 for an all-zero tensor."""
+    a = np.float32(amax_f32)
+    return np.float32(1.0) if a == 0 else np.float32(a / np.float32(NV_TENSOR_DIV))
+
+
+def quantize_nv4(x_bits: np.ndarray, rounding=e2m1_rne_threshold, scale_rounding=e4m3_rne_fields):
+    """Quantize a bf16 tensor [R, K] to NVFP4.
+
+    Returns ``codes`` uint8 [R, K/2] (two E2M1 codes per byte, even k in the low
+    nibble), ``scales`` uint8 [R, K/16] (E4M3 block scale codes) and ``s_t``
+    (float32 tensor scale).  K must be a multiple of 16.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    R, K = x_bits.shape
+    if K % NV_BLOCK:
+        raise ValueError("K must be a multiple of 16")
+    x = (x_bits.astype(np.uint32) << 16).view(np.float32)
+    _check_finite(x)
+    s_t = nv4_tensor_scale(np.abs(x).max() if x.size else 0.0)
+    six_st = np.float32(np.float32(6.0) * s_t)
+    xb = x.reshape(R, K // NV_BLOCK, NV_BLOCK)
+    d = (np.abs(xb).max(axis=-1) / six_st).astype(np.float32)
+    scales = scale_rounding(np.minimum(d, np.float32(E4M3_MAX)))
+    denom = (formats.e4m3_decode(scales).astype(np.float32) * s_t).astype(np.float32)      # fl32(dec(s_b) * s_t)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = (xb / denom[..., None]).astype(np.float32)
+    y = np.where(denom[..., None] == 0, np.float32(0.0), y)
+    mag = rounding(np.minimum(np.abs(y.astype(np.float64)), 6.0)).reshape(R, K)
+    sign = ((x_bits >> 15) & 1).astype(np.uint8)
+    code = mag | (sign << 3)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scales, s_t
+
+
+def dequantize_nv4(packed: np.ndarray, scales: np.ndarray, s_t) -> np.ndarray:
+    codes = unpack_fp4_codes(packed)
+    R, K = codes.shape
+    vals = formats.e2m1_decode(codes).reshape(R, K // NV_BLOCK, NV_BLOCK)
+    return (vals * formats.e4m3_decode(scales)[..., None]).reshape(R, K) * float(np.float32(s_t))

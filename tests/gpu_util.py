@@ -62,3 +62,11 @@ def compare_bf16(gpu_bits: np.ndarray, y: np.ndarray, label: str = "") -> dict:
         raise AssertionError(f"{label}: {rep['bad']} of {rep['n']} elements out of tolerance; first at "
                              f"[{i},{j}] gpu={g[i, j]!r} oracle={y[i, j]!r} rowrms={rms[i]!r}; {rep}")
     return rep
+
+
+def nv4_act_scales(scales: np.ndarray, M: int, K: int):
+    """NVFP4 activation scales buffer -> (E4M3 block scale codes [M, K/16], fp32 tensor scale)."""
+    s = np.asarray(scales, dtype=np.uint8).reshape(-1)
+    blocks = s[:M * K // 16].reshape(K // 128, M, 8).transpose(1, 0, 2).reshape(M, K // 16)
+    st = s[M * K // 16 + 4:M * K // 16 + 8].copy().view(np.float32)[0]
+    return blocks, st

@@ -48,8 +48,11 @@ def test_size_queries():
     assert ditq.dit_packed_weight_bytes(3, 1, 16384, 3072) == 256 + 16384 * 3072 + 16384 * 96
     assert ditq.dit_act_code_bytes(3, 4608, 3072) == 4608 * 3072
     assert ditq.dit_act_scale_bytes(3, 4608, 3072) == 4608 * 96
-    assert ditq.dit_packed_weight_bytes(4, 0, 64, 256) == 0          # no such format
-    assert ditq.dit_act_code_bytes(4, 64, 256) == 0
+    assert ditq.dit_packed_weight_bytes(4, 0, 64, 256) == 256 + 256 * 128 + 256 * 16   # NVFP4
+    assert ditq.dit_act_code_bytes(4, 64, 256) == 64 * 128
+    assert ditq.dit_act_scale_bytes(4, 64, 256) == 64 * 16 + 16          # + the tensor-scale tail
+    assert ditq.dit_packed_weight_bytes(5, 0, 64, 256) == 0          # no such format
+    assert ditq.dit_act_code_bytes(5, 64, 256) == 0
     assert ditq.dit_act_code_bytes(1, 0, 256) == 0
 
 
@@ -114,7 +117,8 @@ def test_gemm_q4_quantized_output_validation():
 def test_other_entry_points_validation():
     lib = ditq._lib
     assert lib.dit_quantize_act(1, None, 4, 256, 256, B, C, None) == EINVAL
-    assert lib.dit_quantize_act(4, A, 4, 256, 256, B, C, None) == EINVAL
+    assert lib.dit_quantize_act(5, A, 4, 256, 256, B, C, None) == EINVAL
+    assert lib.dit_quantize_act(4, A, 4, 256, 256, B, C + 4, None) == EALIGN       # NVFP4 scales: 16 B
     assert lib.dit_quantize_act(3, A, 4, 256, 256, None, C, None) == EINVAL
     assert lib.dit_quantize_act(3, A, 4, 256, 256, B + 8, C, None) == EALIGN       # MXFP8 codes need 16 B
     assert lib.dit_quantize_act(1, A, 4, 300, 304, B, C, None) == EUNSUP
@@ -134,6 +138,8 @@ def test_other_entry_points_validation():
         assert lib.dit_pack_weights(2, 1, A, 128, 256, 256, B, None) == EDEVICE
         assert lib.dit_pack_weights(2, 2, A, 384, 256, 256, B, None) == EDEVICE      # FP8 for QK-RMSNorm
         assert lib.dit_pack_weights(3, 1, A, 128, 256, 256, B, None) == EDEVICE
+        assert lib.dit_pack_weights(4, 1, A, 128, 256, 256, B, None) == EDEVICE
+        assert lib.dit_quantize_act(4, A, 4, 256, 256, B, C, None) == EDEVICE
         assert lib.dit_gemm_q8_epilogue(A, B, C, 4, 512, 256, 1, D, 256, None) == EDEVICE
 
 
@@ -149,7 +155,7 @@ def _any(fmt=3, a=A, s=B, w=C, M=64, N=512, K=256, epi=1, rms=None, out=D, ldo=2
 
 def test_gemm_any_format_validation():
     assert _any(fmt=0) == EINVAL
-    assert _any(fmt=4) == EINVAL
+    assert _any(fmt=5) == EINVAL
     assert _any(out=None) == EINVAL
     assert _any(a=None) == EINVAL
     assert _any(epi=2) == EINVAL                                     # RMSNorm without params
@@ -164,7 +170,7 @@ def test_gemm_any_format_validation():
     assert _any(fmt=2, s=B + 2) == EALIGN
     assert _any(ldo=255) == EALIGN
     if not _has_gpu():
-        for fmt in (1, 2, 3):
+        for fmt in (1, 2, 3, 4):
             assert _any(fmt=fmt) == EDEVICE
             assert _any(fmt=fmt, epi=0, ldo=512) == EDEVICE
             assert _any(fmt=fmt, epi=2, rms=r, N=384, ldo=384) == EDEVICE
@@ -186,7 +192,7 @@ def test_gate_residual_validation():
     assert _gr(gr=P(E, 512, None, 32)) == EINVAL
     assert _gr(gr=P(E, 512, F, 0)) == EINVAL
     assert _gr(gr=P(D + 1024, 512, F, 32)) == EINVAL                 # partial overlap with the output
-    assert _gr(fmt=4) == EINVAL
+    assert _gr(fmt=5) == EINVAL
     assert _gr(K=128) == EUNSUP
     assert _gr(gr=P(E + 8, 512, F, 32)) == EALIGN
     assert _gr(gr=P(E, 500, F, 32)) == EALIGN                         # ldr < N
@@ -199,7 +205,7 @@ def test_gate_residual_validation():
     assert ditq.dit_packed_weight_bytes(1, 4, 512, 256) == ditq.dit_packed_weight_bytes(1, 0, 512, 256)
     assert ditq.dit_packed_weight_bytes(3, 3, 512, 256) == ditq.dit_packed_weight_bytes(3, 0, 512, 256)
     if not _has_gpu():
-        for fmt in (1, 2, 3):
+        for fmt in (1, 2, 3, 4):
             assert _gr(fmt=fmt) == EDEVICE
             assert _gr(fmt=fmt, gr=P(D, 512, F, 7), out=D) == EDEVICE     # in place
             assert _any(fmt=fmt, epi=3, ldo=512) == EDEVICE               # GELU-tanh

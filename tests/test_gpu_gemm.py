@@ -14,7 +14,7 @@ from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-FMT = {"fp4": 1, "fp8": 2, "mx8": 3}
+FMT = {"fp4": 1, "fp8": 2, "mx8": 3, "nv4": 4}
 EPI = {"identity": 0, "gated_silu": 1, "qk_rmsnorm": 2, "gelu_tanh": 3, "gate_residual": 4}
 
 
@@ -148,6 +148,12 @@ SMALL = [
     ("mlp_gelu_tanh", "fp4", "gelu_tanh", 1, 256, 256, None),
     ("mlp_gelu_tanh", "fp8", "gelu_tanh", 129, 512, 768, None),
     ("mlp_gelu_tanh", "mx8", "gelu_tanh", 70, 1024, 256, None),
+    ("mlp_gated_silu", "nv4", "gated_silu", 300, 1024, 512, None),
+    ("mlp_gated_silu", "nv4", "identity", 1, 320, 256, None),
+    ("mlp_gated_silu", "nv4", "identity", 129, 768, 768, None),
+    ("qkv_rmsnorm_hd128", "nv4", "qk_rmsnorm", 257, None, 512, 2),
+    ("qkv_rmsnorm_hd256", "nv4", "qk_rmsnorm", 65, None, 512, 1),
+    ("mlp_gelu_tanh", "nv4", "gelu_tanh", 70, 512, 256, None),
 ]
 
 
@@ -185,7 +191,7 @@ FULL = [("qkv_rmsnorm_hd128", "qk_rmsnorm", None), ("mlp_gated_silu", "gated_sil
         ("fp8_cfg_pair", "gated_silu", None), ("qkv_rmsnorm_hd128", "qk_rmsnorm", "fp8"),
         ("qkv_rmsnorm_hd256", "qk_rmsnorm", "fp8"), ("mlp_gated_silu", "gated_silu", "mx8"),
         ("qkv_rmsnorm_hd128", "qk_rmsnorm", "mx8"), ("fp8_cfg_pair", "identity", "mx8"),
-        ("mlp_gelu_tanh", "gelu_tanh", None)]
+        ("mlp_gelu_tanh", "gelu_tanh", None), ("mlp_gated_silu", "gated_silu", "nv4")]
 
 
 @pytest.mark.parametrize("name,epi,fmt", FULL, ids=[f"{a}-{b}-{c or WORKLOADS[a].fmt}" for a, b, c in FULL])
@@ -224,6 +230,7 @@ GR = [  # fmt, M, N, K, rows_per_gate, in_place
     ("fp8", 64, 256, 256, 7, True),
     ("mx8", 200, 768, 512, 64, False),
     ("mx8", 70, 256, 1024, 1000, True),
+    ("nv4", 130, 512, 512, 50, False),
 ]
 
 

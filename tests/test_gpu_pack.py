@@ -95,3 +95,20 @@ def test_fp8_pack_for_rmsnorm_is_the_identity_blob(ditq):
     b = _pack(ditq, d["w"], 2, 2)
     assert packed.read_header(b)["epi"] == 2
     np.testing.assert_array_equal(a[256:], b[256:])
+
+
+@pytest.mark.parametrize("N,K,epi", [(320, 256, 0), (256, 512, 1), (384, 768, 2), (16384, 3072, 1)])
+def test_nv4_pack_bitexact(ditq, N, K, epi):
+    d = make_inputs("mlp_gated_silu", seed=N + 2, M=1, N=N, K=K)
+    d["w"][3, :] = 0                                                   # an all-zero row
+    d["w"][5, 16:32] = 0x0001                                          # a block far below the tensor maximum
+    blob = _pack(ditq, d["w"], 4, epi)
+    hdr = packed.read_header(blob)
+    assert (hdr["magic"], hdr["fmt"], hdr["epi"], hdr["N"], hdr["K"]) == (packed.MAGIC, 4, epi, N, K)
+    assert hdr["total"] == blob.size
+    c, s, pad = packed.decode(blob, 4, epi, N, K)
+    rc, rs, rst = quant.quantize_nv4(d["w"])
+    assert packed.tensor_scale(blob).view(np.uint32) == np.float32(rst).view(np.uint32)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
+    assert not pad["codes"].any() and not pad["scales"].any()

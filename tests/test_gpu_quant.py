@@ -191,3 +191,57 @@ def test_mx8_quantizer_full_size_workload(ditq):
     rc, rs = quant.quantize_mx8(d["x"])
     np.testing.assert_array_equal(s, rs)
     np.testing.assert_array_equal(c, rc)
+
+
+def _run_nv4(ditq, bits, ldx=None):
+    import torch
+    from tests.gpu_util import act_codes_to_rowmajor, nv4_act_scales, to_dev_bf16
+    M, K = bits.shape
+    ldx = ldx or K
+    buf = np.zeros((M, ldx), dtype=np.uint16)
+    buf[:, :K] = bits
+    x = to_dev_bf16(buf)
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.full((ditq.dit_act_scale_bytes(ditq.FMT_NV4, M, K),), 0xAB, dtype=torch.uint8, device="cuda")
+    ditq.dit_quantize_act(ditq.FMT_NV4, x.data_ptr(), M, K, ldx, codes.data_ptr(), scales.data_ptr(),
+                          torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    blocks, st = nv4_act_scales(scales.cpu().numpy(), M, K)
+    return act_codes_to_rowmajor(codes.cpu().numpy(), M, K, 1), blocks, st
+
+
+@pytest.mark.parametrize("M,K,ldx", [(1, 256, 256), (63, 3072, 3072), (300, 512, 520), (7, 4096, 4104)])
+def test_nv4_quantizer_bitexact(ditq, M, K, ldx):
+    rng = np.random.default_rng(M * 13 + K)
+    bits = _special_rows(rng, M, K)
+    c, s, st = _run_nv4(ditq, bits, ldx)
+    rc, rs, rst = quant.quantize_nv4(bits)
+    assert np.float32(st).view(np.uint32) == np.float32(rst).view(np.uint32)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
+
+
+def test_nv4_quantizer_every_bf16_value(ditq):
+    """Every finite bf16 value (hence every block-scale and element rounding case the
+    tensor's scale allows), twice: once in a tensor whose maximum is bf16's largest
+    value, once in small-magnitude blocks under a tensor maximum of 1."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = allb[np.isfinite(formats.bf16_to_f64(allb))]
+    rng = np.random.default_rng(2)
+    v = rng.permutation(fin)
+    v = np.concatenate([v, np.zeros((-len(v)) % 3072, np.uint16)])
+    for bits in (v.reshape(-1, 3072), np.where((v & 0x7FFF) <= 0x3F80, v, v & 0x803F).reshape(-1, 3072)):
+        c, s, st = _run_nv4(ditq, bits)
+        rc, rs, rst = quant.quantize_nv4(bits)
+        assert np.float32(st).view(np.uint32) == np.float32(rst).view(np.uint32)
+        np.testing.assert_array_equal(s, rs)
+        np.testing.assert_array_equal(c, rc)
+
+
+def test_nv4_quantizer_full_size_workload(ditq):
+    d = make_inputs("mlp_gated_silu", seed=0)
+    c, s, st = _run_nv4(ditq, d["x"])
+    rc, rs, rst = quant.quantize_nv4(d["x"])
+    assert np.float32(st) == rst
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)

@@ -15,6 +15,8 @@ def _write_blob(codes, scales, fmt, epi, N, K):
         cbytes, sbytes = Np * K // 2, Np * K // 32
     elif fmt == packed.FMT_MX8:
         cbytes, sbytes = Np * K, Np * K // 32
+    elif fmt == packed.FMT_NV4:
+        cbytes, sbytes = Np * K // 2, Np * K // 16
     else:
         cbytes, sbytes = Np * K, Np * 4
     blob = np.zeros(packed.HEADER + cbytes + sbytes, dtype=np.uint8)
@@ -27,12 +29,19 @@ def _write_blob(codes, scales, fmt, epi, N, K):
         if n < 0:
             continue
         g, lane_lo = p // 32, p % 32
-        if fmt == packed.FMT_FP4:
+        if fmt in (packed.FMT_FP4, packed.FMT_NV4):
             for k in range(0, K, 2):
                 c, within = k // 64, k % 64
                 L = lane_lo + 32 * (within // 32)
                 b = (within % 32) // 2
                 blob[256 + (g * (K // 64) + c) * 1024 + 16 * L + b] = codes[n, k // 2]
+            if fmt == packed.FMT_NV4:
+                for blk in range(K // 16):
+                    s, r = blk // 8, blk % 8                 # r = 4j + 2 * half + b
+                    j, half, bb = r // 4, (r // 2) % 2, r % 2
+                    L = lane_lo + 32 * half
+                    blob[256 + cbytes + (s * (Np // 32) + g) * 256 + 4 * L + 2 * j + bb] = scales[n, blk]
+                continue
             for blk in range(K // 32):
                 s, r = blk // 4, blk % 4
                 j, half = r // 2, r % 2
@@ -56,7 +65,7 @@ def _write_blob(codes, scales, fmt, epi, N, K):
 
 @pytest.mark.parametrize("fmt,epi,N,K", [(1, 0, 64, 256), (1, 1, 128, 512), (1, 2, 300 - 300 % 32 + 32, 256),
                                          (2, 0, 96, 256), (2, 1, 128, 256), (3, 0, 96, 256), (3, 1, 128, 512),
-                                         (3, 2, 64, 384)])
+                                         (3, 2, 64, 384), (4, 0, 64, 256), (4, 1, 128, 512)])
 def test_writer_and_decoder_invert(fmt, epi, N, K):
     rng = np.random.default_rng(N + K + fmt)
     if fmt == 1:
@@ -65,6 +74,9 @@ def test_writer_and_decoder_invert(fmt, epi, N, K):
     elif fmt == 3:
         codes = rng.integers(0, 256, (N, K), dtype=np.uint8)
         scales = rng.integers(100, 150, (N, K // 32), dtype=np.uint8)
+    elif fmt == 4:
+        codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        scales = rng.integers(0, 0x7F, (N, K // 16), dtype=np.uint8)
     else:
         codes = rng.integers(0, 256, (N, K), dtype=np.uint8)
         scales = rng.uniform(0.01, 1, N).astype(np.float32)
