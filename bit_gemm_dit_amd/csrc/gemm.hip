@@ -67,11 +67,14 @@ constexpr int kGroupM = 4;       // tile-order group height (in M tiles)
 // two waves of a row band, one copy per workgroup); the other TN - WLDS groups are
 // loaded straight into registers.  RING: length of that register ring in units (a
 // unit = one 64-K MFMA step); unit u is loaded RING-1 units before it is used.
-// HD: head_dim of the QK-RMSNorm epilogue (0 otherwise).
-template <int FMT_, int EPI_, int TM_, int RING_, int WLDS_, int HD_ = 0>
+// HD: head_dim of the QK-RMSNorm epilogue (0 otherwise).  WL: waves along N: 2 (a
+// 2 x 2 grid, each wave 128 features x BM/2 tokens) or 4 (a 4 x 1 grid, each wave 64
+// features x all BM tokens: no weight row is needed by two waves, so all weights go
+// straight to registers and only the activation tile is shared).
+template <int FMT_, int EPI_, int TM_, int RING_, int WLDS_, int HD_ = 0, int WL_ = 2>
 struct Tile {
   static constexpr int FMT = FMT_, EPI = EPI_, TM = TM_, RING = RING_, WLDS = WLDS_, HD = HD_;
-  static constexpr int TN = 4, WAVES_N = 2, WAVES_M = 2, NW = 4, NT = 256;
+  static constexpr int WAVES_N = WL_, WAVES_M = 4 / WL_, TN = 8 / WL_, NW = 4, NT = 256;
   static constexpr int WN = 32 * TN, WM = 32 * TM;
   static constexpr int BN = WN * WAVES_N, BM = WM * WAVES_M;
   static constexpr bool MX = FMT != FMT_FP8;                   // E8M0 block scales applied by the MFMA
@@ -140,6 +143,8 @@ struct Tile {
   static_assert(WAIT_UNIT < 64 && WAIT_STAGE < 64, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024 && STAGES >= 3, "LDS");
   static_assert(TN * TM * 16 <= 256, "accumulators fit in the AGPRs");
+  static_assert((WAVES_N == 2 || (WAVES_N == 4 && WLDS == 0)) && (EPI != EPI_GATED_SILU || TN % 2 == 0),
+                "a 4 x 1 grid shares no weights; a wave holds whole gate/up pairs");
 };
 
 struct Params {
@@ -994,23 +999,41 @@ hipError_t launch(Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Token-tile height 192 or 256 (TM = 3 or 4 per wave), whichever gives the fewest
+// Token-tile height 192 or 256 (TM = 3 or 4 per wave on the 2 x 2 grid, 6 or 8 on the
+// 4 x 1 grid), whichever gives the fewest
 // rounds of tiles over the CUs, weighted by the tile's work plus a fixed cost of
 // about half a token tile (FP8 and MXFP8 always 192: with 256 their operand
 // registers spill); FP4 weight ring of 8 units when the k-steps come in groups of
 // 4, else 4 (FP8 and MXFP8: 4).
 template <int FMT, int EPI, int HD = 0, int WLDS = wlds_for(FMT)>
 hipError_t launch_cfg(Params& p, hipStream_t stream) {
-  if constexpr (FMT == FMT_NV4) {
-    return launch<Tile<FMT, EPI, 3, 4, 2, HD>>(p, stream);
-  } else if constexpr (FMT != FMT_FP4) {
-    return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
+  // 4 x 1 wave grid: 64 features x BM tokens per wave, every weight through registers.
+  // Measured faster than the 2 x 2 grid for FP4 (headline 122 vs 129 us) and FP8
+  // (CFG-pair identity 316 vs 325 us): no weight row is loaded by two waves, so the
+  // vector memory path carries less per k-step and CU.  MXFP8 and NVFP4 measured no
+  // faster and keep the 2 x 2 grid.  A head of QK-RMSNorm needs 128 or 256 features
+  // in one or two waves, and the gated residual's epilogue spills in the 256-token
+  // variant, so those keep the 2 x 2 grid too.
+  constexpr bool grid41 = (FMT == FMT_FP4 || FMT == FMT_FP8) && EPI != EPI_QK_RMSNORM &&
+                          EPI != EPI_GATE_RESIDUAL;
+  if constexpr (FMT != FMT_FP4) {
+    if constexpr (grid41) return launch<Tile<FMT, EPI, 6, 4, 0, HD, 4>>(p, stream);
+    else if constexpr (FMT == FMT_NV4) return launch<Tile<FMT, EPI, 3, 4, 2, HD>>(p, stream);
+    else return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
   } else {
     const int nks = p.K / 128;
     const int cus = cu_count();
     const long tn = padded_rows(p.N) / 256;
     const long r3 = ((p.M + 191) / 192 * tn + cus - 1) / cus, r4 = ((p.M + 255) / 256 * tn + cus - 1) / cus;
     const bool tm3 = r3 * 7 < r4 * 9;
+    if constexpr (grid41) {
+      if (nks % 4 != 0) {
+        if (tm3) return launch<Tile<FMT, EPI, 6, 4, 0, HD, 4>>(p, stream);
+        return launch<Tile<FMT, EPI, 8, 4, 0, HD, 4>>(p, stream);
+      }
+      if (tm3) return launch<Tile<FMT, EPI, 6, 8, 0, HD, 4>>(p, stream);
+      return launch<Tile<FMT, EPI, 8, 8, 0, HD, 4>>(p, stream);
+    }
     if (nks % 4 != 0) {
       if (tm3) return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
       return launch<Tile<FMT, EPI, 4, 4, WLDS, HD>>(p, stream);
