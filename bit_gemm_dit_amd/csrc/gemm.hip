@@ -267,6 +267,33 @@ __device__ inline float gelu_tanh(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// The same for the 16 values of a result tile, in stages (all exponentials, then all
+// reciprocals, then the products) held apart by scheduling barriers: the 16 chains
+// are independent, and issued one after another each would wait on its own
+// transcendental results.  Same operations and rounding as silu / gelu_tanh.
+__device__ __forceinline__ void silu_mul16(const float* g, const float* u, float* v) {
+  float e[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(-g[r] * 1.4426950408889634f);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_rcpf(1.0f + e[r]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = g[r] * e[r] * u[r];
+}
+__device__ __forceinline__ void gelu_tanh16(float* v) {
+  float e[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(-2.3022081981443250f * (v[r] * (1.0f + 0.044715f * v[r] * v[r])));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_rcpf(1.0f + e[r]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = v[r] * e[r];
+}
+
 // ---------------------------------------------------------------- operands
 // Activation fragments of one unit (TM token tiles): lane L holds token row
 // wm*WM + 32*tm + L%32 (FP4: the 16 bytes of K chunk 32*(L/32), logical chunk
@@ -507,8 +534,7 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
             }
           }
           if constexpr (T::EPI == EPI_GELU_TANH) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) v[r] = gelu_tanh(v[r]);
+            gelu_tanh16(v);
           }
           if constexpr (T::EPI == EPI_GATE_RESIDUAL) {
             // this lane's 16 columns are 4 runs of 4 (n0 + 8g + 4h + i): the residual
@@ -553,8 +579,7 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
               }
             }
           }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) v[r] = silu(gate[r]) * up[r];
+          silu_mul16(gate, up, v);
           store_tile<T>(p, row, ok, n0w / 2 + 32 * q, p.N / 2, h, v);
         }
       }
