@@ -950,10 +950,13 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
       wait_vmcnt<T::WAIT_BARRIER, true>();         // stage g+1 and unit u1 have landed; reads of `cur` done
       barrier();
       __builtin_amdgcn_sched_barrier(0);
-      copy_stage(cur);
-      load_unit<T>(ring[l1], w_rsrc, wbase, wc_u, (int)wgroup);
+      // The reads of the next stage come first in program order: the copies write
+      // LDS, which the compiler cannot tell apart from the slot being read, so copies
+      // placed before the reads would be held in front of every MFMA of the half.
       load_scales<T>(sn, lds + nxt, wn, wm, lane);
       load_act<T, 0>(fa, lds + nxt, wn, wm, lane);
+      copy_stage(cur);
+      load_unit<T>(ring[l1], w_rsrc, wbase, wc_u, (int)wgroup);
       mfma_part<T, 1, 0, T::TM, false>(acc, ring[u1], fb, sc);
       spread_vmem<T::TN * T::TM * T::MFMA_PER_UNIT, T::NCOPY + T::UNIT_LOADS>();
       pin_accumulators<T>(acc);
@@ -972,9 +975,9 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
       wait_vmcnt<T::WAIT_BARRIER, true>();         // stage g+1 has landed; reads of `cur` done
       barrier();
       __builtin_amdgcn_sched_barrier(0);
+      load_act<T, 0>(fb, lds + nxt, wn, wm, lane);   // reads before the copies (see above)
       copy_stage(cur);
       load_unit<T>(ring[l], w_rsrc, wbase, wc_u, (int)wgroup);
-      load_act<T, 0>(fb, lds + nxt, wn, wm, lane);
       mfma_part<T, 0, T::TM / 2, T::TM, ZERO>(acc, ring[u], fa, sc);
       spread_vmem<T::TN * (T::TM - T::TM / 2), T::NCOPY + T::UNIT_LOADS>();
       pin_accumulators<T>(acc);
