@@ -481,13 +481,17 @@ __device__ __forceinline__ void spread_vmem() {
   if constexpr (NV == 0) {
     __builtin_amdgcn_sched_group_barrier(kMfma, NM, 0);
   } else {
-    constexpr int per = NM / (NV + 1) > 0 ? NM / (NV + 1) : 1;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kMfma, per, 0);
+    // memory operation i follows MFMA number floor((i + 1) * NM / (NV + 1)): evenly
+    // spaced over the whole half-step (the four waves issue in step, so bunching the
+    // operations would ask the CU's vector memory path for several KB at once)
+    static_for<0, NV>([&](auto i_c) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_c)::value;
+      constexpr int before = (i + 1) * NM / (NV + 1) - i * NM / (NV + 1);
+      if constexpr (before > 0) __builtin_amdgcn_sched_group_barrier(kMfma, before, 0);
       __builtin_amdgcn_sched_group_barrier(kVmem, 1, 0);
-    }
-    if constexpr (NM > per * NV) __builtin_amdgcn_sched_group_barrier(kMfma, NM - per * NV, 0);
+    });
+    constexpr int rest = NM - NV * NM / (NV + 1);
+    if constexpr (rest > 0) __builtin_amdgcn_sched_group_barrier(kMfma, rest, 0);
   }
 }
 
