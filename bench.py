@@ -18,6 +18,10 @@ Prints one JSON line:
                  changed since)
   cpu_baseline = the CPU oracle (float64) on a bounded row sample of the same
                  workload, timed on this host's cores
+  library_reference = the vendor library's MXFP4 GEMM (hipBLASLt, through
+                 torch._scaled_mm) on the same M, N, K with random E2M1 codes and
+                 E8M0 scales: a plain GEMM to a bf16 [M, N] output, no epilogue and
+                 no quantizer (informational; null where the library path is absent)
 """
 from __future__ import annotations
 
@@ -151,6 +155,8 @@ def run_gpu(args):
     }
     if not args.no_fusion_compare:
         res["kernels"].update(time_quantized_output(ditq, torch, wl, sets, epi, args))
+    if not args.no_library_compare:
+        res["library_reference"] = time_library_reference(torch, wl, args)
     if args.all_configs:
         res["other_configs"] = time_other_configs(ditq, torch, args)
     return res, d
@@ -194,6 +200,37 @@ def time_quantized_output(ditq, torch, wl, sets, epi, args):
         "gemm_then_quantize_us": round(times["unfused"], 2),
         "q4out_fusion_saving_us": round(times["unfused"] - times["fused"], 2),
     }
+
+
+def time_library_reference(torch, wl, args):
+    """hipBLASLt's MXFP4 GEMM at the workload's shape, timed like the GEMM above
+    (warm-up, then HIP events around each launch).  Inputs are random codes and
+    scales: only the time is used."""
+    M, N, K = wl.M, wl.N, wl.K
+    try:
+        g = torch.Generator(device="cpu").manual_seed(0)
+        a = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, generator=g).cuda().view(torch.float4_e2m1fn_x2)
+        b = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, generator=g).cuda().view(torch.float4_e2m1fn_x2)
+        sa = torch.randint(124, 131, (M, K // 32), dtype=torch.uint8, generator=g).cuda().view(torch.float8_e8m0fnu)
+        sb = torch.randint(124, 131, (N, K // 32), dtype=torch.uint8, generator=g).cuda().view(torch.float8_e8m0fnu)
+
+        def run():
+            return torch._scaled_mm(a, b.t(), sa, sb, out_dtype=torch.bfloat16)
+
+        n = max(20, args.steps // 4)
+        for _ in range(n // 2):
+            run()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record()
+            run()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        us = sum(x.elapsed_time(y) for x, y in ev) / n * 1e3
+    except Exception as e:  # library path missing on this build: report, do not fail the benchmark
+        return {"error": f"{type(e).__name__}: {str(e)[:160]}"}
+    return {"kind": "hipBLASLt MXFP4 GEMM via torch._scaled_mm, bf16 [M, N] output, no epilogue",
+            "gemm_us": round(us, 2), "tflops": round(2 * M * N * K / (us * 1e-6) / 1e12, 1)}
 
 
 def time_other_configs(ditq, torch, args):
@@ -324,6 +361,8 @@ def main():
     ap.add_argument("--all-configs", action="store_true", help="also time the other workloads' kernels")
     ap.add_argument("--no-fusion-compare", action="store_true",
                     help="skip the fused vs unfused quantized-output timing (keeps a kernel trace to the timed steps)")
+    ap.add_argument("--no-library-compare", action="store_true",
+                    help="skip timing the vendor library's MXFP4 GEMM at the same shape")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of this many MiB first (the reference dispatch that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
