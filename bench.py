@@ -276,11 +276,13 @@ def time_other_configs(ditq, torch, args):
             def run_gemm(out=None):
                 return ditq.gemm(codes, scales, blob, wl.N, wl.K, fmt, epi, rms=rms, out=out)
         o = run_gemm()
-        # flush the Infinity Cache between launches by touching a 512 MB buffer
-        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        # evict the Infinity Cache between launches by reading a 512 MB buffer (a read
+        # leaves clean lines behind; writing it would leave dirty ones whose write-back
+        # then competes with the timed kernels for HBM)
+        flush = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
         times_g, times_q = [], []
         for _ in range(max(3, args.steps // 2)):
-            flush.zero_()
+            flush.sum()
             e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             e[0].record()
             ditq.dit_quantize_act(fmt, x.data_ptr(), wl.M, wl.K, wl.K, codes.data_ptr(), scales.data_ptr(),

@@ -30,17 +30,22 @@
 //   multiply the accumulator in the epilogue.  Same loads, stages and lane layouts as
 //   FP4, at the f16 MFMA rate.
 // * A workgroup of 4 waves (one per SIMD) computes a 256 (features) x BM (tokens)
-//   tile; wave (wn, wm) owns 128 features x BM/2 tokens (4 x TM result tiles of
-//   32 x 32, TM = 3 or 4, up to 256 accumulators).
-// * Of each wave's 4 weight row groups, 2 come through LDS (one copy per workgroup,
-//   read by the two waves of a row band) and 2 are loaded straight into a ring of
-//   registers several 64-K steps ahead: the blob holds every fragment in the lane
-//   order of the MFMA operand, so no reshuffle is needed either way.  The
-//   activation tile, which the waves share, also goes through LDS, in a ring of
-//   stages filled by direct-to-LDS buffer loads together with the step's E8M0 scale
-//   bytes.  Staging all weights in LDS or none of them loads one of the two paths
-//   (LDS, or the per-CU vector memory path) well above the other; the even split
-//   measured fastest on every workload.
+//   tile, on one of two wave grids:
+//   - 4 x 1 (FP4 and FP8 with the identity, gated-SiLU and GELU epilogues): wave wn
+//     owns 64 features x all BM tokens (2 x TM result tiles of 32 x 32, TM = 6 or
+//     8).  No weight row is needed by two waves, so every weight fragment is loaded
+//     straight into a ring of registers several 64-K steps ahead, and only the
+//     activation tile is shared.
+//   - 2 x 2 (the other formats and epilogues): wave (wn, wm) owns 128 features x
+//     BM/2 tokens (4 x TM result tiles, TM = 3 or 4).  A head of QK-RMSNorm is then
+//     one or two waves wide.  Of each wave's 4 weight row groups, the 4-bit formats
+//     stage 2 through LDS (one copy per workgroup, read by the two waves of a row
+//     band) and load 2 into the register ring; the 8-bit formats, whose MFMAs take
+//     twice as long per byte, load all 4 into registers.
+//   The blob holds every fragment in the lane order of the MFMA operand, so no
+//   reshuffle is needed on either path.  The activation tile goes through LDS, in
+//   a ring of stages filled by direct-to-LDS buffer loads together with the step's
+//   block scale bytes.
 // * Persistent: one workgroup per CU walks its share of the tiles, and the loads
 //   run ahead across tile boundaries, so the next tile's first steps are in flight
 //   while the current tile's epilogue runs.
