@@ -18,6 +18,13 @@ Prints one JSON line:
                  changed since)
   cpu_baseline = the CPU oracle (float64) on a bounded row sample of the same
                  workload, timed on this host's cores
+  kernels      = per-kernel figures: the GEMM's mean and p10 / p50 / p90 event
+                 times, the quantizer's time and HBM rate, and two fusion
+                 comparisons (quantized output against GEMM + quantizer; gated-SiLU
+                 in the epilogue against an identity GEMM + a separate gated-SiLU
+                 pass over its bf16 output)
+  mfma_probe   = the FP4 MFMA rate of a register-only probe kernel on every CU,
+                 with the shader clock it ran at, and the GEMM's fraction of it
   library_reference = the vendor library's MXFP4 GEMM (hipBLASLt, through
                  torch._scaled_mm) on the same M, N, K with random E2M1 codes and
                  E8M0 scales: a plain GEMM to a bf16 [M, N] output, no epilogue and
@@ -125,6 +132,10 @@ def run_gpu(args):
     ms_per_step = wall * 1e3 / args.steps
     gemm_ms = sum(g_ms) / len(g_ms)
     quant_ms = sum(q_ms) / len(q_ms)
+    g_sorted = sorted(g_ms)
+
+    def pct(q):
+        return round(g_sorted[min(len(g_sorted) - 1, int(q * len(g_sorted)))] * 1e3, 2)
     achieved = flops / (gemm_ms * 1e-3) / 1e12
     quant_bytes = M * K * 2 + M * K // 2 + M * K // 32
     traffic = read_traffic()
@@ -148,6 +159,7 @@ def run_gpu(args):
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["fp4"], 4), "traffic": traffic},
         "kernels": {
             "gemm_fp4_gated_silu_us": round(gemm_ms * 1e3, 2),
+            "gemm_fp4_gated_silu_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
             "quant_fp4_us": round(quant_ms * 1e3, 2),
             "quant_fp4_GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
             "quant_fp4_hbm_frac": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / HBM_GBPS, 4),
@@ -155,6 +167,10 @@ def run_gpu(args):
     }
     if not args.no_fusion_compare:
         res["kernels"].update(time_quantized_output(ditq, torch, wl, sets, epi, args))
+        res["kernels"].update(time_unfused_epilogue(ditq, torch, wl, d, sets, epi, args))
+    if not args.no_probe:
+        res["mfma_probe"] = time_mfma_probe(ditq, torch)
+        res["mfma_probe"]["gemm_frac_of_probe"] = round(achieved / res["mfma_probe"]["tflops"], 4)
     if not args.no_library_compare:
         res["library_reference"] = time_library_reference(torch, wl, args)
     if args.all_configs:
@@ -200,6 +216,83 @@ def time_quantized_output(ditq, torch, wl, sets, epi, args):
         "gemm_then_quantize_us": round(times["unfused"], 2),
         "q4out_fusion_saving_us": round(times["unfused"] - times["fused"], 2),
     }
+
+
+def time_unfused_epilogue(ditq, torch, wl, d, sets, epi, args):
+    """The gated-SiLU GEMM fused (the small op on the accumulators, one bf16 store of
+    [M, N/2]) against unfused: an identity GEMM that stores C = [gate | up] as bf16
+    [M, N] (weights packed for the identity epilogue), then the separate gated-SiLU
+    pass that reads C back and writes [M, N/2].  Back-to-back sustained runs."""
+    M, N, K = wl.M, wl.N, wl.K
+    sptr = torch.cuda.current_stream().cuda_stream
+    w = torch.from_numpy(d["w"].view("int16")).cuda().view(torch.bfloat16)
+    blob_id0 = ditq.pack_weights(w, ditq.FMT_FP4, ditq.EPI_IDENTITY)
+    blob_ids = [blob_id0] + [blob_id0.clone() for _ in range(len(sets) - 1)]   # rotated like the fused blobs
+    del w
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    n = max(20, args.steps // 4)
+
+    def fused(i):
+        _, blob, codes, scales, out = sets[i % len(sets)]
+        ditq.dit_gemm_q4_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi, None,
+                                  out.data_ptr(), N // 2, sptr)
+
+    def identity_gemm(i):
+        _, _, codes, scales, _ = sets[i % len(sets)]
+        ditq.dit_gemm_q4_epilogue(codes.data_ptr(), scales.data_ptr(), blob_ids[i % len(sets)].data_ptr(), M, N, K,
+                                  ditq.EPI_IDENTITY, None, c.data_ptr(), N, sptr)
+
+    def separate_pass(i):
+        out = sets[i % len(sets)][4]
+        ditq.dit_gated_silu_bf16(c.data_ptr(), M, N, N, out.data_ptr(), N // 2, sptr)
+
+    def timed(fns):
+        for i in range(n // 2):
+            for f in fns:
+                f(i)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record()
+            for j, f in enumerate(fns):
+                f(i)
+                ev[i][j + 1].record()
+        torch.cuda.synchronize()
+        return [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / n * 1e3 for j in range(len(fns))]
+
+    t_fused, = timed([fused])
+    t_gemm, t_pass = timed([identity_gemm, separate_pass])
+    del blob_ids, blob_id0, c
+    return {
+        "unfused_identity_gemm_us": round(t_gemm, 2),
+        "unfused_gated_silu_pass_us": round(t_pass, 2),
+        "unfused_total_us": round(t_gemm + t_pass, 2),
+        "fused_gated_silu_gemm_us": round(t_fused, 2),
+        "epilogue_fusion_saving_us": round(t_gemm + t_pass - t_fused, 2),
+    }
+
+
+def time_mfma_probe(ditq, torch):
+    """Register-only FP4 MFMA probe on every CU: sustained TFLOP/s (median of 5
+    launches of ~2 ms) and the shader clock from its s_memtime cycle counts."""
+    wg = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 16000
+    flop = wg * 4 * iters * 8 * 2 * 32 * 32 * 64
+    for _ in range(2):
+        ditq.mfma_fp4_probe(wg, iters)
+    res = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out = ditq.mfma_fp4_probe(wg, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3
+        cyc = sorted(out[:, 0].cpu().tolist())[wg // 2]
+        res.append((flop / sec / 1e12, cyc / sec / 1e9))
+    res.sort()
+    tflops, ghz = res[len(res) // 2]
+    return {"tflops": round(tflops, 1), "clock_ghz": round(ghz, 3), "workgroups": wg, "iters": iters,
+            "frac_of_spec_peak": round(tflops / PEAK_TFLOPS["fp4"], 4)}
 
 
 def time_library_reference(torch, wl, args):
@@ -321,6 +414,12 @@ def cpu_baseline(d, budget_s: float):
     import numpy as np
     from oracle import epilogue, quant
     cores = len(os.sched_getaffinity(0))
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     M, K = d["x"].shape
     N = d["w"].shape[0]
     wc, ws = quant.quantize_fp4(d["w"])
@@ -345,7 +444,7 @@ def cpu_baseline(d, budget_s: float):
     times.sort()
     med = times[len(times) // 2]
     flops = 2.0 * rows * N * K
-    return {"value": round(flops / med / 1e12, 4), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": round(flops / med / 1e12, 4), "unit": "TFLOP/s", "cores": cores, "cpu": cpu, "kind": "oracle",
             "sample": f"{rows} of {M} token rows of the same workload (activation quantize + decode + float64 "
                       f"GEMM + gated-SiLU; weights quantized beforehand); median of {len(times)} repetitions, "
                       f"{med:.2f} s each"}
@@ -362,7 +461,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-configs", action="store_true", help="also time the other workloads' kernels")
     ap.add_argument("--no-fusion-compare", action="store_true",
-                    help="skip the fused vs unfused quantized-output timing (keeps a kernel trace to the timed steps)")
+                    help="skip the fused vs unfused timings (quantized output, gated-SiLU pass), which keeps a "
+                         "kernel trace to the timed steps")
+    ap.add_argument("--no-probe", action="store_true", help="skip the register-only MFMA probe")
     ap.add_argument("--no-library-compare", action="store_true",
                     help="skip timing the vendor library's MXFP4 GEMM at the same shape")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -1,8 +1,8 @@
 """Python binding of libditq (the fused low-bit DiT linear layer on MI355X).
 
 Argument marshalling only: every step runs in the HIP kernels of libditq.so.
-The functions named ``dit_*`` mirror the C ABI in include/ditq.h one to one and
-take raw device pointers (ints); the helpers below them take torch tensors and
+The functions named ``dit_*`` mirror the C ABI in include/ditq.h and
+include/ditq_measure.h one to one and take raw device pointers (ints); the helpers below them take torch tensors and
 use torch only for device memory and the current stream.
 
 The library must have been built (``python bit_gemm_dit_amd/build.py``); import
@@ -19,6 +19,7 @@ __all__ = [
     "dit_packed_weight_bytes", "dit_act_code_bytes", "dit_act_scale_bytes", "dit_pack_weights",
     "dit_quantize_act", "dit_gemm_q4_epilogue", "dit_gemm_q4_epilogue_q4", "dit_gemm_q8_epilogue",
     "dit_gemm_epilogue", "dit_gemm_gate_residual", "gemm_gate_residual",
+    "dit_gated_silu_bf16", "dit_mfma_fp4_probe", "gated_silu", "mfma_fp4_probe",
     "dit_status_str", "dit_last_error", "pack_weights", "quantize_act", "gemm", "gemm_q4out", "linear",
     "library_path", "EXPORTED",
 ]
@@ -75,6 +76,8 @@ _SIGS = {
     "dit_gemm_q8_epilogue": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _i, _p]),
     "dit_gemm_epilogue": (_i, [_i, _p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams), _p, _i, _p]),
     "dit_gemm_gate_residual": (_i, [_i, _p, _p, _p, _i, _i, _i, ctypes.POINTER(GateResidualParams), _p, _i, _p]),
+    "dit_gated_silu_bf16": (_i, [_p, _i, _i, _i, _p, _i, _p]),
+    "dit_mfma_fp4_probe": (_i, [_i, _i, _p, _p]),
     "dit_status_str": (ctypes.c_char_p, [_i]),
     "dit_last_error": (ctypes.c_char_p, []),
 }
@@ -154,6 +157,14 @@ def dit_gemm_gate_residual(fmt, a_codes, a_scales, w_packed, M, N, K, gr, out, l
     gp = ctypes.byref(gr) if gr is not None else None
     _check(_lib.dit_gemm_gate_residual(fmt, a_codes, a_scales, w_packed, M, N, K, gp, out, ldo, stream),
            "dit_gemm_gate_residual")
+
+
+def dit_gated_silu_bf16(c, M, N, ldc, out, ldo, stream=None) -> None:
+    _check(_lib.dit_gated_silu_bf16(c, M, N, ldc, out, ldo, stream), "dit_gated_silu_bf16")
+
+
+def dit_mfma_fp4_probe(workgroups, iters, out_u64, stream=None) -> None:
+    _check(_lib.dit_mfma_fp4_probe(workgroups, iters, out_u64, stream), "dit_mfma_fp4_probe")
 
 
 # ---------------------------------------------------------------- torch helpers
@@ -262,6 +273,26 @@ def linear(x, blob, N: int, fmt: int, epi: int, rms: RmsNormParams | None = None
     """The whole layer: quantize x on the fly, then the fused GEMM + epilogue."""
     codes, scales = quantize_act(x, fmt)
     return gemm(codes, scales, blob, N, x.shape[1], fmt, epi, rms=rms, out=out)
+
+
+def gated_silu(c, out=None):
+    """Gated-SiLU as a separate pass over a bf16 GEMM output c = [gate | up] [M, N];
+    returns bf16 [M, N/2] (the unfused form of EPI_GATED_SILU)."""
+    import torch
+    M, N = c.shape
+    if out is None:
+        out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=c.device)
+    dit_gated_silu_bf16(c.data_ptr(), M, N, _ld(c), out.data_ptr(), _ld(out), _stream())
+    return out
+
+
+def mfma_fp4_probe(workgroups: int, iters: int):
+    """Enqueue the matrix-core probe; returns the uint64 device tensor [workgroups, 2]
+    of (loop cycles of wave 0, checksum) per workgroup."""
+    import torch
+    out = torch.zeros((workgroups, 2), dtype=torch.int64, device="cuda")
+    dit_mfma_fp4_probe(workgroups, iters, out.data_ptr(), _stream())
+    return out
 
 
 def rmsnorm_params(gamma_q, gamma_k, n_heads: int, eps: float) -> RmsNormParams:

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libditq.so")
-SOURCES = ["abi.cpp", "quant.hip", "pack.hip", "gemm.hip"]
+SOURCES = ["abi.cpp", "quant.hip", "pack.hip", "gemm.hip", "measure.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -2,9 +2,10 @@
 //
 // Every check runs on the host before any HIP call (so the error paths can be
 // exercised without a device); the kernels themselves live in quant.hip,
-// pack.hip and gemm.hip.  The entry points and their contracts are declared and
-// documented in include/ditq.h.
+// pack.hip, gemm.hip and measure.hip.  The entry points and their contracts are
+// declared and documented in include/ditq.h and include/ditq_measure.h.
 #include "ditq.h"
+#include "ditq_measure.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -229,6 +230,27 @@ dit_status dit_gemm_gate_residual(dit_fmt fmt, const void* a_codes, const void* 
   if (!gr || !out_bf16) return DIT_EINVAL;
   return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, DIT_EPI_GATE_RESIDUAL, nullptr, gr, out_bf16, ldo,
                   nullptr, nullptr, stream);
+}
+
+dit_status dit_gated_silu_bf16(const void* c_bf16, int M, int N, int ldc, void* out_bf16, int ldo,
+                               void* stream) {
+  if (!c_bf16 || !out_bf16 || M <= 0 || N <= 0) return DIT_EINVAL;
+  if (N % 16 != 0 || (long long)M * (N / 16) >= (1LL << 31)) return DIT_EUNSUPPORTED;
+  if (!aligned16(c_bf16) || !aligned16(out_bf16) || ldc < N || ldo < N / 2 || ldc % 8 != 0 || ldo % 8 != 0)
+    return DIT_EALIGN;
+  if (dit_status s = check_device()) return s;
+  (void)hipGetLastError();
+  return launched(ditq::launch_gated_silu(static_cast<const uint16_t*>(c_bf16), M, N, ldc,
+                                          static_cast<uint16_t*>(out_bf16), ldo, static_cast<hipStream_t>(stream)));
+}
+
+dit_status dit_mfma_fp4_probe(int workgroups, int iters, void* out_u64, void* stream) {
+  if (!out_u64 || workgroups < 1 || workgroups > 65535 || iters < 1 || iters > (1 << 20)) return DIT_EINVAL;
+  if (!aligned(out_u64, 8)) return DIT_EALIGN;
+  if (dit_status s = check_device()) return s;
+  (void)hipGetLastError();
+  return launched(ditq::launch_mfma_probe(workgroups, iters, static_cast<unsigned long long*>(out_u64),
+                                          static_cast<hipStream_t>(stream)));
 }
 
 const char* dit_last_error(void) { return g_last_error; }

@@ -240,4 +240,9 @@ hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, co
                        int K, int epi, const RmsArgs* rms, const ResidualArgs* gr, uint16_t* out, int ldo,
                        uint8_t* q_codes, uint8_t* q_scales, hipStream_t stream);
 
+// measurement kernels (measure.hip)
+hipError_t launch_gated_silu(const uint16_t* c, int M, int N, int ldc, uint16_t* out, int ldo,
+                             hipStream_t stream);
+hipError_t launch_mfma_probe(int workgroups, int iters, unsigned long long* out, hipStream_t stream);
+
 }  // namespace ditq

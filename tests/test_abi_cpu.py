@@ -1,4 +1,4 @@
-"""The C ABI on the CPU: the library loads, exports every function include/ditq.h
+"""The C ABI on the CPU: the library loads, exports every function include/*.h
 declares, its size queries are right, and every validation path returns its
 status before any HIP call (fake pointers are never dereferenced)."""
 import ctypes
@@ -8,7 +8,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ditq.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 ditq = pytest.importorskip("bit_gemm_dit_amd", reason="libditq.so not built")
 
@@ -20,9 +21,11 @@ D = 0x40000
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dit_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(dit_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -211,3 +214,27 @@ def test_gate_residual_validation():
             assert _any(fmt=fmt, epi=3, ldo=512) == EDEVICE               # GELU-tanh
         assert _q4(epi=3, ldo=512) == EDEVICE
         assert ditq._lib.dit_gemm_q8_epilogue(A, B, C, 4, 512, 256, 3, D, 512, None) == EDEVICE
+
+
+def test_measurement_entry_points_validation():
+    gs = ditq._lib.dit_gated_silu_bf16
+    assert gs(None, 64, 512, 512, D, 256, None) == EINVAL
+    assert gs(A, 64, 512, 512, None, 256, None) == EINVAL
+    assert gs(A, 0, 512, 512, D, 256, None) == EINVAL
+    assert gs(A, 64, -16, 512, D, 256, None) == EINVAL
+    assert gs(A, 64, 520, 520, D, 260, None) == EUNSUP               # N % 16
+    assert gs(A + 8, 64, 512, 512, D, 256, None) == EALIGN
+    assert gs(A, 64, 512, 512, D + 4, 256, None) == EALIGN
+    assert gs(A, 64, 512, 500, D, 256, None) == EALIGN               # ldc < N
+    assert gs(A, 64, 512, 512, D, 248, None) == EALIGN               # ldo < N/2
+    assert gs(A, 64, 512, 516, D, 256, None) == EALIGN               # ldc % 8
+    pr = ditq._lib.dit_mfma_fp4_probe
+    assert pr(256, 100, None, None) == EINVAL
+    assert pr(0, 100, A, None) == EINVAL
+    assert pr(65536, 100, A, None) == EINVAL
+    assert pr(256, 0, A, None) == EINVAL
+    assert pr(256, (1 << 20) + 1, A, None) == EINVAL
+    assert pr(256, 100, A + 4, None) == EALIGN
+    if not _has_gpu():
+        assert gs(A, 64, 512, 512, D, 256, None) == EDEVICE
+        assert pr(256, 100, A, None) == EDEVICE
