@@ -28,8 +28,9 @@
  *     DIT_EALIGN       a pointer not 16-byte aligned, or a leading dimension
  *                      smaller than the row width or not a multiple of 8 elements
  *     DIT_EDEVICE      no usable gfx950 device, or a launch error
- * - Outputs must not alias inputs.  Results are bitwise deterministic (no atomics,
- *   no split-K).  Calls on different streams may run concurrently.
+ * - Outputs must not alias inputs.  Results are bitwise deterministic (no split-K;
+ *   the only atomic, the NVFP4 tensor maximum, does not depend on order).  Calls
+ *   on different streams may run concurrently.
  * - Matrices are row-major.  bf16 tensors are given as raw 16-bit patterns.
  */
 #ifndef DITQ_H
