@@ -1036,11 +1036,13 @@ hipError_t launch(Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Token-tile height 192 or 256 (TM = 3 or 4 per wave on the 2 x 2 grid, 6 or 8 on the
-// 4 x 1 grid), whichever gives the fewest
+// Token-tile height: on the 4 x 1 grid always 192 (TM = 6; at 256 tokens its 256
+// accumulators leave too few registers, and the spilling kernel measured 5-8 %
+// slower even where it saves a round of tiles: M = 2048 and 4096 with N = 16384).
+// On the 2 x 2 grid 192 or 256 (TM = 3 or 4 per wave), whichever gives the fewest
 // rounds of tiles over the CUs, weighted by the tile's work plus a fixed cost of
 // about half a token tile (FP8 and MXFP8 always 192: with 256 their operand
-// registers spill); FP4 weight ring of 8 units when the k-steps come in groups of
+// registers spill).  FP4 weight ring of 8 units when the k-steps come in groups of
 // 4, else 4 (FP8 and MXFP8: 4).
 template <int FMT, int EPI, int HD = 0, int WLDS = wlds_for(FMT)>
 hipError_t launch_cfg(Params& p, hipStream_t stream) {
@@ -1059,24 +1061,21 @@ hipError_t launch_cfg(Params& p, hipStream_t stream) {
     else return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
   } else {
     const int nks = p.K / 128;
-    const int cus = cu_count();
-    const long tn = padded_rows(p.N) / 256;
-    const long r3 = ((p.M + 191) / 192 * tn + cus - 1) / cus, r4 = ((p.M + 255) / 256 * tn + cus - 1) / cus;
-    const bool tm3 = r3 * 7 < r4 * 9;
     if constexpr (grid41) {
+      if (nks % 4 != 0) return launch<Tile<FMT, EPI, 6, 4, 0, HD, 4>>(p, stream);
+      return launch<Tile<FMT, EPI, 6, 8, 0, HD, 4>>(p, stream);
+    } else {
+      const int cus = cu_count();
+      const long tn = padded_rows(p.N) / 256;
+      const long r3 = ((p.M + 191) / 192 * tn + cus - 1) / cus, r4 = ((p.M + 255) / 256 * tn + cus - 1) / cus;
+      const bool tm3 = r3 * 7 < r4 * 9;
       if (nks % 4 != 0) {
-        if (tm3) return launch<Tile<FMT, EPI, 6, 4, 0, HD, 4>>(p, stream);
-        return launch<Tile<FMT, EPI, 8, 4, 0, HD, 4>>(p, stream);
+        if (tm3) return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
+        return launch<Tile<FMT, EPI, 4, 4, WLDS, HD>>(p, stream);
       }
-      if (tm3) return launch<Tile<FMT, EPI, 6, 8, 0, HD, 4>>(p, stream);
-      return launch<Tile<FMT, EPI, 8, 8, 0, HD, 4>>(p, stream);
+      if (tm3) return launch<Tile<FMT, EPI, 3, 8, WLDS, HD>>(p, stream);
+      return launch<Tile<FMT, EPI, 4, 8, WLDS, HD>>(p, stream);
     }
-    if (nks % 4 != 0) {
-      if (tm3) return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
-      return launch<Tile<FMT, EPI, 4, 4, WLDS, HD>>(p, stream);
-    }
-    if (tm3) return launch<Tile<FMT, EPI, 3, 8, WLDS, HD>>(p, stream);
-    return launch<Tile<FMT, EPI, 4, 8, WLDS, HD>>(p, stream);
   }
 }
 
