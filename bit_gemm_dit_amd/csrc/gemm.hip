@@ -105,7 +105,11 @@ struct Tile {
   static constexpr int WS_OFF = AS_OFF + AS_BYTES;
   static constexpr int WS_BYTES = NV ? BN / 32 * 256 : MX ? BN / 32 * 128 : 0;
   static constexpr int STAGE = (WS_OFF + WS_BYTES + 255) / 256 * 256;
-  static constexpr int STAGES_FIT = (160 * 1024 - 1024 - (HD == 256 ? WAVES_N * BM * 4 : 0)) / STAGE;
+  // QK-RMSNorm: waves along N per head (a head wider than one wave's columns sums
+  // its squares across waves through LDS: WAVES_N x BM per-token partial sums)
+  static constexpr int HEAD_WAVES = HD > WN ? HD / WN : 1;
+  static constexpr int RED_BYTES = HEAD_WAVES > 1 ? WAVES_N * BM * 4 : 0;
+  static constexpr int STAGES_FIT = (160 * 1024 - 1024 - RED_BYTES) / STAGE;
   static constexpr int WCK = W_BYTES / 1024 / NW;            // 1 KB weight copies per wave per stage
   static constexpr int ACK = A_BYTES / 1024 / NW;            // 1 KB activation copies per wave per stage
   static constexpr int ACKP = ACK / APANELS;                   // ... per code panel
@@ -121,8 +125,7 @@ struct Tile {
   static constexpr int STAGES = STAGES_FIT < 5 ? (STAGES_FIT < STAGES_VM ? STAGES_FIT : STAGES_VM)
                                                : (5 < STAGES_VM ? 5 : STAGES_VM);
   static constexpr int JUNK_OFF = STAGES * STAGE;            // target of the prologue's padding copies
-  static constexpr int RED_OFF = JUNK_OFF + 1024;            // per-token partial sums (head_dim 256)
-  static constexpr int RED_BYTES = HD == 256 ? WAVES_N * BM * 4 : 0;
+  static constexpr int RED_OFF = JUNK_OFF + 1024;            // per-token partial sums of squares
   static constexpr int LDS_BYTES = RED_OFF + RED_BYTES;
   // Waits, as the number of operations that may stay outstanding (vmcnt counts
   // in issue order; the counts below hold whatever the order inside a half).
@@ -594,12 +597,14 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
       }
     }
   } else {
-    // Per-head QK-RMSNorm.  head_dim 128: the wave's 128 columns are one head.
-    // head_dim 256: the workgroup's 256 columns are one head; waves wn = 0 and 1
-    // hold its first and second 128 columns and exchange per-token partial sums of
-    // squares through LDS (both add the same two numbers, so both get the same sum).
-    constexpr int D = T::HD;
-    static_assert(D == T::WN || D == T::BN, "a head is one wave or one workgroup wide");
+    // Per-head QK-RMSNorm.  A head is HW = head_dim / (the wave's columns) waves
+    // wide: one wave (2 x 2 grid, head_dim 128), two (2 x 2 grid with head_dim 256,
+    // 4 x 1 grid with 128) or four (4 x 1 grid, 256).  Waves of one head exchange
+    // per-token partial sums of squares through LDS, and each of them adds the HW
+    // partial sums in the same order, so all get the same sum.
+    constexpr int D = T::HD, HW = T::HEAD_WAVES;
+    static_assert(D % T::WN == 0, "a head is whole waves wide");
+    static_assert(T::BN % D == 0, "a tile holds whole heads");
     if constexpr (T::FMT == FMT_FP8) {
       // the row / column scales first: the norm is taken over the scaled values
 #pragma unroll
@@ -617,10 +622,8 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
           }
       }
     }
-    const int head = D == T::WN ? n0w / D : (n0w - wn * T::WN) / D;
-    const int part = head / p.n_heads;          // 0 = Q, 1 = K, 2 = V, 3 = padding past N
-    if (part >= 3) return;                      // uniform over the workgroup when D == BN
-    if (part == 2) {
+    const int part = (n0w / D) / p.n_heads;     // 0 = Q, 1 = K, 2 = V, 3 = padding past N
+    auto store_raw = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int tm = 0; tm < T::TM; ++tm) {
         __builtin_amdgcn_sched_barrier(0);
@@ -633,12 +636,18 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
           store_tile<T>(p, row, row < p.M, n0w + 32 * tn, p.N, h, v);
         }
       }
-      return;
+    };
+    if constexpr (HW == 1) {
+      if (part >= 3) return;
+      if (part == 2) {
+        store_raw();
+        return;
+      }
     }
-    const float* gamma = (part == 0 ? p.gamma_q : p.gamma_k) + (D == T::WN ? 0 : wn * T::WN);
-    // Sums of squares per token: the two 64-column halves of the wave (the first
+    const float* gamma = (part == 0 ? p.gamma_q : p.gamma_k) + (wn % HW) * T::WN;
+    // Sums of squares per token: the two halves of the wave's columns (the first
     // half's values stay in registers while the second half's sum is formed), then
-    // the partner lane's 16 rows of each tile, then (head_dim 256) the other wave.
+    // the partner lane's 16 rows of each tile, then the other waves of the head.
     float ss[T::TM];
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) {
@@ -654,7 +663,8 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
       ss[tm] = ss_first + ss_second;
       ss[tm] += __shfl_xor(ss[tm], 32);
     }
-    if constexpr (D != T::WN) {
+    if constexpr (HW > 1) {
+      // every wave of the workgroup writes and reaches the barrier, whatever its part
       float* red = reinterpret_cast<float*>(lds + T::RED_OFF);
       if (lane < 32) {
 #pragma unroll
@@ -662,8 +672,19 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
       }
       wait_lds();
       barrier();
+      const int w0 = wn - wn % HW;
 #pragma unroll
-      for (int tm = 0; tm < T::TM; ++tm) ss[tm] += red[(1 - wn) * T::BM + wm * T::WM + 32 * tm + l32];
+      for (int tm = 0; tm < T::TM; ++tm) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < HW; ++j) sum += red[(w0 + j) * T::BM + wm * T::WM + 32 * tm + l32];
+        ss[tm] = sum;
+      }
+      if (part >= 3) return;
+      if (part == 2) {
+        store_raw();
+        return;
+      }
     }
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) {
@@ -1050,9 +1071,11 @@ hipError_t launch_cfg(Params& p, hipStream_t stream) {
   // Measured faster than the 2 x 2 grid for FP4 (headline 122 vs 129 us) and FP8
   // (CFG-pair identity 316 vs 325 us): no weight row is loaded by two waves, so the
   // vector memory path carries less per k-step and CU.  MXFP8 and NVFP4 measured no
-  // faster and keep the 2 x 2 grid.  A head of QK-RMSNorm needs 128 or 256 features
-  // in one or two waves, and the gated residual's epilogue spills in the 256-token
-  // variant, so those keep the 2 x 2 grid too.
+  // faster and keep the 2 x 2 grid.  So does the gated residual, whose epilogue
+  // spills on the 4 x 1 grid, and so does QK-RMSNorm: on the 4 x 1 grid a head spans
+  // two or four waves (the epilogue handles it), but FP4 measured slower there
+  // (head_dim 128: 109.6 vs 102 us; head_dim 256: 156 vs 127 us, where the 2 x 2
+  // grid's 256-token tiles fit M = 4096 in 3 rounds) and FP8 no faster.
   constexpr bool grid41 = (FMT == FMT_FP4 || FMT == FMT_FP8) && EPI != EPI_QK_RMSNORM &&
                           EPI != EPI_GATE_RESIDUAL;
   if constexpr (FMT != FMT_FP4) {
