@@ -66,7 +66,11 @@ constexpr int kRowBytes = 64;    // operand bytes per row per k-step
 // four evenly; FP8 and MXFP8, whose MFMAs take twice as long per byte, load all of
 // them into registers.
 constexpr int wlds_for(int fmt) { return fmt == FMT_FP4 ? 2 : 0; }
-constexpr int kGroupM = 4;       // tile-order group height (in M tiles)
+// Tile-order group height (in M tiles).  8 and 4 run at the same speed on the
+// headline shape; 8 keeps each weight tile shared by more of the tiles in flight on
+// an XCD, which cuts the L2 miss traffic per launch from 226 to 204 MB (12 and 24
+// measured slower).
+constexpr int kGroupM = 8;
 
 // WLDS: how many of the wave's 4 weight row groups come through LDS (shared by the
 // two waves of a row band, one copy per workgroup); the other TN - WLDS groups are
