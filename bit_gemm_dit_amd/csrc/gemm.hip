@@ -38,10 +38,10 @@
 //     activation tile is shared.
 //   - 2 x 2 (the other formats and epilogues): wave (wn, wm) owns 128 features x
 //     BM/2 tokens (4 x TM result tiles, TM = 3 or 4).  A head of QK-RMSNorm is then
-//     one or two waves wide.  Of each wave's 4 weight row groups, the 4-bit formats
-//     stage 2 through LDS (one copy per workgroup, read by the two waves of a row
-//     band) and load 2 into the register ring; the 8-bit formats, whose MFMAs take
-//     twice as long per byte, load all 4 into registers.
+//     one or two waves wide.  Of each wave's 4 weight row groups, FP4, NVFP4 and
+//     FP8 stage 2 through LDS (one copy per workgroup, read by the two waves of a
+//     row band) and load 2 into the register ring; MXFP8 loads all 4 into
+//     registers.
 //   The blob holds every fragment in the lane order of the MFMA operand, so no
 //   reshuffle is needed on either path.  The activation tile goes through LDS, in
 //   a ring of stages filled by direct-to-LDS buffer loads together with the step's
@@ -62,10 +62,12 @@ namespace ditq {
 namespace {
 
 constexpr int kRowBytes = 64;    // operand bytes per row per k-step
-// Weight row groups per wave staged through LDS (measured best): FP4 splits the
-// four evenly; FP8 and MXFP8, whose MFMAs take twice as long per byte, load all of
-// them into registers.
-constexpr int wlds_for(int fmt) { return fmt == FMT_FP4 ? 2 : 0; }
+// Weight row groups per wave staged through LDS on the 2 x 2 grid (measured best):
+// FP4 and FP8 split the four evenly (FP8 with all four in registers spills in the
+// QK-RMSNorm and gated-residual epilogues and measured 1-3 % slower); MXFP8, whose
+// 4 KB groups per k-step the LDS copies do not cover, loads all of them into
+// registers.
+constexpr int wlds_for(int fmt) { return fmt == FMT_FP4 || fmt == FMT_FP8 ? 2 : 0; }
 // Tile-order group height (in M tiles).  8 and 4 run at the same speed on the
 // headline shape; 8 keeps each weight tile shared by more of the tiles in flight on
 // an XCD, which cuts the L2 miss traffic per launch from 226 to 204 MB (12 and 24
