@@ -606,8 +606,8 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
     // Per-head QK-RMSNorm.  A head is HW = head_dim / (the wave's columns) waves
     // wide: one wave (2 x 2 grid, head_dim 128), two (2 x 2 grid with head_dim 256,
     // 4 x 1 grid with 128) or four (4 x 1 grid, 256).  Waves of one head exchange
-    // per-token partial sums of squares through LDS, and each of them adds the HW
-    // partial sums in the same order, so all get the same sum.
+    // per-token partial sums of squares through LDS, and all of them form the same
+    // sum (two waves: own + partner; more: the partial sums in one fixed order).
     constexpr int D = T::HD, HW = T::HEAD_WAVES;
     static_assert(D % T::WN == 0, "a head is whole waves wide");
     static_assert(T::BN % D == 0, "a tile holds whole heads");
@@ -643,7 +643,11 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
         }
       }
     };
-    if constexpr (HW == 1) {
+    // Where every wave of the workgroup has the same part (a head is one wave, or the
+    // whole tile), V and padding leave here; otherwise only after the exchange,
+    // which every wave of the workgroup must reach.
+    constexpr bool uniform_part = HW == 1 || HW == T::WAVES_N;
+    if constexpr (uniform_part) {
       if (part >= 3) return;
       if (part == 2) {
         store_raw();
@@ -670,7 +674,7 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
       ss[tm] += __shfl_xor(ss[tm], 32);
     }
     if constexpr (HW > 1) {
-      // every wave of the workgroup writes and reaches the barrier, whatever its part
+      // every wave still here writes and reaches the barrier
       float* red = reinterpret_cast<float*>(lds + T::RED_OFF);
       if (lane < 32) {
 #pragma unroll
@@ -678,18 +682,26 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
       }
       wait_lds();
       barrier();
-      const int w0 = wn - wn % HW;
+      if constexpr (HW == 2) {
+        // own + partner: fp32 addition commutes, so both waves get the same sum
 #pragma unroll
-      for (int tm = 0; tm < T::TM; ++tm) {
-        float sum = 0.0f;
+        for (int tm = 0; tm < T::TM; ++tm) ss[tm] += red[(wn ^ 1) * T::BM + wm * T::WM + 32 * tm + l32];
+      } else {
+        const int w0 = wn - wn % HW;
 #pragma unroll
-        for (int j = 0; j < HW; ++j) sum += red[(w0 + j) * T::BM + wm * T::WM + 32 * tm + l32];
-        ss[tm] = sum;
+        for (int tm = 0; tm < T::TM; ++tm) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int j = 0; j < HW; ++j) sum += red[(w0 + j) * T::BM + wm * T::WM + 32 * tm + l32];
+          ss[tm] = sum;
+        }
       }
-      if (part >= 3) return;
-      if (part == 2) {
-        store_raw();
-        return;
+      if constexpr (!uniform_part) {
+        if (part >= 3) return;
+        if (part == 2) {
+          store_raw();
+          return;
+        }
       }
     }
 #pragma unroll
