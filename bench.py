@@ -25,6 +25,8 @@ Prints one JSON line:
                  pass over its bf16 output)
   mfma_probe   = the FP4 MFMA rate of a register-only probe kernel on every CU,
                  with the shader clock it ran at, and the GEMM's fraction of it
+  power        = socket power and GFX clock (amdsmi) sampled while ~1.5 s of the
+                 same steps run back to back, and the steps' TFLOP/s per watt
   library_reference = the vendor library's MXFP4 GEMM (hipBLASLt, through
                  torch._scaled_mm) on the same M, N, K with random E2M1 codes and
                  E8M0 scales: a plain GEMM to a bf16 [M, N] output, no epilogue and
@@ -37,6 +39,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -168,6 +171,8 @@ def run_gpu(args):
     if not args.no_fusion_compare:
         res["kernels"].update(time_quantized_output(ditq, torch, wl, sets, epi, args))
         res["kernels"].update(time_unfused_epilogue(ditq, torch, wl, d, sets, epi, args))
+    if not args.no_power:
+        res["power"] = sample_power_and_clock(torch, step, wl.flops)
     if not args.no_probe:
         res["mfma_probe"] = time_mfma_probe(ditq, torch)
         res["mfma_probe"]["gemm_frac_of_probe"] = round(achieved / res["mfma_probe"]["tflops"], 4)
@@ -269,6 +274,61 @@ def time_unfused_epilogue(ditq, torch, wl, d, sets, epi, args):
         "fused_gated_silu_gemm_us": round(t_fused, 2),
         "epilogue_fusion_saving_us": round(t_gemm + t_pass - t_fused, 2),
     }
+
+
+def sample_power_and_clock(torch, step, flops, seconds=1.5):
+    """Socket power and GFX clock from amdsmi, sampled every 20 ms by a thread while
+    the benchmark's step (quantize + GEMM) runs back to back for about `seconds`
+    (after 0.3 s of warm-up at load).  Read-only queries; null where amdsmi is absent."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # no amdsmi on this host: report it, do not fail
+        return {"error": f"{type(e).__name__}: {str(e)[:160]}"}
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                pw = amdsmi.amdsmi_get_power_info(h)
+                ck = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+                samples.append((float(pw["current_socket_power"]), float(ck["clk"])))
+            except Exception:
+                pass
+            time.sleep(0.02)
+
+    i = 0
+
+    def run_for(sec):
+        nonlocal i
+        t_end = time.perf_counter() + sec
+        while time.perf_counter() < t_end:
+            for _ in range(32):
+                step(i)
+                i += 1
+            torch.cuda.synchronize()
+
+    run_for(0.3)
+    th = threading.Thread(target=sampler, daemon=True)
+    i0, t0 = i, time.perf_counter()
+    th.start()
+    run_for(seconds)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if not samples:
+        return {"error": "no samples"}
+    watts = sum(p for p, _ in samples) / len(samples)
+    mhz = sum(c for _, c in samples) / len(samples)
+    tflops = flops * (i - i0) / elapsed / 1e12
+    return {"socket_power_w": round(watts, 1), "gfx_clock_mhz": round(mhz, 1), "samples": len(samples),
+            "steps": i - i0, "step_tflops": round(tflops, 1), "tflops_per_w": round(tflops / watts, 2)}
 
 
 def time_mfma_probe(ditq, torch):
@@ -464,6 +524,8 @@ def main():
                     help="skip the fused vs unfused timings (quantized output, gated-SiLU pass), which keeps a "
                          "kernel trace to the timed steps")
     ap.add_argument("--no-probe", action="store_true", help="skip the register-only MFMA probe")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the power / clock sampling run (keeps a kernel trace to the timed steps)")
     ap.add_argument("--no-library-compare", action="store_true",
                     help="skip timing the vendor library's MXFP4 GEMM at the same shape")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
