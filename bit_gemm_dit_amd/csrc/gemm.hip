@@ -32,8 +32,8 @@
 // * A workgroup of 4 waves (one per SIMD) computes a 256 (features) x BM (tokens)
 //   tile, on one of two wave grids:
 //   - 4 x 1 (FP4 and FP8 with the identity, gated-SiLU and GELU epilogues): wave wn
-//     owns 64 features x all BM tokens (2 x TM result tiles of 32 x 32, TM = 6 or
-//     8).  No weight row is needed by two waves, so every weight fragment is loaded
+//     owns 64 features x all BM tokens (2 x 6 result tiles of 32 x 32, BM = 192).
+//     No weight row is needed by two waves, so every weight fragment is loaded
 //     straight into a ring of registers several 64-K steps ahead, and only the
 //     activation tile is shared.
 //   - 2 x 2 (the other formats and epilogues): wave (wn, wm) owns 128 features x
