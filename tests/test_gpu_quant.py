@@ -238,6 +238,34 @@ def test_nv4_quantizer_every_bf16_value(ditq):
         np.testing.assert_array_equal(c, rc)
 
 
+@pytest.mark.parametrize("where", ["first", "last", "interior"])
+def test_nv4_tensor_maximum_anywhere(ditq, where):
+    """The tensor maximum is found wherever the one largest magnitude sits: the first
+    element, the last, or a random one inside.  The shape spans more than one
+    grid-stride pass of the maximum kernel, and the row stride is padded (the
+    padding holds a larger value that must be ignored)."""
+    import torch
+    from tests.gpu_util import to_dev_bf16
+    M, K, ldx = 4608, 3072, 3080
+    rng = np.random.default_rng({"first": 1, "last": 2, "interior": 3}[where])
+    bits = f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    r, c = {"first": (0, 0), "last": (M - 1, K - 1)}.get(where, (int(rng.integers(M)), int(rng.integers(K))))
+    bits[r, c] = f32_to_bf16_bits(np.array([-1000.0 if where == "interior" else 1000.0], np.float32))[0]
+    buf = np.full((M, ldx), f32_to_bf16_bits(np.array([30000.0], np.float32))[0], dtype=np.uint16)
+    buf[:, :K] = bits
+    x = to_dev_bf16(buf)
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((ditq.dit_act_scale_bytes(ditq.FMT_NV4, M, K),), dtype=torch.uint8, device="cuda")
+    print(f"nv4 tensor maximum at {where} ({r}, {c})", flush=True)
+    ditq.dit_quantize_act(ditq.FMT_NV4, x.data_ptr(), M, K, ldx, codes.data_ptr(), scales.data_ptr(),
+                          torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    from tests.gpu_util import nv4_act_scales
+    _, st = nv4_act_scales(scales.cpu().numpy(), M, K)
+    want = quant.nv4_tensor_scale(np.float32(1000.0))
+    assert np.float32(st).view(np.uint32) == np.float32(want).view(np.uint32)
+
+
 def test_nv4_quantizer_full_size_workload(ditq):
     d = make_inputs("mlp_gated_silu", seed=0)
     c, s, st = _run_nv4(ditq, d["x"])
