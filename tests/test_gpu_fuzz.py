@@ -12,7 +12,10 @@ Each case is drawn from one seeded generator:
 Every element is compared with the oracle, guard bytes around the output and its
 padding must stay untouched, and the residual must only be read.  The fixed cases
 of test_gpu_gemm.py pin chosen shapes; these cover the combinations in between.
+The environment variable DITQ_FUZZ_CASES sets a longer list for a soak run.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -24,7 +27,7 @@ KIND = {"identity": "mlp_gated_silu", "gated_silu": "mlp_gated_silu", "gelu_tanh
         "rms128": "qkv_rmsnorm_hd128", "rms256": "qkv_rmsnorm_hd256", "gate_residual": "mlp_down_gate_residual"}
 
 
-def _cases(n=48, seed=2024):
+def _cases(n=200, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -51,7 +54,8 @@ def _cases(n=48, seed=2024):
     return out
 
 
-CASES = _cases()
+# DITQ_FUZZ_CASES draws a longer list (the first 200 cases are always the same)
+CASES = _cases(int(os.environ.get("DITQ_FUZZ_CASES", "200")))
 
 
 @pytest.fixture(scope="module")
