@@ -99,7 +99,7 @@ size_t dit_act_code_bytes(dit_fmt fmt, int M, int K) {
 size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K) {
   if (!valid_fmt(fmt) || M <= 0 || K <= 0 || K % 256 != 0) return 0;
   if (fmt == DIT_FMT_FP8_E4M3_ROWCOL) return (size_t)M * 4;
-  if (fmt == DIT_FMT_FP4_E2M1_NV16) return ditq::nv4_act_tail(M, K) + 16;
+  if (fmt == DIT_FMT_FP4_E2M1_NV16) return ditq::nv4_act_tail(M, K) + ditq::kNvTailBytes + ditq::kNvPartialBytes;
   return (size_t)M * K / 32;
 }
 

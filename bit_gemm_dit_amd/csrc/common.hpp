@@ -42,7 +42,11 @@ __host__ __device__ inline size_t blob_scale_bytes(int fmt, int Np, int K) {
   return fmt == FMT_FP8 ? (size_t)Np * 4 : fmt == FMT_NV4 ? (size_t)Np * K / 16 : (size_t)Np * K / 32;
 }
 // NVFP4 activation scales: M*K/16 block scale bytes, then a 16-byte tail holding the
-// tensor-maximum slot (u32) and the fp32 tensor scale.
+// tensor-maximum slot (u32) and the fp32 tensor scale, then the per-workgroup maxima
+// of the tensor-maximum pass (kAmaxBlocks u32).
+constexpr uint32_t kAmaxBlocks = 512;
+constexpr int kNvTailBytes = 16;
+constexpr int kNvPartialBytes = 4 * kAmaxBlocks;
 __host__ __device__ inline size_t nv4_act_tail(int M, int K) { return (size_t)M * K / 16; }
 __host__ __device__ inline size_t blob_scales_offset(int fmt, int Np, int K) {
   return kHeaderBytes + blob_code_bytes(fmt, Np, K);
@@ -224,12 +228,13 @@ hipError_t launch_quant_fp8(const uint16_t* x, int M, int K, int ldx, uint8_t* c
                             hipStream_t stream);
 hipError_t launch_quant_mx8(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
                             hipStream_t stream);
-// scales: M*K/16 block scale bytes plus the 16-byte tail (nv4_act_tail)
+// scales: M*K/16 block scale bytes plus the tail (nv4_act_tail, kNvTailBytes + kNvPartialBytes)
 hipError_t launch_quant_nv4(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
                             hipStream_t stream);
-// Largest bf16 magnitude (bit pattern) of x [R][ld] (first `cols` columns), merged into
-// *slot with an atomic maximum; the slot must hold 0 (or a smaller maximum) before.
-hipError_t launch_amax_bf16(const uint16_t* x, int R, int cols, int ld, uint32_t* slot, hipStream_t stream);
+// Largest bf16 magnitude (bit pattern) of x [R][ld] (first `cols` columns), written to
+// *slot; `partial` is work space for kAmaxBlocks u32 (the per-workgroup maxima).
+hipError_t launch_amax_bf16(const uint16_t* x, int R, int cols, int ld, uint32_t* slot, uint32_t* partial,
+                            hipStream_t stream);
 hipError_t launch_pack(int fmt, int epi, const uint16_t* w, int N, int K, int ldw, uint8_t* blob,
                        hipStream_t stream);
 // Fused GEMM + epilogue in any format.  a_scales: FP4 / MXFP8 E8M0 bytes, FP8 fp32

@@ -206,9 +206,12 @@ hipError_t launch_pack(int fmt, int epi, const uint16_t* w, int N, int K, int ld
   const int Np = padded_rows(N);
   if (fmt == FMT_NV4) {
     // header + cleared slot, the tensor maximum of W (logical rows; padding rows are
-    // zero), then the codes and scales
+    // zero), then the codes and scales.  The tensor maximum's per-workgroup maxima go
+    // to the start of the code area (at least 8 KB), which the packer then overwrites.
     hipLaunchKernelGGL(nv4_header_kernel, dim3(1), dim3(1), 0, stream, blob, epi, N, K, Np);
-    if (hipError_t e = launch_amax_bf16(w, N, K, ldw, reinterpret_cast<uint32_t*>(blob + kNvAmaxOff), stream))
+    static_assert(kNvPartialBytes <= 64 * 256 / 2, "the smallest code area holds the work space");
+    if (hipError_t e = launch_amax_bf16(w, N, K, ldw, reinterpret_cast<uint32_t*>(blob + kNvAmaxOff),
+                                        reinterpret_cast<uint32_t*>(blob + kHeaderBytes), stream))
       return e;
     const uint32_t total = (uint32_t)Np / 32 * ((uint32_t)K / 64) * 64;
     hipLaunchKernelGGL(pack_nv4_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, w, N, K, ldw, epi, Np,

@@ -12,8 +12,8 @@
 // FP4 scale layout), scales computed per call like the FP4 path's.
 // NVFP4: bf16 [M, K] -> E2M1 codes (the FP4 code layout) + E4M3 block-16 scales + one
 // fp32 tensor scale (the 4-bit format page "How fal made Ideogram V4 6x faster"
-// names, paragraph 2), in three launches: clear the tensor-maximum slot, an atomic
-// tensor maximum, then the quantizer.
+// names, paragraph 2), in three launches: per-workgroup maxima, the tensor maximum,
+// then the quantizer.
 //
 // All kernels are HBM-bound streams: 2 bytes read per element, 0.5 + 1/32 (FP4),
 // 1 (FP8) or 1 + 1/32 (MXFP8) bytes written.  Outputs are K-panel-major
@@ -76,13 +76,23 @@ __global__ __launch_bounds__(256) void quant_mx8_kernel(const uint16_t* __restri
   }
 }
 
-// Tensor maximum: one thread per 8 elements, grid-stride over a few hundred
-// workgroups; each workgroup reduces its 256 lanes (waves, then LDS) and merges its
-// maximum with one global atomic maximum (bf16 magnitude bit patterns order like
-// their values, so the unsigned maximum is the maximum).  One atomic per workgroup
-// keeps the contention on the single slot negligible.
+// Maximum of the 256 lanes' values of a workgroup (waves, then LDS), valid in thread 0.
+__device__ inline uint32_t block_max256(uint32_t m, uint32_t* wave_max) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  return max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+}
+
+// Tensor maximum, in two launches and without atomics: one thread per 8 elements,
+// grid-stride over at most kAmaxBlocks workgroups, each leaving its maximum in
+// partial[workgroup]; then one workgroup reduces those into the slot.  (bf16
+// magnitude bit patterns order like their values, so the unsigned maximum is the
+// maximum.)  Every workgroup merging into the one slot with an atomic maximum
+// measured slower: those atomics are serialised on one address.
 __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int ld, uint32_t total,
-                                                   uint32_t per_row, uint32_t* slot) {
+                                                   uint32_t per_row, uint32_t* partial) {
   __shared__ uint32_t wave_max[4];
   uint32_t m = 0;
   const uint32_t stride = gridDim.x * 256u;
@@ -90,17 +100,18 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
     const uint32_t row = c / per_row, col = c - row * per_row;
     m = max(m, absmax8(*reinterpret_cast<const v4i*>(x + (size_t)row * ld + (size_t)col * 8)));
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    m = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
-    if (m != 0) atomicMax(slot, m);
-  }
+  m = block_max256(m, wave_max);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
-__global__ void clear_slot_kernel(uint32_t* slot) { slot[0] = 0u; }
+__global__ __launch_bounds__(256) void amax_final_kernel(const uint32_t* __restrict__ partial, uint32_t n,
+                                                         uint32_t* slot) {
+  __shared__ uint32_t wave_max[4];
+  uint32_t m = 0;
+  for (uint32_t i = threadIdx.x; i < n; i += 256u) m = max(m, partial[i]);
+  m = block_max256(m, wave_max);
+  if (threadIdx.x == 0) slot[0] = m;
+}
 
 // NVFP4: the FP4 kernel's structure; a block of 16 is one lane pair (DPP xor 1).
 // Chunk `col` (8 elements) goes to the FP4 code position; its block (col/2) scale to
@@ -216,21 +227,21 @@ hipError_t launch_quant_mx8(const uint16_t* x, int M, int K, int ldx, uint8_t* c
   return hipGetLastError();
 }
 
-hipError_t launch_amax_bf16(const uint16_t* x, int R, int cols, int ld, uint32_t* slot, hipStream_t stream) {
+hipError_t launch_amax_bf16(const uint16_t* x, int R, int cols, int ld, uint32_t* slot, uint32_t* partial,
+                            hipStream_t stream) {
   const uint32_t per_row = (uint32_t)cols / 8;
   const uint32_t total = (uint32_t)R * per_row;
   uint32_t blocks = (total + 255) / 256;
-  const uint32_t cap = 512u;                              // two workgroups per CU, grid-stride beyond
-  if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(256), 0, stream, x, ld, total, per_row, slot);
+  if (blocks > kAmaxBlocks) blocks = kAmaxBlocks;         // two workgroups per CU, grid-stride beyond
+  hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(256), 0, stream, x, ld, total, per_row, partial);
+  hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(256), 0, stream, partial, blocks, slot);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_nv4(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
                             hipStream_t stream) {
   uint32_t* slot = reinterpret_cast<uint32_t*>(scales + nv4_act_tail(M, K));
-  hipLaunchKernelGGL(clear_slot_kernel, dim3(1), dim3(1), 0, stream, slot);
-  if (hipError_t e = launch_amax_bf16(x, M, K, ldx, slot, stream)) return e;
+  if (hipError_t e = launch_amax_bf16(x, M, K, ldx, slot, slot + kNvTailBytes / 4, stream)) return e;
   const uint32_t per_row = (uint32_t)K / 8;
   const uint32_t total = (uint32_t)M * per_row;
   uint32_t blocks = (total + 255) / 256;

@@ -28,8 +28,8 @@
  *     DIT_EALIGN       a pointer not 16-byte aligned, or a leading dimension
  *                      smaller than the row width or not a multiple of 8 elements
  *     DIT_EDEVICE      no usable gfx950 device, or a launch error
- * - Outputs must not alias inputs.  Results are bitwise deterministic (no split-K;
- *   the only atomic, the NVFP4 tensor maximum, does not depend on order).  Calls
+ * - Outputs must not alias inputs.  Results are bitwise deterministic (no split-K,
+ *   no atomics).  Calls
  *   on different streams may run concurrently.
  * - Matrices are row-major.  bf16 tensors are given as raw 16-bit patterns.
  */
@@ -109,7 +109,7 @@ size_t dit_packed_weight_bytes(dit_fmt fmt, dit_epi epi, int N, int K);
 
 /* Bytes of the activation codes / scales written by dit_quantize_act.
  * FP4: codes M*K/2, scales M*K/32.  FP8: codes M*K, scales 4*M.  MXFP8: codes M*K,
- * scales M*K/32.  NVFP4: codes M*K/2, scales M*K/16 + 16. */
+ * scales M*K/32.  NVFP4: codes M*K/2, scales M*K/16 + 16 + 2048. */
 size_t dit_act_code_bytes(dit_fmt fmt, int M, int K);
 size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
 
@@ -201,8 +201,9 @@ dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N,
  *   magnitude 0 where s_b = 0.
  *   Codes in the FP4 layout.  Scales: byte (s*M + m)*8 + (k%128)/16, s = k / 128,
  *   then a 16-byte tail at byte M*K/16: u32 work space, then the fp32 tensor scale
- *   s_t.  Three kernel launches (the tensor maximum is a grid-wide reduction);
- *   the scales buffer must be 16-byte aligned.
+ *   s_t, then 2048 bytes of work space (per-workgroup maxima).  Three kernel
+ *   launches (the tensor maximum is a grid-wide reduction, in two launches); the
+ *   scales buffer must be 16-byte aligned.
  *
  * Supported: K % 256 == 0, ldx >= K, ldx % 8 == 0, pointers 16-byte aligned
  * (FP4 and MXFP8 scales: any alignment).  x must be finite. */

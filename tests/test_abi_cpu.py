@@ -53,7 +53,7 @@ def test_size_queries():
     assert ditq.dit_act_scale_bytes(3, 4608, 3072) == 4608 * 96
     assert ditq.dit_packed_weight_bytes(4, 0, 64, 256) == 256 + 256 * 128 + 256 * 16   # NVFP4
     assert ditq.dit_act_code_bytes(4, 64, 256) == 64 * 128
-    assert ditq.dit_act_scale_bytes(4, 64, 256) == 64 * 16 + 16          # + the tensor-scale tail
+    assert ditq.dit_act_scale_bytes(4, 64, 256) == 64 * 16 + 16 + 2048   # + the tensor-scale tail and work space
     assert ditq.dit_packed_weight_bytes(5, 0, 64, 256) == 0          # no such format
     assert ditq.dit_act_code_bytes(5, 64, 256) == 0
     assert ditq.dit_act_code_bytes(1, 0, 256) == 0

@@ -5,7 +5,7 @@ replayed several times, with eager work and synchronisations between the
 replays and new activations copied into the static input before some of them.
 Every replay must equal the eager result on the same input bit for bit (the
 path is deterministic).  NVFP4 is included: its quantizer's three launches
-(clear the tensor-maximum slot with a kernel, the atomic tensor maximum, the
+(per-workgroup maxima, their reduction into the tensor-maximum slot, the
 quantizer) must all be replayed, or a stale maximum would change the scales.
 """
 import numpy as np
