@@ -462,7 +462,55 @@ def time_other_configs(ditq, torch, args):
         }
         del keep, flush, blob, x, codes, scales, o
         torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            # the oracle on the host cores, for the same format and epilogue (the
+            # default run times it on the headline workload only)
+            out[key]["cpu_baseline"] = oracle_rate(d, fmt_name, epi_name, args.cpu_budget / 4)
+        print(f"other config {key} done", file=sys.stderr, flush=True)
     return out
+
+
+def oracle_rate(d, fmt: str, epi: str, budget_s: float):
+    """The CPU oracle on a bounded row sample of one of the other workloads, the same
+    way as cpu_baseline: the weights quantized and decoded once beforehand, then
+    activation quantize + decode + float64 GEMM + the epilogue on as many token rows
+    as fit about budget_s / 3 seconds, repeated to about budget_s, median reported."""
+    import numpy as np
+    from oracle import epilogue, quant
+    q = {"fp4": quant.quantize_fp4, "fp8": quant.quantize_fp8, "mx8": quant.quantize_mx8,
+         "nv4": quant.quantize_nv4}[fmt]
+    dq = {"fp4": quant.dequantize_fp4, "fp8": quant.dequantize_fp8, "mx8": quant.dequantize_mx8,
+          "nv4": quant.dequantize_nv4}[fmt]
+    M, K = d["x"].shape
+    N = d["w"].shape[0]
+    WdT = np.ascontiguousarray(dq(*q(d["w"])).T)
+    kw = {}
+    if epi == "qk_rmsnorm":
+        kw = dict(n_heads=d["n_heads"], head_dim=d["head_dim"], gamma_q=d["gamma_q"], gamma_k=d["gamma_k"],
+                  eps=d["eps"])
+
+    def run(rows):
+        acc = dq(*q(d["x"][:rows])) @ WdT
+        if epi == "gate_residual":
+            return epilogue.apply(epi, acc, residual=d["residual"], gate=d["gate"],
+                                  rows_per_gate=d["rows_per_gate"], row_ids=np.arange(rows))
+        return epilogue.apply(epi, acc, **kw)
+
+    t = time.perf_counter()
+    run(64)
+    dt = time.perf_counter() - t
+    rows = max(64, int(min(M, max(64, 64 * (budget_s / 3) / max(dt, 1e-3)))) // 64 * 64)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - t_start < budget_s and len(times) < 50):
+        t = time.perf_counter()
+        run(rows)
+        times.append(time.perf_counter() - t)
+    times.sort()
+    med = times[len(times) // 2]
+    return {"value": round(2.0 * rows * N * K / med / 1e12, 4), "unit": "TFLOP/s",
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{rows} of {M} token rows; median of {len(times)} repetitions, {med:.2f} s each"}
 
 
 def cpu_baseline(d, budget_s: float):
