@@ -1095,10 +1095,12 @@ hipError_t launch(Params& p, hipStream_t stream) {
 // Token-tile height: on the 4 x 1 grid always 192 (TM = 6; at 256 tokens its 256
 // accumulators leave too few registers, and the spilling kernel measured 5-8 %
 // slower even where it saves a round of tiles: M = 2048 and 4096 with N = 16384).
-// On the 2 x 2 grid 192 or 256 (TM = 3 or 4 per wave), whichever gives the fewest
-// rounds of tiles over the CUs, weighted by the tile's work plus a fixed cost of
-// about half a token tile (FP8 and MXFP8 always 192: with 256 their operand
-// registers spill).  FP4 weight ring of 8 units when the k-steps come in groups of
+// On the 2 x 2 grid 192 or 256 (TM = 3 or 4 per wave), whichever takes less time:
+// rounds of tiles over the CUs times the time of one tile, a 256-token tile taking
+// 1.35x a 192-token one (measured 1.34-1.37x: QK-RMSNorm head_dim 128, 4 against 3
+// rounds, 100.1 against 102.9 us; head_dim 256, 5 against 3 rounds, 154.5 against
+// 125.7 us; the gated residual, 3 against 2 rounds, 232.9 against 207.8 us).  FP8
+// and MXFP8 always take 192: with 256 their operand registers spill.  FP4 weight ring of 8 units when the k-steps come in groups of
 // 4, else 4 (FP8 and MXFP8: 4).
 template <int FMT, int EPI, int HD = 0, int WLDS = wlds_for(FMT)>
 hipError_t launch_cfg(Params& p, hipStream_t stream) {
@@ -1126,7 +1128,7 @@ hipError_t launch_cfg(Params& p, hipStream_t stream) {
       const int cus = cu_count();
       const long tn = padded_rows(p.N) / 256;
       const long r3 = ((p.M + 191) / 192 * tn + cus - 1) / cus, r4 = ((p.M + 255) / 256 * tn + cus - 1) / cus;
-      const bool tm3 = r3 * 7 < r4 * 9;
+      const bool tm3 = r3 * 20 < r4 * 27;
       if (nks % 4 != 0) {
         if (tm3) return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
         return launch<Tile<FMT, EPI, 4, 4, WLDS, HD>>(p, stream);
