@@ -21,7 +21,8 @@ __all__ = [
     "dit_gemm_epilogue", "dit_gemm_gate_residual", "gemm_gate_residual",
     "dit_gated_silu_bf16", "dit_mfma_fp4_probe", "gated_silu", "mfma_fp4_probe",
     "dit_status_str", "dit_last_error", "pack_weights", "quantize_act", "gemm", "gemm_q4out", "linear",
-    "library_path", "EXPORTED",
+    "library_path", "EXPORTED", "BLOB_MAGIC", "BLOB_VERSION", "blob_header", "check_blob", "save_packed",
+    "load_packed",
 ]
 
 FMT_FP4 = 1
@@ -189,6 +190,73 @@ def pack_weights(w, fmt: int, epi: int):
     blob = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
     dit_pack_weights(fmt, epi, w.data_ptr(), N, K, _ld(w), blob.data_ptr(), _stream())
     return blob
+
+
+BLOB_MAGIC = 0x51544944          # "DITQ", the first u32 of a packed blob
+BLOB_VERSION = 2
+_HEADER_FIELDS = ("magic", "version", "fmt", "epi", "N", "K", "Np")
+
+
+def blob_header(data) -> dict:
+    """The header fields of a packed blob (the layout in include/ditq.h): magic,
+    version, fmt, epi, N, K, Np and the total byte count.  `data` is the blob as a
+    torch uint8 tensor (device or host) or as bytes / a NumPy uint8 array; only its
+    first 64 bytes are read (copied to the host)."""
+    import numpy as np
+    if hasattr(data, "cpu"):
+        data = data[:64].cpu().numpy()
+    h = np.frombuffer(bytes(memoryview(np.ascontiguousarray(data[:64], dtype=np.uint8))), dtype=np.uint8)
+    if h.size < 64:
+        raise ValueError("packed blob shorter than its header")
+    u32 = h[:28].view("<u4")
+    out = {k: int(v) for k, v in zip(_HEADER_FIELDS, u32)}
+    out["bytes"] = int(h[48:56].view("<u8")[0])
+    return out
+
+
+def check_blob(data, fmt=None, epi=None, N=None, K=None, nbytes=None) -> dict:
+    """Validate a packed blob's header against the call it is meant for; returns the
+    header.  Raises ValueError on a foreign or truncated blob, another layout version,
+    or a format / shape / row order that does not match.  Blobs packed for
+    gated-SiLU have their own row order; all other epilogues share one."""
+    hdr = blob_header(data)
+    if hdr["magic"] != BLOB_MAGIC:
+        raise ValueError(f"not a packed weight blob (magic {hdr['magic']:#x})")
+    if hdr["version"] != BLOB_VERSION:
+        raise ValueError(f"blob layout version {hdr['version']}, this library writes {BLOB_VERSION}")
+    if dit_packed_weight_bytes(hdr["fmt"], hdr["epi"], hdr["N"], hdr["K"]) != hdr["bytes"]:
+        raise ValueError("blob header is inconsistent (byte count)")
+    if nbytes is not None and nbytes < hdr["bytes"]:
+        raise ValueError(f"blob truncated: {nbytes} of {hdr['bytes']} bytes")
+    if fmt is not None and hdr["fmt"] != fmt:
+        raise ValueError(f"blob packed for format {hdr['fmt']}, not {fmt}")
+    if epi is not None and (hdr["epi"] == EPI_GATED_SILU) != (epi == EPI_GATED_SILU):
+        raise ValueError(f"blob packed for epilogue {hdr['epi']}: row order differs from epilogue {epi}")
+    if N is not None and hdr["N"] != N:
+        raise ValueError(f"blob packed for N = {hdr['N']}, not {N}")
+    if K is not None and hdr["K"] != K:
+        raise ValueError(f"blob packed for K = {hdr['K']}, not {K}")
+    return hdr
+
+
+def save_packed(blob, path) -> dict:
+    """Write a packed blob (device tensor) to a file, after checking its header."""
+    import numpy as np
+    host = blob.cpu().numpy()
+    hdr = check_blob(host, nbytes=host.size)
+    np.ascontiguousarray(host[:hdr["bytes"]], dtype=np.uint8).tofile(path)
+    return hdr
+
+
+def load_packed(path, fmt=None, epi=None, N=None, K=None, device="cuda"):
+    """Read a blob written by save_packed and check its header against the expected
+    format, epilogue row order and shape before it is uploaded; returns a uint8
+    tensor on `device`."""
+    import numpy as np
+    import torch
+    data = np.fromfile(path, dtype=np.uint8)
+    check_blob(data, fmt, epi, N, K, nbytes=data.size)
+    return torch.from_numpy(data).to(device)
 
 
 def quantize_act(x, fmt: int):

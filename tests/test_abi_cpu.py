@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -238,3 +239,45 @@ def test_measurement_entry_points_validation():
     if not _has_gpu():
         assert gs(A, 64, 512, 512, D, 256, None) == EDEVICE
         assert pr(256, 100, A, None) == EDEVICE
+
+
+def _blob_bytes(fmt, epi, N, K):
+    """A blob of the documented size with a header as the packer writes it (the
+    payload is zero: these tests only exercise the header checks)."""
+    nbytes = ditq.dit_packed_weight_bytes(fmt, epi, N, K)
+    Np = (N + 255) // 256 * 256
+    b = np.zeros(nbytes, dtype=np.uint8)
+    b[:28].view("<u4")[:] = [0x51544944, 2, fmt, epi, N, K, Np]
+    b[32:56].view("<u8")[:] = [256, 256 + Np * K // 2, nbytes]
+    return b
+
+
+def test_packed_blob_save_load_header_checks(tmp_path):
+    b = _blob_bytes(1, 1, 512, 256)
+    hdr = ditq.check_blob(b, 1, 1, 512, 256, nbytes=b.size)
+    assert (hdr["fmt"], hdr["epi"], hdr["N"], hdr["K"], hdr["Np"]) == (1, 1, 512, 256, 512)
+    path = tmp_path / "w.ditq"
+    b.tofile(path)
+    t = ditq.load_packed(path, fmt=1, epi=1, N=512, K=256, device="cpu")
+    assert t.numel() == b.size and (t.numpy() == b).all()
+    # a blob packed for identity serves every epilogue but gated-SiLU (same row order)
+    c = _blob_bytes(1, 0, 512, 256)
+    ditq.check_blob(c, 1, 3, 512, 256)
+    bad = {"magic": (0, 0xDEADBEEF), "version": (1, 1)}
+    for name, (i, v) in bad.items():
+        x = b.copy()
+        x[:28].view("<u4")[i] = v
+        with pytest.raises(ValueError, match=name):
+            ditq.check_blob(x)
+    for kw, msg in [(dict(fmt=2), "format"), (dict(epi=0), "row order"), (dict(N=256), "N ="), (dict(K=512), "K =")]:
+        with pytest.raises(ValueError, match=msg):
+            ditq.check_blob(b, **kw)
+    with pytest.raises(ValueError, match="row order"):
+        ditq.check_blob(c, epi=1)
+    b[:-1].tofile(tmp_path / "short.ditq")
+    with pytest.raises(ValueError, match="truncated"):
+        ditq.load_packed(tmp_path / "short.ditq", device="cpu")
+    x = b.copy()
+    x[48:56].view("<u8")[0] = 1234
+    with pytest.raises(ValueError, match="inconsistent"):
+        ditq.check_blob(x)

@@ -112,3 +112,27 @@ def test_nv4_pack_bitexact(ditq, N, K, epi):
     np.testing.assert_array_equal(s, rs)
     np.testing.assert_array_equal(c, rc)
     assert not pad["codes"].any() and not pad["scales"].any()
+
+
+@pytest.mark.parametrize("fmt_name,epi_name", [("fp4", "gated_silu"), ("nv4", "identity")])
+def test_saved_blob_reloads_to_the_same_layer(ditq, tmp_path, fmt_name, epi_name):
+    """pack -> save_packed -> load_packed (header checked) gives a blob that yields the
+    same GEMM output, bit for bit, as the blob it was saved from."""
+    import torch
+    from tests.gpu_util import to_dev_bf16
+    fmt = {"fp4": ditq.FMT_FP4, "nv4": ditq.FMT_NV4}[fmt_name]
+    epi = {"gated_silu": ditq.EPI_GATED_SILU, "identity": ditq.EPI_IDENTITY}[epi_name]
+    d = make_inputs("tiny_gated_silu", seed=9, M=200, N=512, K=512)
+    x, w = to_dev_bf16(d["x"]), to_dev_bf16(d["w"])
+    blob = ditq.pack_weights(w, fmt, epi)
+    path = tmp_path / "w.ditq"
+    hdr = ditq.save_packed(blob, path)
+    assert (hdr["fmt"], hdr["epi"], hdr["N"], hdr["K"]) == (fmt, epi, 512, 512)
+    blob2 = ditq.load_packed(path, fmt=fmt, epi=epi, N=512, K=512)
+    assert torch.equal(blob.cpu(), blob2.cpu())
+    y1 = ditq.linear(x, blob, 512, fmt, epi)
+    y2 = ditq.linear(x, blob2, 512, fmt, epi)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    with pytest.raises(ValueError):
+        ditq.load_packed(path, fmt=fmt, epi=ditq.EPI_GATED_SILU if epi != ditq.EPI_GATED_SILU else ditq.EPI_IDENTITY)
