@@ -224,8 +224,10 @@ def check_blob(data, fmt=None, epi=None, N=None, K=None, nbytes=None) -> dict:
         raise ValueError(f"not a packed weight blob (magic {hdr['magic']:#x})")
     if hdr["version"] != BLOB_VERSION:
         raise ValueError(f"blob layout version {hdr['version']}, this library writes {BLOB_VERSION}")
-    if dit_packed_weight_bytes(hdr["fmt"], hdr["epi"], hdr["N"], hdr["K"]) != hdr["bytes"]:
-        raise ValueError("blob header is inconsistent (byte count)")
+    fields_ok = all(0 < hdr[k] < 2 ** 31 for k in ("fmt", "N", "K")) and 0 <= hdr["epi"] < 2 ** 31
+    expected = dit_packed_weight_bytes(hdr["fmt"], hdr["epi"], hdr["N"], hdr["K"]) if fields_ok else 0
+    if expected == 0 or expected != hdr["bytes"]:
+        raise ValueError("blob header is inconsistent (format, shape or byte count)")
     if nbytes is not None and nbytes < hdr["bytes"]:
         raise ValueError(f"blob truncated: {nbytes} of {hdr['bytes']} bytes")
     if fmt is not None and hdr["fmt"] != fmt:

@@ -281,3 +281,10 @@ def test_packed_blob_save_load_header_checks(tmp_path):
     x[48:56].view("<u8")[0] = 1234
     with pytest.raises(ValueError, match="inconsistent"):
         ditq.check_blob(x)
+    # fields no packer writes: an unknown format, an impossible shape, an empty blob
+    for i, v in [(2, 99), (4, 0xFFFFFFFF), (5, 0x80000000), (4, 0)]:
+        x = b.copy()
+        x[:28].view("<u4")[i] = v
+        x[48:56].view("<u8")[0] = 0
+        with pytest.raises(ValueError, match="inconsistent"):
+            ditq.check_blob(x)
