@@ -108,7 +108,9 @@ def _run_fp8(ditq, bits, ldx=None):
     return act_codes_to_rowmajor(codes.cpu().numpy(), M, K, 2), scales.cpu().numpy()
 
 
-@pytest.mark.parametrize("M,K,ldx", [(1, 256, 256), (77, 3072, 3080), (33, 8448, 8448), (5, 768, 768)])
+# the row cache: 16 register slots up to K = 8192 (including its edges), none beyond (rows read twice)
+@pytest.mark.parametrize("M,K,ldx", [(1, 256, 256), (77, 3072, 3080), (33, 8448, 8448), (5, 768, 768),
+                                     (9, 4096, 4104), (5, 4352, 4352), (3, 8192, 8192)])
 def test_fp8_quantizer_bitexact(ditq, M, K, ldx):
     rng = np.random.default_rng(M + K)
     x = rng.standard_normal((M, K)).astype(np.float32) * (2.0 ** rng.integers(-30, 30, (M, 1))).astype(np.float32)
