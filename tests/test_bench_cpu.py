@@ -42,3 +42,17 @@ def test_source_hash_covers_the_gemm_sources(tmp_path, monkeypatch):
     h0 = bench.kernel_source_hash()
     src.write_text(src.read_text() + "\n// changed\n")
     assert bench.kernel_source_hash() != h0
+
+
+def test_oracle_rate_runs_for_every_format_and_epilogue():
+    """bench.py --all-configs times the oracle beside each workload; every format and
+    epilogue it uses must run on a small problem of the same kind."""
+    from workloads import make_inputs
+    cases = [("tiny_gated_silu", "fp4", "gated_silu", {}), ("qkv_rmsnorm_hd128", "fp8", "qk_rmsnorm",
+             dict(M=64, n_heads=1)), ("mlp_gelu_tanh", "mx8", "gelu_tanh", dict(M=64, N=256, K=256)),
+             ("mlp_down_gate_residual", "fp4", "gate_residual", dict(M=64, N=256, K=256, rows_per_gate=32)),
+             ("tiny_gated_silu", "nv4", "identity", {})]
+    for name, fmt, epi, kw in cases:
+        d = make_inputs(name, seed=1, **kw)
+        r = bench.oracle_rate(d, fmt, epi, 0.05)
+        assert r["value"] > 0 and r["kind"] == "oracle" and r["unit"] == "TFLOP/s", (name, fmt, epi, r)
