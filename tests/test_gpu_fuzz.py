@@ -12,7 +12,8 @@ Each case is drawn from one seeded generator:
 Every element is compared with the oracle, guard bytes around the output and its
 padding must stay untouched, and the residual must only be read.  The fixed cases
 of test_gpu_gemm.py pin chosen shapes; these cover the combinations in between.
-The environment variable DITQ_FUZZ_CASES sets a longer list for a soak run.
+The environment variables DITQ_FUZZ_CASES and DITQ_FUZZ_SEED set a longer or another list
+for a soak run.
 """
 import os
 
@@ -54,8 +55,9 @@ def _cases(n=200, seed=2024):
     return out
 
 
-# DITQ_FUZZ_CASES draws a longer list (the first 200 cases are always the same)
-CASES = _cases(int(os.environ.get("DITQ_FUZZ_CASES", "200")))
+# DITQ_FUZZ_CASES draws a longer list (the first 200 cases are always the same);
+# DITQ_FUZZ_SEED draws another list
+CASES = _cases(int(os.environ.get("DITQ_FUZZ_CASES", "200")), int(os.environ.get("DITQ_FUZZ_SEED", "2024")))
 
 
 @pytest.fixture(scope="module")
