@@ -33,12 +33,14 @@ bool valid_epi(int e) {
          e == DIT_EPI_GATE_RESIDUAL;
 }
 
-// Shapes the kernels implement.  K: whole 256-element k-steps (FP4 scale groups);
+// Shapes the kernels implement.  K: whole 128-element k-steps (one 128-byte FP4
+// scale record per 32 weight rows, one 64-byte activation panel row per token);
 // N: whole 64-row weight groups (128 for gated-SiLU so each 64-row packed group
-// holds 32 gate/up pairs).  Byte counts stay below 2^32 so that 32-bit buffer
-// offsets cover every tensor (plus one tile of ragged rows).
+// holds 32 gate/up pairs).  Byte counts stay below 2^31 so that 32-bit buffer
+// offsets cover every tensor plus one tile of ragged rows, and the k-steps the
+// GEMM pads K with (at most three, reading zeros past the end).
 bool shape_ok(int fmt, int epi, int N, int K) {
-  if (K % 256 != 0 || N % 64 != 0) return false;
+  if (K % 128 != 0 || N % 64 != 0) return false;
   if (epi == DIT_EPI_GATED_SILU && N % 128 != 0) return false;
   const size_t Np = (size_t)ditq::padded_rows(N);
   const size_t code_bytes = ditq::is_fp4_codes(fmt) ? Np * K / 2 : Np * K;
@@ -92,12 +94,12 @@ size_t dit_packed_weight_bytes(dit_fmt fmt, dit_epi epi, int N, int K) {
 }
 
 size_t dit_act_code_bytes(dit_fmt fmt, int M, int K) {
-  if (!valid_fmt(fmt) || M <= 0 || K <= 0 || K % 256 != 0) return 0;
+  if (!valid_fmt(fmt) || M <= 0 || K <= 0 || K % 128 != 0) return 0;
   return ditq::is_fp4_codes(fmt) ? (size_t)M * K / 2 : (size_t)M * K;
 }
 
 size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K) {
-  if (!valid_fmt(fmt) || M <= 0 || K <= 0 || K % 256 != 0) return 0;
+  if (!valid_fmt(fmt) || M <= 0 || K <= 0 || K % 128 != 0) return 0;
   if (fmt == DIT_FMT_FP8_E4M3_ROWCOL) return (size_t)M * 4;
   if (fmt == DIT_FMT_FP4_E2M1_NV16) return ditq::nv4_act_tail(M, K) + ditq::kNvTailBytes + ditq::kNvPartialBytes;
   return (size_t)M * K / 32;
@@ -117,7 +119,7 @@ dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N,
 dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int ldx, void* codes, void* scales,
                             void* stream) {
   if (!valid_fmt(fmt) || !x_bf16 || !codes || !scales || M <= 0 || K <= 0) return DIT_EINVAL;
-  if (K % 256 != 0 || !rows_ok(fmt, M, K)) return DIT_EUNSUPPORTED;
+  if (K % 128 != 0 || !rows_ok(fmt, M, K)) return DIT_EUNSUPPORTED;
   if (!aligned16(x_bf16) || !aligned16(codes) || ldx < K || ldx % 8 != 0) return DIT_EALIGN;
   if (fmt == DIT_FMT_FP8_E4M3_ROWCOL && !aligned(scales, 4)) return DIT_EALIGN;
   if (fmt == DIT_FMT_FP4_E2M1_NV16 && !aligned16(scales)) return DIT_EALIGN;
@@ -143,21 +145,23 @@ namespace {
 // quantization of the output is written too (FP4 only), and out_bf16 may be null.
 dit_status gemm_any(int fmt, const void* a_codes, const void* a_scales, const void* w_packed, int M, int N, int K,
                     dit_epi epi, const dit_rmsnorm_params* rms, const dit_gate_residual_params* gr,
-                    void* out_bf16, int ldo, void* out_codes, void* out_scales, void* stream) {
+                    void* out_bf16, int ldo, void* out_codes, void* out_scales, float* out_f32, void* stream) {
   const bool quantized = out_codes != nullptr;
   if (!valid_fmt(fmt) || !a_codes || !a_scales || !w_packed || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi))
     return DIT_EINVAL;
-  if (!quantized && !out_bf16) return DIT_EINVAL;
+  if (!quantized && !out_bf16 && !out_f32) return DIT_EINVAL;
   if (quantized && !out_scales) return DIT_EINVAL;
   if ((epi == DIT_EPI_QK_RMSNORM) != (rms != nullptr)) return DIT_EINVAL;
   if ((epi == DIT_EPI_GATE_RESIDUAL) != (gr != nullptr)) return DIT_EINVAL;
   if (gr) {
-    if (!gr->residual || !gr->gate || gr->rows_per_gate <= 0 || !out_bf16) return DIT_EINVAL;
-    // the residual may be the output itself (an in-place update), but no other overlap
-    const uintptr_t r0 = reinterpret_cast<uintptr_t>(gr->residual), o0 = reinterpret_cast<uintptr_t>(out_bf16);
+    if (!gr->residual || !gr->gate || gr->rows_per_gate <= 0 || !(out_bf16 || out_f32)) return DIT_EINVAL;
+    // the residual may be the bf16 output itself (an in-place update), but no other overlap
+    const size_t esz = out_f32 ? 4 : 2;
+    const uintptr_t r0 = reinterpret_cast<uintptr_t>(gr->residual);
+    const uintptr_t o0 = reinterpret_cast<uintptr_t>(out_f32 ? static_cast<void*>(out_f32) : out_bf16);
     const uintptr_t r1 = r0 + 2 * ((size_t)(M - 1) * (size_t)gr->ldr + N);
-    const uintptr_t o1 = o0 + 2 * ((size_t)(M - 1) * (size_t)ldo + N);
-    const bool same = r0 == o0 && gr->ldr == ldo;
+    const uintptr_t o1 = o0 + esz * ((size_t)(M - 1) * (size_t)ldo + N);
+    const bool same = !out_f32 && r0 == o0 && gr->ldr == ldo;
     if (!same && r0 < o1 && o0 < r1) return DIT_EINVAL;
   }
   if (rms) {
@@ -172,6 +176,7 @@ dit_status gemm_any(int fmt, const void* a_codes, const void* a_scales, const vo
   if (!aligned16(a_codes) || !aligned16(w_packed)) return DIT_EALIGN;
   if (fmt == FMT_FP8 ? !aligned(a_scales, 4) : !aligned16(a_scales)) return DIT_EALIGN;
   if (out_bf16 && (!aligned16(out_bf16) || ldo < width || ldo % 8 != 0)) return DIT_EALIGN;
+  if (out_f32 && (!aligned16(out_f32) || ldo < width || ldo % 4 != 0)) return DIT_EALIGN;
   if (quantized && (!aligned16(out_codes) || !aligned16(out_scales))) return DIT_EALIGN;
   if (rms && (!aligned16(rms->gamma_q) || !aligned16(rms->gamma_k))) return DIT_EALIGN;
   if (gr && (!aligned16(gr->residual) || !aligned16(gr->gate) || gr->ldr < N || gr->ldr % 8 != 0))
@@ -185,7 +190,7 @@ dit_status gemm_any(int fmt, const void* a_codes, const void* a_scales, const vo
   return launched(ditq::launch_gemm(fmt, static_cast<const uint8_t*>(a_codes), a_scales,
                                     static_cast<const uint8_t*>(w_packed), M, N, K, epi, rms ? &r : nullptr,
                                     gr ? &g : nullptr, static_cast<uint16_t*>(out_bf16), ldo,
-                                    static_cast<uint8_t*>(out_codes), static_cast<uint8_t*>(out_scales),
+                                    static_cast<uint8_t*>(out_codes), static_cast<uint8_t*>(out_scales), out_f32,
                                     static_cast<hipStream_t>(stream)));
 }
 }  // namespace
@@ -195,7 +200,7 @@ dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const
                                 void* stream) {
   if (!out_bf16) return DIT_EINVAL;
   return gemm_any(FMT_FP4, a_codes, a_scales, w_packed, M, N, K, epi, rms, nullptr, out_bf16, ldo, nullptr,
-                  nullptr, stream);
+                  nullptr, nullptr, stream);
 }
 
 dit_status dit_gemm_q4_epilogue_q4(const void* a_codes, const void* a_scales, const void* w_packed, int M, int N,
@@ -203,7 +208,7 @@ dit_status dit_gemm_q4_epilogue_q4(const void* a_codes, const void* a_scales, co
                                    void* out_codes, void* out_scales, void* stream) {
   if (!out_codes || !out_scales) return DIT_EINVAL;
   return gemm_any(FMT_FP4, a_codes, a_scales, w_packed, M, N, K, epi, rms, nullptr, out_bf16, ldo, out_codes,
-                  out_scales, stream);
+                  out_scales, nullptr, stream);
 }
 
 dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, const void* w_packed, int M, int N,
@@ -213,7 +218,7 @@ dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, cons
   // no parameters for RMSNorm or the gated residual here
   if (epi == DIT_EPI_QK_RMSNORM || epi == DIT_EPI_GATE_RESIDUAL) return DIT_EUNSUPPORTED;
   return gemm_any(FMT_FP8, a_codes, a_scales, w_packed, M, N, K, epi, nullptr, nullptr, out_bf16, ldo, nullptr,
-                  nullptr, stream);
+                  nullptr, nullptr, stream);
 }
 
 dit_status dit_gemm_epilogue(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed, int M,
@@ -221,7 +226,7 @@ dit_status dit_gemm_epilogue(dit_fmt fmt, const void* a_codes, const void* a_sca
                              void* stream) {
   if (!out_bf16) return DIT_EINVAL;
   return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, nullptr, out_bf16, ldo, nullptr, nullptr,
-                  stream);
+                  nullptr, stream);
 }
 
 dit_status dit_gemm_gate_residual(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed,
@@ -229,7 +234,15 @@ dit_status dit_gemm_gate_residual(dit_fmt fmt, const void* a_codes, const void* 
                                   void* stream) {
   if (!gr || !out_bf16) return DIT_EINVAL;
   return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, DIT_EPI_GATE_RESIDUAL, nullptr, gr, out_bf16, ldo,
-                  nullptr, nullptr, stream);
+                  nullptr, nullptr, nullptr, stream);
+}
+
+dit_status dit_gemm_epilogue_f32(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed, int M,
+                                 int N, int K, dit_epi epi, const dit_rmsnorm_params* rms,
+                                 const dit_gate_residual_params* gr, float* out_f32, int ldo, void* stream) {
+  if (!out_f32) return DIT_EINVAL;
+  return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, gr, nullptr, ldo, nullptr, nullptr, out_f32,
+                  stream);
 }
 
 dit_status dit_gated_silu_bf16(const void* c_bf16, int M, int N, int ldc, void* out_bf16, int ldo,

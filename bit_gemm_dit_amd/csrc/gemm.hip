@@ -172,6 +172,7 @@ struct Params {
   const uint8_t* w_codes;     // blob + header
   const void* w_scales;       // FP4 / MXFP8: E8M0 records; FP8: f32 [Np]
   uint16_t* out;              // bf16 output, or null when only the quantized output is wanted
+  float* out_f32;             // debug: the fp32 values the bf16 store would round, instead of it (or null)
   uint8_t* q_codes;           // FP4 quantization of the output for the next GEMM, or null
   uint8_t* q_scales;
   int M, N, K, ldo;
@@ -226,6 +227,18 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 template <class T>
 __device__ inline void store_tile(const Params& p, int row, bool row_ok, int col0, int ncols, int h,
                                   const float* v) {
+  if (p.out_f32 != nullptr) {
+    // debug store: the lane's four runs of 4 columns (8g + 4h) as fp32, no rounding
+    if (row_ok) {
+      float* o = p.out_f32 + (size_t)row * p.ldo;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = col0 + 8 * g + 4 * h;
+        if (c < ncols) *reinterpret_cast<v4f*>(o + c) = v4f{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+      }
+    }
+    return;
+  }
   uint32_t g[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -562,15 +575,22 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
           if constexpr (T::EPI == EPI_GATE_RESIDUAL) {
             // this lane's 16 columns are 4 runs of 4 (n0 + 8g + 4h + i): the residual
             // as four 8-byte reads, the gate row of the token's sample as four 16-byte
-            // reads; rows past M read row M - 1 and are not stored
+            // reads.  Rows past M read row M - 1 and runs at or past N (the padded
+            // columns of the last tile; N is a multiple of 64, so a run is wholly in or
+            // out) read nothing: every read stays inside residual[M][ldr] and
+            // gate[ceil(M / rows_per_gate)][N], and neither kind is stored.
             const int rr = ok ? row : p.M - 1;
             const int col = n0w + 32 * tn + 4 * h;
             const uint16_t* rp = p.residual + (size_t)rr * p.ldr + col;
             const float* gp = p.gate + (size_t)(rr / p.rows_per_gate) * p.N + col;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              const uint2 rv = *reinterpret_cast<const uint2*>(rp + 8 * g);
-              const v4f gv = *reinterpret_cast<const v4f*>(gp + 8 * g);
+              uint2 rv = {0u, 0u};
+              v4f gv = {0.0f, 0.0f, 0.0f, 0.0f};
+              if (col + 8 * g < p.N) {
+                rv = *reinterpret_cast<const uint2*>(rp + 8 * g);
+                gv = *reinterpret_cast<const v4f*>(gp + 8 * g);
+              }
               v[4 * g + 0] = __builtin_fmaf(gv[0], v[4 * g + 0], bf16_lo(rv.x));
               v[4 * g + 1] = __builtin_fmaf(gv[1], v[4 * g + 1], bf16_hi(rv.x));
               v[4 * g + 2] = __builtin_fmaf(gv[2], v[4 * g + 2], bf16_lo(rv.y));
@@ -828,7 +848,12 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
     m0 = tmi * T::BM;
   };
 
-  const int nks = p.K / T::KSTEP;
+  // k-steps per tile, rounded up to whole unrolled groups of the weight ring.  The
+  // steps past K add exact zeros: their activation code and scale offsets lie past
+  // the end of those buffers, where raw buffer loads return zeros (the range check
+  // covers voffset + soffset), and E2M1 / E4M3 zeros times any finite weight code
+  // (the rows that follow in the blob, or zeros past its end) are zero.
+  const int nks = (p.K / T::KSTEP + T::STEPS_PER_GROUP - 1) / T::STEPS_PER_GROUP * T::STEPS_PER_GROUP;
   const int units = nks * T::CH;                                  // units per tile
   const uint32_t wgroup = (uint32_t)(p.K / 64) * T::FRAG;         // blob bytes of one 32-row group
   const uint32_t a_panel = (uint32_t)p.M * kRowBytes;            // bytes of one K panel of activation codes
@@ -1164,7 +1189,7 @@ hipError_t launch_epi(Params& p, int epi, const RmsArgs* rms, hipStream_t stream
 
 hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, const uint8_t* blob, int M, int N,
                        int K, int epi, const RmsArgs* rms, const ResidualArgs* gr, uint16_t* out, int ldo,
-                       uint8_t* q_codes, uint8_t* q_scales, hipStream_t stream) {
+                       uint8_t* q_codes, uint8_t* q_scales, float* out_f32, hipStream_t stream) {
   const int Np = padded_rows(N);
   Params p{};
   p.a_codes = a_codes;
@@ -1172,6 +1197,7 @@ hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, co
   p.w_codes = blob + kHeaderBytes;
   p.w_scales = blob + blob_scales_offset(fmt, Np, K);
   p.out = out;
+  p.out_f32 = out_f32;
   p.q_codes = q_codes;
   p.q_scales = q_scales;
   p.M = M;

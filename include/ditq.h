@@ -114,6 +114,11 @@ size_t dit_act_code_bytes(dit_fmt fmt, int M, int K);
 size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
 
 /* ---------------------------------------------------------------- weight packer
+ * The offline half of the layer: the weights are quantized once to the GEMM's
+ * low-bit format and B's columns are permuted at packing time so that the
+ * gate/up pairs of gated-SiLU sit next to each other (page "How fal made Ideogram
+ * V4 6x faster", paragraph 2 for the 4-bit format, paragraph 4 for the
+ * packing-time permutation of B).
  * Quantizes W (bf16 [N, K], row stride ldw elements; torch Linear layout, so
  * row n is output column n) and writes the packed blob (`packed`, at least
  * dit_packed_weight_bytes bytes, 256-byte aligned recommended).  Run once per
@@ -160,7 +165,7 @@ size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K);
  *     fp32 tensor scale is stored in the header at byte 56 (byte 60 is work space
  *     of the packer).
  *
- * Supported: K % 256 == 0; N % 64 == 0 (GATED_SILU: N % 128 == 0); ldw >= K,
+ * Supported: K % 128 == 0; N % 64 == 0 (GATED_SILU: N % 128 == 0); ldw >= K,
  * ldw % 8 == 0; w_bf16 and packed 16-byte aligned.  W must be finite. */
 dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N, int K,
                             int ldw, void* packed, void* stream);
@@ -205,12 +210,17 @@ dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N,
  *   launches (the tensor maximum is a grid-wide reduction, in two launches); the
  *   scales buffer must be 16-byte aligned.
  *
- * Supported: K % 256 == 0, ldx >= K, ldx % 8 == 0, pointers 16-byte aligned
+ * Supported: K % 128 == 0, ldx >= K, ldx % 8 == 0, pointers 16-byte aligned
  * (FP4 and MXFP8 scales: any alignment).  x must be finite. */
 dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int ldx,
                             void* codes, void* scales, void* stream);
 
 /* ---------------------------------------------------------------- fused GEMM + epilogue, FP4
+ * The big GEMM in the 4-bit format, C = A @ B (page "How fal made Ideogram V4 6x
+ * faster", paragraph 4), with the small op that follows it applied to the fp32
+ * accumulator before the one store, so the output makes a single trip to HBM
+ * (same page, paragraphs 2-3: the matmuls in a 4-bit float format, epilogue
+ * fusion of per-head RMSNorm and gated-SiLU).
  * out = epi(A W^T) with A the FP4 activations from dit_quantize_act (a_codes,
  * a_scales in its K-panel-major layout) and W the blob from dit_pack_weights
  * (FP4, packed for the same epi family).  The fp32 accumulator goes through the
@@ -220,7 +230,7 @@ dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int l
  * the struct; the gammas inside are device pointers), with
  * N == 3 * n_heads * head_dim and head_dim in {128, 256}.  DIT_EPI_GATE_RESIDUAL
  * needs its parameters, which dit_gemm_gate_residual takes (here: DIT_EINVAL).
- * Supported: M >= 1 (any), K % 256 == 0, N % 64 == 0 (GATED_SILU: N % 128 == 0),
+ * Supported: M >= 1 (any), K % 128 == 0, N % 64 == 0 (GATED_SILU: N % 128 == 0),
  * ldo >= output width, ldo % 8 == 0, pointers 16-byte aligned. */
 dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const void* w_packed,
                                 int M, int N, int K, dit_epi epi, const dit_rmsnorm_params* rms,
@@ -248,6 +258,10 @@ dit_status dit_gemm_q4_epilogue_q4(const void* a_codes, const void* a_scales, co
                                    void* stream);
 
 /* ---------------------------------------------------------------- fused GEMM + epilogue, FP8
+ * The same fused GEMM in FP8 E4M3, the second precision beside the 4-bit path
+ * (page "WaveSpeedAI X DataCrunch: FLUX real-time image inference on B200",
+ * engine list: BF16/FP8 mixed precision; the epilogues as on page "How fal made
+ * Ideogram V4 6x faster", paragraphs 3-4).
  * out = epi((A W^T) * s_a[m] * s_w[n]) with A the E4M3 codes (K-panel-major) and
  * fp32 row scales [M] from dit_quantize_act, W an FP8 blob.  epi is IDENTITY,
  * GATED_SILU or GELU_TANH (QK_RMSNORM and GATE_RESIDUAL, which need parameters,

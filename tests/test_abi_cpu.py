@@ -45,7 +45,10 @@ def test_size_queries():
     assert ditq.dit_packed_weight_bytes(1, 1, 16384, 3072) == 256 + 16384 * 1536 + 16384 * 96
     assert ditq.dit_packed_weight_bytes(1, 0, 320, 256) == 256 + 512 * 128 + 512 * 8     # rows padded to 512
     assert ditq.dit_packed_weight_bytes(2, 0, 12288, 3072) == 256 + 12288 * 3072 + 12288 * 4
-    assert ditq.dit_packed_weight_bytes(1, 0, 64, 128) == 0          # K % 256
+    assert ditq.dit_packed_weight_bytes(1, 0, 64, 128) == 256 + 256 * 64 + 256 * 4    # K = 128: one k-step
+    assert ditq.dit_packed_weight_bytes(1, 0, 64, 384) == 256 + 256 * 192 + 256 * 12  # K = 3 * 128
+    assert ditq.dit_packed_weight_bytes(1, 0, 64, 192) == 0          # K % 128
+    assert ditq.dit_act_code_bytes(1, 10, 384) == 10 * 192 and ditq.dit_act_code_bytes(1, 10, 320) == 0
     assert ditq.dit_packed_weight_bytes(1, 1, 64, 256) == 0          # gated needs N % 128
     assert ditq.dit_packed_weight_bytes(2, 2, 384, 256) == 256 + 512 * 256 + 512 * 4   # = the identity blob
     assert ditq.dit_packed_weight_bytes(3, 0, 64, 256) == 256 + 256 * 256 + 256 * 8    # MXFP8
@@ -80,7 +83,7 @@ def test_gemm_q4_validation():
     assert _q4(epi=2, rms=r, N=512) == EINVAL                        # N != 3 H D
     assert _q4(epi=2, rms=ditq.RmsNormParams(128, 1, A, B, 0.0), N=384, ldo=384) == EINVAL   # eps <= 0
     assert _q4(epi=2, rms=ditq.RmsNormParams(64, 2, A, B, 1e-6), N=384, ldo=384) == EUNSUP   # head_dim 64
-    assert _q4(K=128) == EUNSUP
+    assert _q4(K=192) == EUNSUP                                      # K % 128
     assert _q4(N=576) == EUNSUP                                      # gated needs N % 128
     assert _q4(out=D + 8) == EALIGN
     assert _q4(ldo=255) == EALIGN                                    # < output width 256
@@ -90,6 +93,8 @@ def test_gemm_q4_validation():
     # every argument valid: the first HIP call reports that no gfx950 device is usable
     if not _has_gpu():
         assert _q4() == EDEVICE
+        assert _q4(K=384) == EDEVICE                                 # K = 3 * 128 is accepted
+        assert _q4(K=128) == EDEVICE
 
 
 E = 0x50000
@@ -126,6 +131,7 @@ def test_other_entry_points_validation():
     assert lib.dit_quantize_act(3, A, 4, 256, 256, None, C, None) == EINVAL
     assert lib.dit_quantize_act(3, A, 4, 256, 256, B + 8, C, None) == EALIGN       # MXFP8 codes need 16 B
     assert lib.dit_quantize_act(1, A, 4, 300, 304, B, C, None) == EUNSUP
+    assert lib.dit_quantize_act(1, A, 4, 192, 192, B, C, None) == EUNSUP          # K % 128
     assert lib.dit_quantize_act(1, A, 4, 256, 250, B, C, None) == EALIGN
     assert lib.dit_quantize_act(1, A + 2, 4, 256, 256, B, C, None) == EALIGN
     assert lib.dit_quantize_act(2, A, 4, 256, 256, B, C + 2, None) == EALIGN
@@ -138,6 +144,7 @@ def test_other_entry_points_validation():
     assert lib.dit_gemm_q8_epilogue(A, None, C, 4, 512, 256, 0, D, 512, None) == EINVAL
     if not _has_gpu():
         assert lib.dit_quantize_act(1, A, 4, 256, 256, B, C, None) == EDEVICE
+        assert lib.dit_quantize_act(1, A, 4, 384, 384, B, C, None) == EDEVICE
         assert lib.dit_quantize_act(3, A, 4, 256, 256, B, C + 1, None) == EDEVICE    # MXFP8 scales: any alignment
         assert lib.dit_pack_weights(2, 1, A, 128, 256, 256, B, None) == EDEVICE
         assert lib.dit_pack_weights(2, 2, A, 384, 256, 256, B, None) == EDEVICE      # FP8 for QK-RMSNorm
@@ -167,7 +174,7 @@ def test_gemm_any_format_validation():
     r = ditq.RmsNormParams(128, 1, A, B, 1e-6)
     assert _any(epi=0, rms=r, ldo=512) == EINVAL                     # params without RMSNorm
     assert _any(fmt=2, epi=2, rms=ditq.RmsNormParams(64, 2, A, B, 1e-6), N=384, ldo=384) == EUNSUP
-    assert _any(K=128) == EUNSUP
+    assert _any(K=320) == EUNSUP                                     # K % 128
     assert _any(fmt=2, N=576) == EUNSUP                              # gated needs N % 128
     assert _any(s=B + 4) == EALIGN                                   # MXFP8 scales: 16 B
     assert _any(fmt=2, s=B + 4) != EALIGN                            # FP8 row scales: 4 B is enough
@@ -197,7 +204,7 @@ def test_gate_residual_validation():
     assert _gr(gr=P(E, 512, F, 0)) == EINVAL
     assert _gr(gr=P(D + 1024, 512, F, 32)) == EINVAL                 # partial overlap with the output
     assert _gr(fmt=5) == EINVAL
-    assert _gr(K=128) == EUNSUP
+    assert _gr(K=64) == EUNSUP                                       # K % 128
     assert _gr(gr=P(E + 8, 512, F, 32)) == EALIGN
     assert _gr(gr=P(E, 500, F, 32)) == EALIGN                         # ldr < N
     assert _gr(gr=P(E, 516, F, 32)) == EALIGN                         # ldr % 8

@@ -256,3 +256,27 @@ def test_gate_residual_full_size_sampled_rows(ditq):
     rows = np.unique(np.concatenate([[0, 1, 4607, 4608, 4609, wl.M - 1], rng.choice(wl.M, 40, replace=False)]))
     rep = compare_bf16(g[rows], oracle_rows(d, "fp4", "gate_residual", rows=rows), "mlp_down_gate_residual")
     print(f"mlp_down_gate_residual: literal max err / row-RMS = {rep['literal_max_err_over_rowrms']:.4g}")
+
+
+ODD_K = [(f, e, K) for K in (384, 1152, 2432) for f in ("fp4", "fp8", "mx8", "nv4")
+         for e in ("identity", "gated_silu", "qk_rmsnorm", "gelu_tanh", "gate_residual")]
+
+
+@pytest.mark.parametrize("fmt,epi,K", ODD_K, ids=[f"{f}-{e}-K{k}" for f, e, k in ODD_K])
+def test_k_multiple_of_128(ditq, fmt, epi, K):
+    """K = 3, 9 and 19 k-steps of 128: the main loop pads to whole groups of its
+    unrolled ring with steps that read zeros; every element still equals the
+    oracle's result for the true K."""
+    from tests.gpu_util import compare_bf16
+    M = 70
+    print(f"case odd K {fmt} {epi} K={K}", flush=True)
+    if epi == "gate_residual":
+        d = make_inputs("mlp_down_gate_residual", seed=K, M=M, N=320, K=K, rows_per_gate=33)
+        g = run_gate_residual(ditq, d, fmt, guard=32, ldo=328)
+    else:
+        kind = {"identity": "mlp_gated_silu", "gated_silu": "mlp_gated_silu", "gelu_tanh": "mlp_gelu_tanh",
+                "qk_rmsnorm": "qkv_rmsnorm_hd128"}[epi]
+        d = make_inputs(kind, seed=K, M=M, N=None if epi == "qk_rmsnorm" else 640, K=K,
+                        n_heads=1 if epi == "qk_rmsnorm" else None)
+        g = run_layer(ditq, d, fmt, epi, guard=32, generic=True)
+    compare_bf16(g, oracle_rows(d, fmt, epi), f"odd K {fmt}/{epi}/K{K}")
