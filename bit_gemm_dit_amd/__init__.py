@@ -18,7 +18,7 @@ __all__ = [
     "EPI_GATE_RESIDUAL", "DitError", "RmsNormParams", "GateResidualParams",
     "dit_packed_weight_bytes", "dit_act_code_bytes", "dit_act_scale_bytes", "dit_pack_weights",
     "dit_quantize_act", "dit_gemm_q4_epilogue", "dit_gemm_q4_epilogue_q4", "dit_gemm_q8_epilogue",
-    "dit_gemm_epilogue", "dit_gemm_gate_residual", "gemm_gate_residual",
+    "dit_gemm_epilogue", "dit_gemm_gate_residual", "gemm_gate_residual", "dit_gemm_epilogue_f32",
     "dit_gated_silu_bf16", "dit_mfma_fp4_probe", "gated_silu", "mfma_fp4_probe",
     "dit_status_str", "dit_last_error", "pack_weights", "quantize_act", "gemm", "gemm_q4out", "linear",
     "library_path", "EXPORTED", "BLOB_MAGIC", "BLOB_VERSION", "blob_header", "check_blob", "save_packed",
@@ -77,6 +77,8 @@ _SIGS = {
     "dit_gemm_q8_epilogue": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _i, _p]),
     "dit_gemm_epilogue": (_i, [_i, _p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams), _p, _i, _p]),
     "dit_gemm_gate_residual": (_i, [_i, _p, _p, _p, _i, _i, _i, ctypes.POINTER(GateResidualParams), _p, _i, _p]),
+    "dit_gemm_epilogue_f32": (_i, [_i, _p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams),
+                                   ctypes.POINTER(GateResidualParams), _p, _i, _p]),
     "dit_gated_silu_bf16": (_i, [_p, _i, _i, _i, _p, _i, _p]),
     "dit_mfma_fp4_probe": (_i, [_i, _i, _p, _p]),
     "dit_status_str": (ctypes.c_char_p, [_i]),
@@ -158,6 +160,14 @@ def dit_gemm_gate_residual(fmt, a_codes, a_scales, w_packed, M, N, K, gr, out, l
     gp = ctypes.byref(gr) if gr is not None else None
     _check(_lib.dit_gemm_gate_residual(fmt, a_codes, a_scales, w_packed, M, N, K, gp, out, ldo, stream),
            "dit_gemm_gate_residual")
+
+
+def dit_gemm_epilogue_f32(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, gr, out_f32, ldo,
+                          stream=None) -> None:
+    rp = ctypes.byref(rms) if rms is not None else None
+    gp = ctypes.byref(gr) if gr is not None else None
+    _check(_lib.dit_gemm_epilogue_f32(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rp, gp, out_f32, ldo, stream),
+           "dit_gemm_epilogue_f32")
 
 
 def dit_gated_silu_bf16(c, M, N, ldc, out, ldo, stream=None) -> None:

@@ -240,10 +240,11 @@ hipError_t launch_pack(int fmt, int epi, const uint16_t* w, int N, int K, int ld
 // Fused GEMM + epilogue in any format.  a_scales: FP4 / MXFP8 E8M0 bytes, FP8 fp32
 // row scales.  rms: non-null exactly for EPI_QK_RMSNORM; gr: exactly for
 // EPI_GATE_RESIDUAL.  q_codes / q_scales (FP4 only): optional FP4 quantization of
-// the output (null: none); out may be null when q_codes is set.
+// the output (null: none); out may be null when q_codes is set.  out_f32 (debug, or
+// null): the fp32 values the bf16 store would round go there instead, [M][ldo] fp32.
 hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, const uint8_t* blob, int M, int N,
                        int K, int epi, const RmsArgs* rms, const ResidualArgs* gr, uint16_t* out, int ldo,
-                       uint8_t* q_codes, uint8_t* q_scales, hipStream_t stream);
+                       uint8_t* q_codes, uint8_t* q_scales, float* out_f32, hipStream_t stream);
 
 // measurement kernels (measure.hip)
 hipError_t launch_gated_silu(const uint16_t* c, int M, int N, int ldc, uint16_t* out, int ldo,

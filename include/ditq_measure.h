@@ -34,6 +34,20 @@ extern "C" {
 dit_status dit_gated_silu_bf16(const void* c_bf16, int M, int N, int ldc, void* out_bf16, int ldo,
                                void* stream);
 
+/* Debug form of the fused GEMM + epilogue: the same kernels as dit_gemm_epilogue and
+ * dit_gemm_gate_residual (same arguments, formats, epilogues, shape rules and
+ * errors), except that each output element is stored as the fp32 value the bf16
+ * store would round, into out_f32 [M][ldo] (fp32, 16-byte aligned, ldo >= output
+ * width, ldo % 4 == 0).  It shows the accuracy of the fused arithmetic before the
+ * final bf16 rounding: the bf16 output of the other entry points equals the
+ * round-to-nearest-even bf16 of this output, bit for bit.  Page "How fal made
+ * Ideogram V4 6x faster", paragraphs 3-4 (the epilogues on the accumulator before
+ * the one store).  gr must be non-NULL exactly when epi == DIT_EPI_GATE_RESIDUAL;
+ * the residual must not overlap out_f32 (DIT_EINVAL). */
+dit_status dit_gemm_epilogue_f32(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed,
+                                 int M, int N, int K, dit_epi epi, const dit_rmsnorm_params* rms,
+                                 const dit_gate_residual_params* gr, float* out_f32, int ldo, void* stream);
+
 /* Matrix-core throughput probe: `workgroups` workgroups of 4 waves, each wave
  * issuing iters x 8 independent v_mfma_scale_f32_32x32x64_f8f6f4 (FP4 E2M1
  * operands, unit scales) on register operands, with no memory traffic in its loop.
