@@ -36,7 +36,9 @@ EPI_GELU_TANH = 3
 EPI_GATE_RESIDUAL = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libditq.so")
+# DITQ_LIB selects another build of the library, e.g. the CPU-only sanitizer build
+# of the ABI layer (build.py --sanitize); the default is the in-tree libditq.so.
+library_path = os.environ.get("DITQ_LIB") or os.path.join(_HERE, "libditq.so")
 
 if not os.path.exists(library_path):
     raise ImportError(

@@ -12,6 +12,7 @@
 
 #include <atomic>
 #include <cstdio>
+#include <cstring>
 
 #include "common.hpp"
 
@@ -21,6 +22,18 @@ using ditq::FMT_FP4;
 using ditq::FMT_FP8;
 using ditq::FMT_MX8;
 using ditq::FMT_NV4;
+
+// The value of an enum argument as an int.  A C caller (or ctypes) may pass any int
+// for an enum parameter, and in C++ reading an enum object whose value lies outside
+// the enumeration's range is undefined behaviour; so the entry points copy the
+// argument's bytes instead and work with ints.
+template <class E>
+int raw(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -87,26 +100,30 @@ dit_status launched(hipError_t e) { return e == hipSuccess ? DIT_OK : device_err
 
 extern "C" {
 
-size_t dit_packed_weight_bytes(dit_fmt fmt, dit_epi epi, int N, int K) {
+size_t dit_packed_weight_bytes(dit_fmt fmt_, dit_epi epi_, int N, int K) {
+  const int fmt = raw(fmt_), epi = raw(epi_);
   if (!valid_fmt(fmt) || !valid_epi(epi) || N <= 0 || K <= 0) return 0;
   if (!shape_ok(fmt, epi, N, K)) return 0;
   return ditq::blob_total_bytes(fmt, ditq::padded_rows(N), K);
 }
 
-size_t dit_act_code_bytes(dit_fmt fmt, int M, int K) {
+size_t dit_act_code_bytes(dit_fmt fmt_, int M, int K) {
+  const int fmt = raw(fmt_);
   if (!valid_fmt(fmt) || M <= 0 || K <= 0 || K % 128 != 0) return 0;
   return ditq::is_fp4_codes(fmt) ? (size_t)M * K / 2 : (size_t)M * K;
 }
 
-size_t dit_act_scale_bytes(dit_fmt fmt, int M, int K) {
+size_t dit_act_scale_bytes(dit_fmt fmt_, int M, int K) {
+  const int fmt = raw(fmt_);
   if (!valid_fmt(fmt) || M <= 0 || K <= 0 || K % 128 != 0) return 0;
   if (fmt == DIT_FMT_FP8_E4M3_ROWCOL) return (size_t)M * 4;
   if (fmt == DIT_FMT_FP4_E2M1_NV16) return ditq::nv4_act_tail(M, K) + ditq::kNvTailBytes + ditq::kNvPartialBytes;
   return (size_t)M * K / 32;
 }
 
-dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N, int K, int ldw, void* packed,
+dit_status dit_pack_weights(dit_fmt fmt_, dit_epi epi_, const void* w_bf16, int N, int K, int ldw, void* packed,
                             void* stream) {
+  const int fmt = raw(fmt_), epi = raw(epi_);
   if (!valid_fmt(fmt) || !valid_epi(epi) || !w_bf16 || !packed || N <= 0 || K <= 0) return DIT_EINVAL;
   if (!shape_ok(fmt, epi, N, K)) return DIT_EUNSUPPORTED;
   if (!aligned16(w_bf16) || !aligned16(packed) || ldw < K || ldw % 8 != 0) return DIT_EALIGN;
@@ -116,8 +133,12 @@ dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N,
                                     static_cast<uint8_t*>(packed), static_cast<hipStream_t>(stream)));
 }
 
-dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int ldx, void* codes, void* scales,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+// Checks and launch of the quantizer.
+dit_status quantize_any(int fmt, const void* x_bf16, int M, int K, int ldx, void* codes, void* scales,
+                        void* stream) {
   if (!valid_fmt(fmt) || !x_bf16 || !codes || !scales || M <= 0 || K <= 0) return DIT_EINVAL;
   if (K % 128 != 0 || !rows_ok(fmt, M, K)) return DIT_EUNSUPPORTED;
   if (!aligned16(x_bf16) || !aligned16(codes) || ldx < K || ldx % 8 != 0) return DIT_EALIGN;
@@ -126,25 +147,30 @@ dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int l
   if (dit_status s = check_device()) return s;
   (void)hipGetLastError();
   const auto x = static_cast<const uint16_t*>(x_bf16);
+  const auto c = static_cast<uint8_t*>(codes);
   const auto st = static_cast<hipStream_t>(stream);
   if (fmt == DIT_FMT_FP4_E2M1_MX32)
-    return launched(ditq::launch_quant_fp4(x, M, K, ldx, static_cast<uint8_t*>(codes),
-                                           static_cast<uint8_t*>(scales), st));
+    return launched(ditq::launch_quant_fp4(x, M, K, ldx, c, static_cast<uint8_t*>(scales), st));
   if (fmt == DIT_FMT_FP8_E4M3_MX32)
-    return launched(ditq::launch_quant_mx8(x, M, K, ldx, static_cast<uint8_t*>(codes),
-                                           static_cast<uint8_t*>(scales), st));
+    return launched(ditq::launch_quant_mx8(x, M, K, ldx, c, static_cast<uint8_t*>(scales), st));
   if (fmt == DIT_FMT_FP4_E2M1_NV16)
-    return launched(ditq::launch_quant_nv4(x, M, K, ldx, static_cast<uint8_t*>(codes),
-                                           static_cast<uint8_t*>(scales), st));
-  return launched(
-      ditq::launch_quant_fp8(x, M, K, ldx, static_cast<uint8_t*>(codes), static_cast<float*>(scales), st));
+    return launched(ditq::launch_quant_nv4(x, M, K, ldx, c, static_cast<uint8_t*>(scales), st));
+  return launched(ditq::launch_quant_fp8(x, M, K, ldx, c, static_cast<float*>(scales), st));
+}
+}  // namespace
+
+extern "C" {
+
+dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int ldx, void* codes, void* scales,
+                            void* stream) {
+  return quantize_any(raw(fmt), x_bf16, M, K, ldx, codes, scales, stream);
 }
 
 namespace {
 // Checks and launch shared by every GEMM entry point.  out_codes set: the FP4
 // quantization of the output is written too (FP4 only), and out_bf16 may be null.
 dit_status gemm_any(int fmt, const void* a_codes, const void* a_scales, const void* w_packed, int M, int N, int K,
-                    dit_epi epi, const dit_rmsnorm_params* rms, const dit_gate_residual_params* gr,
+                    int epi, const dit_rmsnorm_params* rms, const dit_gate_residual_params* gr,
                     void* out_bf16, int ldo, void* out_codes, void* out_scales, float* out_f32, void* stream) {
   const bool quantized = out_codes != nullptr;
   if (!valid_fmt(fmt) || !a_codes || !a_scales || !w_packed || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi))
@@ -196,23 +222,26 @@ dit_status gemm_any(int fmt, const void* a_codes, const void* a_scales, const vo
 }  // namespace
 
 dit_status dit_gemm_q4_epilogue(const void* a_codes, const void* a_scales, const void* w_packed, int M, int N,
-                                int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
+                                int K, dit_epi epi_, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
                                 void* stream) {
+  const int epi = raw(epi_);
   if (!out_bf16) return DIT_EINVAL;
   return gemm_any(FMT_FP4, a_codes, a_scales, w_packed, M, N, K, epi, rms, nullptr, out_bf16, ldo, nullptr,
                   nullptr, nullptr, stream);
 }
 
 dit_status dit_gemm_q4_epilogue_q4(const void* a_codes, const void* a_scales, const void* w_packed, int M, int N,
-                                   int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
+                                   int K, dit_epi epi_, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
                                    void* out_codes, void* out_scales, void* stream) {
+  const int epi = raw(epi_);
   if (!out_codes || !out_scales) return DIT_EINVAL;
   return gemm_any(FMT_FP4, a_codes, a_scales, w_packed, M, N, K, epi, rms, nullptr, out_bf16, ldo, out_codes,
                   out_scales, nullptr, stream);
 }
 
 dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, const void* w_packed, int M, int N,
-                                int K, dit_epi epi, void* out_bf16, int ldo, void* stream) {
+                                int K, dit_epi epi_, void* out_bf16, int ldo, void* stream) {
+  const int epi = raw(epi_);
   if (!a_codes || !a_scales || !w_packed || !out_bf16 || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi))
     return DIT_EINVAL;
   // no parameters for RMSNorm or the gated residual here
@@ -221,25 +250,28 @@ dit_status dit_gemm_q8_epilogue(const void* a_codes, const float* a_scales, cons
                   nullptr, nullptr, stream);
 }
 
-dit_status dit_gemm_epilogue(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed, int M,
-                             int N, int K, dit_epi epi, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
+dit_status dit_gemm_epilogue(dit_fmt fmt_, const void* a_codes, const void* a_scales, const void* w_packed, int M,
+                             int N, int K, dit_epi epi_, const dit_rmsnorm_params* rms, void* out_bf16, int ldo,
                              void* stream) {
+  const int fmt = raw(fmt_), epi = raw(epi_);
   if (!out_bf16) return DIT_EINVAL;
   return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, nullptr, out_bf16, ldo, nullptr, nullptr,
                   nullptr, stream);
 }
 
-dit_status dit_gemm_gate_residual(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed,
+dit_status dit_gemm_gate_residual(dit_fmt fmt_, const void* a_codes, const void* a_scales, const void* w_packed,
                                   int M, int N, int K, const dit_gate_residual_params* gr, void* out_bf16, int ldo,
                                   void* stream) {
+  const int fmt = raw(fmt_);
   if (!gr || !out_bf16) return DIT_EINVAL;
   return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, DIT_EPI_GATE_RESIDUAL, nullptr, gr, out_bf16, ldo,
                   nullptr, nullptr, nullptr, stream);
 }
 
-dit_status dit_gemm_epilogue_f32(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed, int M,
-                                 int N, int K, dit_epi epi, const dit_rmsnorm_params* rms,
+dit_status dit_gemm_epilogue_f32(dit_fmt fmt_, const void* a_codes, const void* a_scales, const void* w_packed,
+                                 int M, int N, int K, dit_epi epi_, const dit_rmsnorm_params* rms,
                                  const dit_gate_residual_params* gr, float* out_f32, int ldo, void* stream) {
+  const int fmt = raw(fmt_), epi = raw(epi_);
   if (!out_f32) return DIT_EINVAL;
   return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, gr, nullptr, ldo, nullptr, nullptr, out_f32,
                   stream);
@@ -269,7 +301,7 @@ dit_status dit_mfma_fp4_probe(int workgroups, int iters, void* out_u64, void* st
 const char* dit_last_error(void) { return g_last_error; }
 
 const char* dit_status_str(dit_status status) {
-  switch (status) {
+  switch (raw(status)) {
     case DIT_OK: return "ok";
     case DIT_EINVAL: return "invalid argument";
     case DIT_EUNSUPPORTED: return "unsupported shape or combination";

@@ -295,3 +295,25 @@ def test_packed_blob_save_load_header_checks(tmp_path):
         x[48:56].view("<u8")[0] = 0
         with pytest.raises(ValueError, match="inconsistent"):
             ditq.check_blob(x)
+
+
+def _f32(fmt=1, a=A, s=B, w=C, M=64, N=512, K=256, epi=1, rms=None, gr=None, out=D, ldo=256):
+    return ditq._lib.dit_gemm_epilogue_f32(fmt, a, s, w, M, N, K, epi, ctypes.byref(rms) if rms else None,
+                                           ctypes.byref(gr) if gr else None, out, ldo, None)
+
+
+def test_gemm_f32_debug_validation():
+    P = ditq.GateResidualParams
+    assert _f32(out=None) == EINVAL
+    assert _f32(epi=2) == EINVAL                                     # RMSNorm without params
+    assert _f32(epi=4, ldo=512) == EINVAL                            # gated residual without params
+    assert _f32(epi=1, gr=P(E, 512, F, 32)) == EINVAL                # params without the gated residual
+    assert _f32(epi=4, gr=P(D, 512, F, 32), ldo=512) == EINVAL       # the residual overlaps the fp32 output
+    assert _f32(K=192) == EUNSUP
+    assert _f32(out=D + 8) == EALIGN
+    assert _f32(ldo=255) == EALIGN                                   # < output width
+    assert _f32(ldo=258) == EALIGN                                   # fp32 rows: a multiple of 4 elements
+    if not _has_gpu():
+        assert _f32(ldo=260) == EDEVICE
+        assert _f32(fmt=2, epi=0, ldo=512) == EDEVICE
+        assert _f32(epi=4, gr=P(0x1000000, 512, 0x2000000, 32), ldo=512) == EDEVICE

@@ -197,7 +197,7 @@ def test_forward_equals_exact_composition(fmt, epi):
 
 @pytest.mark.parametrize("fmt,epi", CASES, ids=[f"{f}-{e}" for f, e in CASES])
 def test_forward_on_row_subsets(fmt, epi):
-    """``rows=`` (the sampled-row path of the full-size tests) gives exactly those
+    """``rows=`` (the sampled-row path of the largest-size tests) gives exactly those
     rows of the full computation, in the order asked for; for the gated residual
     each row takes its own residual row and its sample's gate row."""
     inp = make_case(fmt, epi, seed=100 + FORMATS.index(fmt) * 10 + EPIS.index(epi))
