@@ -17,7 +17,7 @@ __all__ = [
     "FMT_FP4", "FMT_FP8", "FMT_MX8", "FMT_NV4", "EPI_IDENTITY", "EPI_GATED_SILU", "EPI_QK_RMSNORM", "EPI_GELU_TANH",
     "EPI_GATE_RESIDUAL", "DitError", "RmsNormParams", "GateResidualParams",
     "dit_packed_weight_bytes", "dit_act_code_bytes", "dit_act_scale_bytes", "dit_pack_weights",
-    "dit_quantize_act", "dit_gemm_q4_epilogue", "dit_gemm_q4_epilogue_q4", "dit_gemm_q8_epilogue",
+    "dit_quantize_act", "dit_quantize_act_noalloc", "dit_gemm_q4_epilogue", "dit_gemm_q4_epilogue_q4", "dit_gemm_q8_epilogue",
     "dit_gemm_epilogue", "dit_gemm_gate_residual", "gemm_gate_residual", "dit_gemm_epilogue_f32",
     "dit_gated_silu_bf16", "dit_mfma_fp4_probe", "gated_silu", "mfma_fp4_probe",
     "dit_status_str", "dit_last_error", "pack_weights", "quantize_act", "gemm", "gemm_q4out", "linear",
@@ -73,6 +73,7 @@ _SIGS = {
     "dit_act_scale_bytes": (_sz, [_i, _i, _i]),
     "dit_pack_weights": (_i, [_i, _i, _p, _i, _i, _i, _p, _p]),
     "dit_quantize_act": (_i, [_i, _p, _i, _i, _i, _p, _p, _p]),
+    "dit_quantize_act_noalloc": (_i, [_i, _p, _i, _i, _i, _p, _p, _p]),
     "dit_gemm_q4_epilogue": (_i, [_p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams), _p, _i, _p]),
     "dit_gemm_q4_epilogue_q4": (_i, [_p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams), _p, _i, _p, _p,
                                      _p]),
@@ -132,6 +133,11 @@ def dit_pack_weights(fmt, epi, w_ptr, N, K, ldw, packed_ptr, stream=None) -> Non
 
 def dit_quantize_act(fmt, x_ptr, M, K, ldx, codes_ptr, scales_ptr, stream=None) -> None:
     _check(_lib.dit_quantize_act(fmt, x_ptr, M, K, ldx, codes_ptr, scales_ptr, stream), "dit_quantize_act")
+
+
+def dit_quantize_act_noalloc(fmt, x_ptr, M, K, ldx, codes_ptr, scales_ptr, stream=None) -> None:
+    _check(_lib.dit_quantize_act_noalloc(fmt, x_ptr, M, K, ldx, codes_ptr, scales_ptr, stream),
+           "dit_quantize_act_noalloc")
 
 
 def dit_gemm_q4_epilogue(a_codes, a_scales, w_packed, M, N, K, epi, rms, out, ldo, stream=None) -> None:

@@ -136,9 +136,11 @@ dit_status dit_pack_weights(dit_fmt fmt_, dit_epi epi_, const void* w_bf16, int 
 }  // extern "C"
 
 namespace {
-// Checks and launch of the quantizer.
+// Checks and launch of both quantizer entry points.  static_work: NVFP4 keeps its
+// tensor-maximum work space in the library's static array instead of the scale
+// buffer's tail.
 dit_status quantize_any(int fmt, const void* x_bf16, int M, int K, int ldx, void* codes, void* scales,
-                        void* stream) {
+                        bool static_work, void* stream) {
   if (!valid_fmt(fmt) || !x_bf16 || !codes || !scales || M <= 0 || K <= 0) return DIT_EINVAL;
   if (K % 128 != 0 || !rows_ok(fmt, M, K)) return DIT_EUNSUPPORTED;
   if (!aligned16(x_bf16) || !aligned16(codes) || ldx < K || ldx % 8 != 0) return DIT_EALIGN;
@@ -153,8 +155,11 @@ dit_status quantize_any(int fmt, const void* x_bf16, int M, int K, int ldx, void
     return launched(ditq::launch_quant_fp4(x, M, K, ldx, c, static_cast<uint8_t*>(scales), st));
   if (fmt == DIT_FMT_FP8_E4M3_MX32)
     return launched(ditq::launch_quant_mx8(x, M, K, ldx, c, static_cast<uint8_t*>(scales), st));
-  if (fmt == DIT_FMT_FP4_E2M1_NV16)
-    return launched(ditq::launch_quant_nv4(x, M, K, ldx, c, static_cast<uint8_t*>(scales), st));
+  if (fmt == DIT_FMT_FP4_E2M1_NV16) {
+    if (static_work)
+      return launched(ditq::launch_quant_nv4_static(x, M, K, ldx, c, static_cast<uint8_t*>(scales), st));
+    return launched(ditq::launch_quant_nv4(x, M, K, ldx, c, static_cast<uint8_t*>(scales), nullptr, st));
+  }
   return launched(ditq::launch_quant_fp8(x, M, K, ldx, c, static_cast<float*>(scales), st));
 }
 }  // namespace
@@ -163,7 +168,12 @@ extern "C" {
 
 dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int ldx, void* codes, void* scales,
                             void* stream) {
-  return quantize_any(raw(fmt), x_bf16, M, K, ldx, codes, scales, stream);
+  return quantize_any(raw(fmt), x_bf16, M, K, ldx, codes, scales, false, stream);
+}
+
+dit_status dit_quantize_act_noalloc(dit_fmt fmt, const void* x_bf16, int M, int K, int ldx, void* codes,
+                                    void* scales, void* stream) {
+  return quantize_any(raw(fmt), x_bf16, M, K, ldx, codes, scales, true, stream);
 }
 
 namespace {

@@ -228,9 +228,15 @@ hipError_t launch_quant_fp8(const uint16_t* x, int M, int K, int ldx, uint8_t* c
                             hipStream_t stream);
 hipError_t launch_quant_mx8(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
                             hipStream_t stream);
-// scales: M*K/16 block scale bytes plus the tail (nv4_act_tail, kNvTailBytes + kNvPartialBytes)
+// scales: M*K/16 block scale bytes plus the tail (nv4_act_tail, kNvTailBytes + kNvPartialBytes).
+// work: 1 + kAmaxBlocks u32 of work space for the tensor maximum, or null to use the
+// scale buffer's tail for it.
 hipError_t launch_quant_nv4(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
-                            hipStream_t stream);
+                            uint32_t* work, hipStream_t stream);
+// The same with the library's static per-device work space (quant.hip `scratch`): the
+// scale buffer then needs only M*K/16 + kNvTailBytes bytes.  No allocation.
+hipError_t launch_quant_nv4_static(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
+                                   hipStream_t stream);
 // Largest bf16 magnitude (bit pattern) of x [R][ld] (first `cols` columns), written to
 // *slot; `partial` is work space for kAmaxBlocks u32 (the per-workgroup maxima).
 hipError_t launch_amax_bf16(const uint16_t* x, int R, int cols, int ld, uint32_t* slot, uint32_t* partial,

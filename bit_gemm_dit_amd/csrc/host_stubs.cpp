@@ -19,7 +19,10 @@ hipError_t launch_quant_fp8(const uint16_t*, int, int, int, uint8_t*, float*, hi
 hipError_t launch_quant_mx8(const uint16_t*, int, int, int, uint8_t*, uint8_t*, hipStream_t) {
   return hipErrorNoDevice;
 }
-hipError_t launch_quant_nv4(const uint16_t*, int, int, int, uint8_t*, uint8_t*, hipStream_t) {
+hipError_t launch_quant_nv4(const uint16_t*, int, int, int, uint8_t*, uint8_t*, uint32_t*, hipStream_t) {
+  return hipErrorNoDevice;
+}
+hipError_t launch_quant_nv4_static(const uint16_t*, int, int, int, uint8_t*, uint8_t*, hipStream_t) {
   return hipErrorNoDevice;
 }
 hipError_t launch_amax_bf16(const uint16_t*, int, int, int, uint32_t*, uint32_t*, hipStream_t) {

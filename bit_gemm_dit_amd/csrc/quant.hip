@@ -19,6 +19,8 @@
 // 1 (FP8) or 1 + 1/32 (MXFP8) bytes written.  Outputs are K-panel-major
 // (include/ditq.h): the GEMM then copies each 64-byte-per-token panel slice of a
 // token tile as one contiguous run.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace ditq {
@@ -253,17 +255,54 @@ hipError_t launch_amax_bf16(const uint16_t* x, int R, int cols, int ld, uint32_t
 }
 
 hipError_t launch_quant_nv4(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
-                            hipStream_t stream) {
+                            uint32_t* work, hipStream_t stream) {
   uint32_t* slot = reinterpret_cast<uint32_t*>(scales + nv4_act_tail(M, K));
-  if (hipError_t e = launch_amax_bf16(x, M, K, ldx, slot, slot + kNvTailBytes / 4, stream)) return e;
+  // work: the tensor-maximum slot and the per-workgroup maxima; by default the
+  // scale buffer's own tail (slot, then the maxima after the 16-byte tail)
+  uint32_t* amax = work ? work : slot;
+  uint32_t* partial = work ? work + 1 : slot + kNvTailBytes / 4;
+  if (hipError_t e = launch_amax_bf16(x, M, K, ldx, amax, partial, stream)) return e;
   const uint32_t per_row = (uint32_t)K / 8;
   const uint32_t total = (uint32_t)M * per_row;
   uint32_t blocks = (total + 255) / 256;
   const uint32_t cap = 256u * 32u;
   if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(quant_nv4_kernel, dim3(blocks), dim3(256), 0, stream, x, M, ldx, codes, scales, total,
-                     per_row, slot, reinterpret_cast<float*>(slot + 1));
+                     per_row, amax, reinterpret_cast<float*>(slot + 1));
   return hipGetLastError();
+}
+
+// Work space of the allocation-free NVFP4 quantizer: the tensor-maximum slot and the
+// kAmaxBlocks per-workgroup maxima, 2052 bytes whatever M and K.  Each device holds
+// its own copy until the process ends; every call on that device shares it, so calls
+// that overlap on one device race.  Nothing in it needs clearing: every call writes
+// each entry it reads first.
+static __device__ __align__(256) uint32_t scratch[1 + kAmaxBlocks];
+
+// Device address of `scratch` on the current device, looked up once per device
+// (the host-side name is only a stand-in: a kernel must be given this address).
+static hipError_t scratch_address(uint32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<uint32_t*> addr[kMaxDevices];
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uint32_t* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch))) return e;
+    p = static_cast<uint32_t*>(q);
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_quant_nv4_static(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, uint8_t* scales,
+                                   hipStream_t stream) {
+  uint32_t* work = nullptr;
+  if (hipError_t e = scratch_address(&work)) return e;
+  return launch_quant_nv4(x, M, K, ldx, codes, scales, work, stream);
 }
 
 hipError_t launch_quant_fp8(const uint16_t* x, int M, int K, int ldx, uint8_t* codes, float* scales,

@@ -215,6 +215,24 @@ dit_status dit_pack_weights(dit_fmt fmt, dit_epi epi, const void* w_bf16, int N,
 dit_status dit_quantize_act(dit_fmt fmt, const void* x_bf16, int M, int K, int ldx,
                             void* codes, void* scales, void* stream);
 
+/* ---------------------------------------------------------------- activation quantizer, no work space
+ * For callers that cannot allocate or hand over work space: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The same
+ * quantization, codes and scales as dit_quantize_act, bit for bit, for every
+ * format.  Only NVFP4 needs work space beyond its outputs (the tensor-maximum slot
+ * and 512 per-workgroup maxima, 2052 bytes for any M and K): dit_quantize_act takes
+ * it from the scale buffer's tail, this entry from a static array of the library
+ * (one per device, held until the process ends), so its NVFP4 scale buffer needs
+ * only M*K/16 + 16 bytes (the block scales, then the 16-byte tail whose fp32 tensor
+ * scale at byte M*K/16 + 4 the GEMM reads).  Other formats: exactly
+ * dit_quantize_act.  Allocates, frees and synchronises nothing.
+ * NVFP4 calls on one device share the static work space, so calls that overlap on
+ * one device (on different streams) race; calls on one stream are ordered.
+ * Arguments, shapes (the same limits on M and K; larger sizes DIT_EUNSUPPORTED)
+ * and errors as dit_quantize_act. */
+dit_status dit_quantize_act_noalloc(dit_fmt fmt, const void* x_bf16, int M, int K, int ldx,
+                                    void* codes, void* scales, void* stream);
+
 /* ---------------------------------------------------------------- fused GEMM + epilogue, FP4
  * The big GEMM in the 4-bit format, C = A @ B (page "How fal made Ideogram V4 6x
  * faster", paragraph 4), with the small op that follows it applied to the fp32

@@ -317,3 +317,18 @@ def test_gemm_f32_debug_validation():
         assert _f32(ldo=260) == EDEVICE
         assert _f32(fmt=2, epi=0, ldo=512) == EDEVICE
         assert _f32(epi=4, gr=P(0x1000000, 512, 0x2000000, 32), ldo=512) == EDEVICE
+
+
+def test_quantize_noalloc_validation():
+    lib = ditq._lib
+    assert lib.dit_quantize_act_noalloc(4, None, 4, 256, 256, B, C, None) == EINVAL
+    assert lib.dit_quantize_act_noalloc(4, A, 4, 256, 256, B, None, None) == EINVAL
+    assert lib.dit_quantize_act_noalloc(4, A, 0, 256, 256, B, C, None) == EINVAL
+    assert lib.dit_quantize_act_noalloc(9, A, 4, 256, 256, B, C, None) == EINVAL
+    assert lib.dit_quantize_act_noalloc(4, A, 4, 320, 320, B, C, None) == EUNSUP     # K % 128
+    assert lib.dit_quantize_act_noalloc(4, A, 1 << 30, 4096, 4096, B, C, None) == EUNSUP   # beyond the code limit
+    assert lib.dit_quantize_act_noalloc(4, A, 4, 256, 256, B, C + 4, None) == EALIGN
+    assert lib.dit_quantize_act_noalloc(4, A + 2, 4, 256, 256, B, C, None) == EALIGN
+    if not _has_gpu():
+        for fmt in (1, 2, 3, 4):
+            assert lib.dit_quantize_act_noalloc(fmt, A, 4, 256, 256, B, C, None) == EDEVICE
