@@ -82,9 +82,14 @@ constexpr int kGroupM = 8;
 // 2 x 2 grid, each wave 128 features x BM/2 tokens) or 4 (a 4 x 1 grid, each wave 64
 // features x all BM tokens: no weight row is needed by two waves, so all weights go
 // straight to registers and only the activation tile is shared).
-template <int FMT_, int EPI_, int TM_, int RING_, int WLDS_, int HD_ = 0, int WL_ = 2>
+// F32: the debug form of the kernel, whose store writes the fp32 value the bf16 store
+// would round (a separate instantiation, so that the production kernels carry no
+// trace of it).
+template <int FMT_, int EPI_, int TM_, int RING_, int WLDS_, int HD_ = 0, int WL_ = 2, bool F32_ = false>
 struct Tile {
   static constexpr int FMT = FMT_, EPI = EPI_, TM = TM_, RING = RING_, WLDS = WLDS_, HD = HD_;
+  static constexpr bool F32 = F32_;
+  using Debug = Tile<FMT_, EPI_, TM_, RING_, WLDS_, HD_, WL_, true>;
   static constexpr int WAVES_N = WL_, WAVES_M = 4 / WL_, TN = 8 / WL_, NW = 4, NT = 256;
   static constexpr int WN = 32 * TN, WM = 32 * TM;
   static constexpr int BN = WN * WAVES_N, BM = WM * WAVES_M;
@@ -227,7 +232,7 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 template <class T>
 __device__ inline void store_tile(const Params& p, int row, bool row_ok, int col0, int ncols, int h,
                                   const float* v) {
-  if (p.out_f32 != nullptr) {
+  if constexpr (T::F32) {
     // debug store: the lane's four runs of 4 columns (8g + 4h) as fp32, no rounding
     if (row_ok) {
       float* o = p.out_f32 + (size_t)row * p.ldo;
@@ -575,19 +580,26 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
           if constexpr (T::EPI == EPI_GATE_RESIDUAL) {
             // this lane's 16 columns are 4 runs of 4 (n0 + 8g + 4h + i): the residual
             // as four 8-byte reads, the gate row of the token's sample as four 16-byte
-            // reads.  Rows past M read row M - 1 and runs at or past N (the padded
-            // columns of the last tile; N is a multiple of 64, so a run is wholly in or
-            // out) read nothing: every read stays inside residual[M][ldr] and
-            // gate[ceil(M / rows_per_gate)][N], and neither kind is stored.
+            // reads.  Rows past M read row M - 1, and a 32-column result tile at or past
+            // N (the padding of the last tile; N is a multiple of 64, so a tile is
+            // wholly in or out) reads nothing: every read stays inside residual[M][ldr]
+            // and gate[ceil(M / rows_per_gate)][N], and neither kind of result is
+            // stored.  The test is uniform over the wave: a per-lane test measured dozens
+            // of register spills more.  The 4-bit formats skip the reads of such a tile,
+            // the 8-bit ones read the last 32 columns instead (each form is the one that
+            // spills fewer registers in that format's kernels).
             const int rr = ok ? row : p.M - 1;
-            const int col = n0w + 32 * tn + 4 * h;
+            constexpr bool kSkip = is_fp4_codes(T::FMT);
+            const bool live = kSkip ? n0w + 32 * tn < p.N : true;
+            const int col = (kSkip ? n0w + 32 * tn : __builtin_amdgcn_readfirstlane(min(n0w + 32 * tn, p.N - 32))) +
+                            4 * h;
             const uint16_t* rp = p.residual + (size_t)rr * p.ldr + col;
             const float* gp = p.gate + (size_t)(rr / p.rows_per_gate) * p.N + col;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               uint2 rv = {0u, 0u};
               v4f gv = {0.0f, 0.0f, 0.0f, 0.0f};
-              if (col + 8 * g < p.N) {
+              if (live) {
                 rv = *reinterpret_cast<const uint2*>(rp + 8 * g);
                 gv = *reinterpret_cast<const v4f*>(gp + 8 * g);
               }
@@ -1113,7 +1125,10 @@ hipError_t launch(Params& p, hipStream_t stream) {
   p.tiles_n = padded_rows(p.N) / T::BN;
   p.tiles = p.tiles_m * p.tiles_n;
   const int grid = p.tiles < cu_count() ? p.tiles : cu_count();
-  hipLaunchKernelGGL(gemm_kernel<T>, dim3(grid), dim3(T::NT), 0, stream, p);
+  if (p.out_f32 != nullptr)
+    hipLaunchKernelGGL(gemm_kernel<typename T::Debug>, dim3(grid), dim3(T::NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gemm_kernel<T>, dim3(grid), dim3(T::NT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1125,8 +1140,9 @@ hipError_t launch(Params& p, hipStream_t stream) {
 // 1.35x a 192-token one (measured 1.34-1.37x: QK-RMSNorm head_dim 128, 4 against 3
 // rounds, 100.1 against 102.9 us; head_dim 256, 5 against 3 rounds, 154.5 against
 // 125.7 us; the gated residual, 3 against 2 rounds, 232.9 against 207.8 us).  FP8
-// and MXFP8 always take 192: with 256 their operand registers spill.  FP4 weight ring of 8 units when the k-steps come in groups of
-// 4, else 4 (FP8 and MXFP8: 4).
+// and MXFP8 always take 192: with 256 their operand registers spill.  Weight ring: 8
+// units on the FP4 4 x 1 grid when the k-steps come in groups of 4, else 4 (every 2 x 2
+// grid, FP8 and MXFP8).
 template <int FMT, int EPI, int HD = 0, int WLDS = wlds_for(FMT)>
 hipError_t launch_cfg(Params& p, hipStream_t stream) {
   // 4 x 1 wave grid: 64 features x BM tokens per wave, every weight through registers.
@@ -1154,12 +1170,13 @@ hipError_t launch_cfg(Params& p, hipStream_t stream) {
       const long tn = padded_rows(p.N) / 256;
       const long r3 = ((p.M + 191) / 192 * tn + cus - 1) / cus, r4 = ((p.M + 255) / 256 * tn + cus - 1) / cus;
       const bool tm3 = r3 * 20 < r4 * 27;
-      if (nks % 4 != 0) {
-        if (tm3) return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
-        return launch<Tile<FMT, EPI, 4, 4, WLDS, HD>>(p, stream);
-      }
-      if (tm3) return launch<Tile<FMT, EPI, 3, 8, WLDS, HD>>(p, stream);
-      return launch<Tile<FMT, EPI, 4, 8, WLDS, HD>>(p, stream);
+      // 2 x 2 grid: a 4-unit weight ring (2 of the 4 groups come through LDS, so a
+      // deeper ring only adds registers: with 8 units the QK-RMSNorm kernels spill
+      // 3-24 VGPRs, and same-box A/B measured 4 units faster or level: QK-RMSNorm
+      // head_dim 128 93.7 vs 96.9 us, 256 118.7 vs 119.9 us, the gated residual
+      // 179.1 vs 179.9 us)
+      if (tm3) return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
+      return launch<Tile<FMT, EPI, 4, 4, WLDS, HD>>(p, stream);
     }
   }
 }

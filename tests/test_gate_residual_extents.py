@@ -3,8 +3,8 @@
 The fused epilogue out = residual + gate[m / rows_per_gate] * C reads the residual
 and the gate table of every column its result tile covers.  The tiles cover the
 padded width Np = ceil(N / 256) * 256 and whole 32-token slices past M, so the
-reads must be clipped: rows past M read row M - 1, and 4-column runs at or past N
-read nothing.  This test replays the kernel's address arithmetic (2 x 2 wave grid,
+reads must be clipped: rows past M read row M - 1, and a 32-column result tile that
+starts at or past N reads nothing (4-bit formats) or the last 32 columns (8-bit).  This test replays the kernel's address arithmetic (2 x 2 wave grid,
 128 features x 32*TM tokens per wave, lane l: token l % 32, runs 8g + 4(l / 32) of
 each 32-column result tile) for the fuzz shapes and the full-size workload, and
 checks that every element read lies inside the documented extents:
@@ -28,8 +28,10 @@ def tm_for(fmt: str, M: int, N: int, cus: int = 256) -> int:
     return 3 if r3 * 20 < r4 * 27 else 4
 
 
-def reads(M, N, ldr, rpg, TM, clip_columns=True):
-    """Element indices of every residual and gate read the epilogue makes."""
+def reads(M, N, ldr, rpg, TM, clip_columns=True, fmt="fp4"):
+    """Element indices of every residual and gate read the epilogue makes.  A result
+    tile that starts at or past N: the 4-bit formats skip its reads, the 8-bit ones
+    read the last 32 columns instead."""
     WN, WM = 128, 32 * TM
     BN, BM = 2 * WN, 2 * WM
     Np = (N + 255) // 256 * 256
@@ -43,11 +45,15 @@ def reads(M, N, ldr, rpg, TM, clip_columns=True):
     tn = np.arange(4)[None, None, None, None, None, None, :]
     row = m0 + wm * WM + 32 * tm + (lane & 31)
     rr = np.where(row < M, row, M - 1)
-    col = n0 + wn * WN + 32 * tn + 4 * (lane >> 5)
+    tile_col = n0 + wn * WN + 32 * tn                # first column of the 32-column result tile
+    skip = fmt in ("fp4", "nv4") or not clip_columns
+    col = (tile_col if skip else np.minimum(tile_col, N - 32)) + 4 * (lane >> 5)
     res, gat = [], []
     for g in range(4):
         c = col + 8 * g
-        take = np.broadcast_to(c < N, np.broadcast(rr, c).shape) if clip_columns else \
+        # the kernel reads a result tile only when it starts before N (a test uniform
+        # over the wave; N % 64 == 0, so a tile is wholly in or out)
+        take = np.broadcast_to(tile_col < N, np.broadcast(rr, c).shape) if clip_columns and skip else \
             np.ones(np.broadcast(rr, c).shape, dtype=bool)
         r_b = np.broadcast_to(rr, take.shape)[take].astype(np.int64)
         c_b = np.broadcast_to(c, take.shape)[take].astype(np.int64)
@@ -57,8 +63,8 @@ def reads(M, N, ldr, rpg, TM, clip_columns=True):
     return np.concatenate(res), np.concatenate(gat)
 
 
-def check(M, N, ldr, rpg, TM):
-    res, gat = reads(M, N, ldr, rpg, TM)
+def check(M, N, ldr, rpg, TM, fmt):
+    res, gat = reads(M, N, ldr, rpg, TM, fmt=fmt)
     assert res.min() >= 0 and res.max() < (M - 1) * ldr + N, (M, N, ldr, rpg, TM, int(res.max()))
     assert gat.min() >= 0 and gat.max() < (M + rpg - 1) // rpg * N, (M, N, ldr, rpg, TM, int(gat.max()))
     # every output element's residual and gate value is read
@@ -73,14 +79,14 @@ GR_CASES = [c for c in _cases() if c[2] == "gate_residual"]
 def test_fuzz_shapes_read_inside_extents(case):
     i, fmt, _, M, N, K, _, rpg, pad = case
     # the fuzz runs the residual with ldr = N (exact rows) and the output with ldo = N + pad
-    check(M, N, N, rpg, tm_for(fmt, M, N))
+    check(M, N, N, rpg, tm_for(fmt, M, N), fmt)
 
 
 @pytest.mark.parametrize("fmt,M,N,ldr,rpg", [("fp4", 9216, 3072, 3072, 4608), ("fp4", 300, 576, 576, 7),
                                             ("fp8", 257, 320, 328, 129), ("mx8", 1, 64, 64, 1),
                                             ("nv4", 193, 1600, 1600, 193)])
 def test_chosen_shapes_read_inside_extents(fmt, M, N, ldr, rpg):
-    check(M, N, ldr, rpg, tm_for(fmt, M, N))
+    check(M, N, ldr, rpg, tm_for(fmt, M, N), fmt)
 
 
 def test_model_detects_reads_past_the_extents_without_the_column_clip():
