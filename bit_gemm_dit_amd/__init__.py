@@ -19,7 +19,6 @@ __all__ = [
     "dit_packed_weight_bytes", "dit_act_code_bytes", "dit_act_scale_bytes", "dit_pack_weights",
     "dit_quantize_act", "dit_quantize_act_noalloc", "dit_gemm_q4_epilogue", "dit_gemm_q4_epilogue_q4", "dit_gemm_q8_epilogue",
     "dit_gemm_epilogue", "dit_gemm_gate_residual", "gemm_gate_residual", "dit_gemm_epilogue_f32",
-    "dit_gemm_workspace_bytes", "dit_gemm_epilogue_ws", "dit_gemm_gate_residual_ws", "gemm_workspace",
     "dit_gated_silu_bf16", "dit_mfma_fp4_probe", "gated_silu", "mfma_fp4_probe",
     "dit_status_str", "dit_last_error", "pack_weights", "quantize_act", "gemm", "gemm_q4out", "linear",
     "library_path", "EXPORTED", "BLOB_MAGIC", "BLOB_VERSION", "blob_header", "check_blob", "save_packed",
@@ -81,11 +80,6 @@ _SIGS = {
     "dit_gemm_q8_epilogue": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _i, _p]),
     "dit_gemm_epilogue": (_i, [_i, _p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams), _p, _i, _p]),
     "dit_gemm_gate_residual": (_i, [_i, _p, _p, _p, _i, _i, _i, ctypes.POINTER(GateResidualParams), _p, _i, _p]),
-    "dit_gemm_workspace_bytes": (_sz, []),
-    "dit_gemm_epilogue_ws": (_i, [_i, _p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams), _p, _i, _p, _sz,
-                                  _p]),
-    "dit_gemm_gate_residual_ws": (_i, [_i, _p, _p, _p, _i, _i, _i, ctypes.POINTER(GateResidualParams), _p, _i, _p,
-                                       _sz, _p]),
     "dit_gemm_epilogue_f32": (_i, [_i, _p, _p, _p, _i, _i, _i, _i, ctypes.POINTER(RmsNormParams),
                                    ctypes.POINTER(GateResidualParams), _p, _i, _p]),
     "dit_gated_silu_bf16": (_i, [_p, _i, _i, _i, _p, _i, _p]),
@@ -174,24 +168,6 @@ def dit_gemm_gate_residual(fmt, a_codes, a_scales, w_packed, M, N, K, gr, out, l
     gp = ctypes.byref(gr) if gr is not None else None
     _check(_lib.dit_gemm_gate_residual(fmt, a_codes, a_scales, w_packed, M, N, K, gp, out, ldo, stream),
            "dit_gemm_gate_residual")
-
-
-def dit_gemm_workspace_bytes() -> int:
-    return _lib.dit_gemm_workspace_bytes()
-
-
-def dit_gemm_epilogue_ws(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, out, ldo, workspace, workspace_bytes,
-                         stream=None) -> None:
-    rp = ctypes.byref(rms) if rms is not None else None
-    _check(_lib.dit_gemm_epilogue_ws(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rp, out, ldo, workspace,
-                                     workspace_bytes, stream), "dit_gemm_epilogue_ws")
-
-
-def dit_gemm_gate_residual_ws(fmt, a_codes, a_scales, w_packed, M, N, K, gr, out, ldo, workspace, workspace_bytes,
-                              stream=None) -> None:
-    gp = ctypes.byref(gr) if gr is not None else None
-    _check(_lib.dit_gemm_gate_residual_ws(fmt, a_codes, a_scales, w_packed, M, N, K, gp, out, ldo, workspace,
-                                          workspace_bytes, stream), "dit_gemm_gate_residual_ws")
 
 
 def dit_gemm_epilogue_f32(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, gr, out_f32, ldo,
@@ -329,31 +305,14 @@ def quantize_act(x, fmt: int):
     return codes, scales
 
 
-def gemm_workspace(device="cuda"):
-    """A zeroed work space for the split-last-round GEMMs (``workspace=`` below) on the
-    current device.  Use one per stream: calls that share it must not overlap."""
-    import torch
-    nbytes = dit_gemm_workspace_bytes()
-    if nbytes == 0:
-        raise DitError(4, "dit_gemm_workspace_bytes")
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
-
-
-def gemm(codes, scales, blob, N: int, K: int, fmt: int, epi: int, rms: RmsNormParams | None = None, out=None,
-         workspace=None):
-    """Fused GEMM + epilogue on quantized activations; returns the bf16 output [M, N or N/2].
-    With a ``workspace`` (gemm_workspace()), tiles of a partly empty last round are split
-    along K over the idle compute units."""
+def gemm(codes, scales, blob, N: int, K: int, fmt: int, epi: int, rms: RmsNormParams | None = None, out=None):
+    """Fused GEMM + epilogue on quantized activations; returns the bf16 output [M, N or N/2]."""
     import torch
     M = codes.shape[1]
     width = N // 2 if epi == EPI_GATED_SILU else N
     if out is None:
         out = torch.empty((M, width), dtype=torch.bfloat16, device=codes.device)
-    if workspace is not None:
-        dit_gemm_epilogue_ws(fmt, codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi, rms,
-                             out.data_ptr(), _ld(out), workspace.data_ptr(),
-                             workspace.numel() * workspace.element_size(), _stream())
-    elif fmt == FMT_FP4:
+    if fmt == FMT_FP4:
         dit_gemm_q4_epilogue(codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, epi, rms,
                              out.data_ptr(), _ld(out), _stream())
     elif fmt == FMT_FP8 and epi != EPI_QK_RMSNORM:
@@ -385,29 +344,23 @@ def gemm_q4out(codes, scales, blob, N: int, K: int, epi: int, rms: RmsNormParams
 
 
 def gemm_gate_residual(codes, scales, blob, N: int, K: int, fmt: int, residual, gate, rows_per_gate: int,
-                       out=None, workspace=None):
+                       out=None):
     """out = residual + gate[row // rows_per_gate] * (A W^T), bf16 [M, N]; `out` may be
-    `residual` itself (an in-place update of the residual stream).  ``workspace``: as
-    for gemm."""
+    `residual` itself (an in-place update of the residual stream)."""
     import torch
     M = codes.shape[1]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=codes.device)
     gr = GateResidualParams(residual.data_ptr(), _ld(residual), gate.data_ptr(), rows_per_gate)
-    if workspace is not None:
-        dit_gemm_gate_residual_ws(fmt, codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, gr,
-                                  out.data_ptr(), _ld(out), workspace.data_ptr(),
-                                  workspace.numel() * workspace.element_size(), _stream())
-    else:
-        dit_gemm_gate_residual(fmt, codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, gr,
-                               out.data_ptr(), _ld(out), _stream())
+    dit_gemm_gate_residual(fmt, codes.data_ptr(), scales.data_ptr(), blob.data_ptr(), M, N, K, gr,
+                           out.data_ptr(), _ld(out), _stream())
     return out
 
 
-def linear(x, blob, N: int, fmt: int, epi: int, rms: RmsNormParams | None = None, out=None, workspace=None):
+def linear(x, blob, N: int, fmt: int, epi: int, rms: RmsNormParams | None = None, out=None):
     """The whole layer: quantize x on the fly, then the fused GEMM + epilogue."""
     codes, scales = quantize_act(x, fmt)
-    return gemm(codes, scales, blob, N, x.shape[1], fmt, epi, rms=rms, out=out, workspace=workspace)
+    return gemm(codes, scales, blob, N, x.shape[1], fmt, epi, rms=rms, out=out)
 
 
 def gated_silu(c, out=None):

@@ -181,8 +181,7 @@ namespace {
 // quantization of the output is written too (FP4 only), and out_bf16 may be null.
 dit_status gemm_any(int fmt, const void* a_codes, const void* a_scales, const void* w_packed, int M, int N, int K,
                     int epi, const dit_rmsnorm_params* rms, const dit_gate_residual_params* gr,
-                    void* out_bf16, int ldo, void* out_codes, void* out_scales, float* out_f32, void* stream,
-                    void* workspace = nullptr, size_t workspace_bytes = 0) {
+                    void* out_bf16, int ldo, void* out_codes, void* out_scales, float* out_f32, void* stream) {
   const bool quantized = out_codes != nullptr;
   if (!valid_fmt(fmt) || !a_codes || !a_scales || !w_packed || M <= 0 || N <= 0 || K <= 0 || !valid_epi(epi))
     return DIT_EINVAL;
@@ -218,21 +217,6 @@ dit_status gemm_any(int fmt, const void* a_codes, const void* a_scales, const vo
   if (rms && (!aligned16(rms->gamma_q) || !aligned16(rms->gamma_k))) return DIT_EALIGN;
   if (gr && (!aligned16(gr->residual) || !aligned16(gr->gate) || gr->ldr < N || gr->ldr % 8 != 0))
     return DIT_EALIGN;
-  if (workspace) {
-    if (!aligned(workspace, 256)) return DIT_EALIGN;
-    // the size depends on the device's compute units
-    const int cus = ditq::gemm_cus();
-    if (cus <= 0) {
-      const dit_status s = check_device();
-      return s != DIT_OK ? s : DIT_EDEVICE;
-    }
-    if (cus > ditq::kSplitMaxGrid || workspace_bytes < ditq::split_workspace_bytes(cus)) return DIT_EINVAL;
-    // the output (bf16 [M][ldo]) must lie outside the work space
-    const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + workspace_bytes;
-    const uintptr_t o0 = reinterpret_cast<uintptr_t>(out_bf16);
-    const uintptr_t o1 = o0 + 2 * ((size_t)(M - 1) * (size_t)ldo + width);
-    if (w0 < o1 && o0 < w1) return DIT_EINVAL;
-  }
   if (dit_status s = check_device()) return s;
   (void)hipGetLastError();
   ditq::RmsArgs r{};
@@ -243,7 +227,7 @@ dit_status gemm_any(int fmt, const void* a_codes, const void* a_scales, const vo
                                     static_cast<const uint8_t*>(w_packed), M, N, K, epi, rms ? &r : nullptr,
                                     gr ? &g : nullptr, static_cast<uint16_t*>(out_bf16), ldo,
                                     static_cast<uint8_t*>(out_codes), static_cast<uint8_t*>(out_scales), out_f32,
-                                    workspace, static_cast<hipStream_t>(stream)));
+                                    static_cast<hipStream_t>(stream)));
 }
 }  // namespace
 
@@ -292,30 +276,6 @@ dit_status dit_gemm_gate_residual(dit_fmt fmt_, const void* a_codes, const void*
   if (!gr || !out_bf16) return DIT_EINVAL;
   return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, DIT_EPI_GATE_RESIDUAL, nullptr, gr, out_bf16, ldo,
                   nullptr, nullptr, nullptr, stream);
-}
-
-size_t dit_gemm_workspace_bytes(void) {
-  const int cus = ditq::gemm_cus();
-  if (cus <= 0 || cus > ditq::kSplitMaxGrid) return 0;
-  return ditq::split_workspace_bytes(cus);
-}
-
-dit_status dit_gemm_epilogue_ws(dit_fmt fmt_, const void* a_codes, const void* a_scales, const void* w_packed,
-                                int M, int N, int K, dit_epi epi_, const dit_rmsnorm_params* rms, void* out_bf16,
-                                int ldo, void* workspace, size_t workspace_bytes, void* stream) {
-  const int fmt = raw(fmt_), epi = raw(epi_);
-  if (!out_bf16) return DIT_EINVAL;
-  return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, epi, rms, nullptr, out_bf16, ldo, nullptr, nullptr,
-                  nullptr, stream, workspace, workspace_bytes);
-}
-
-dit_status dit_gemm_gate_residual_ws(dit_fmt fmt_, const void* a_codes, const void* a_scales, const void* w_packed,
-                                     int M, int N, int K, const dit_gate_residual_params* gr, void* out_bf16,
-                                     int ldo, void* workspace, size_t workspace_bytes, void* stream) {
-  const int fmt = raw(fmt_);
-  if (!gr || !out_bf16) return DIT_EINVAL;
-  return gemm_any(fmt, a_codes, a_scales, w_packed, M, N, K, DIT_EPI_GATE_RESIDUAL, nullptr, gr, out_bf16, ldo,
-                  nullptr, nullptr, nullptr, stream, workspace, workspace_bytes);
 }
 
 dit_status dit_gemm_epilogue_f32(dit_fmt fmt_, const void* a_codes, const void* a_scales, const void* w_packed,

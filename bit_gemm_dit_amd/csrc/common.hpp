@@ -248,24 +248,9 @@ hipError_t launch_pack(int fmt, int epi, const uint16_t* w, int N, int K, int ld
 // EPI_GATE_RESIDUAL.  q_codes / q_scales (FP4 only): optional FP4 quantization of
 // the output (null: none); out may be null when q_codes is set.  out_f32 (debug, or
 // null): the fp32 values the bf16 store would round go there instead, [M][ldo] fp32.
-// workspace (or null): the split last round's work space, split_workspace_bytes(gemm_cus())
-// bytes whose flag area is zero (see below); null runs every tile whole.
 hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, const uint8_t* blob, int M, int N,
                        int K, int epi, const RmsArgs* rms, const ResidualArgs* gr, uint16_t* out, int ldo,
-                       uint8_t* q_codes, uint8_t* q_scales, float* out_f32, void* workspace, hipStream_t stream);
-// Workgroups of a GEMM launch on the current device (one per CU), or 0 if the query fails.
-int gemm_cus();
-
-// Work space of the split last round (gemm.hip).  Ready flags: one u32 per (workgroup,
-// wave) of up to kSplitMaxGrid workgroups, zero between calls; then, at u32 index
-// kSplitTimeoutWord, the count of flag waits that gave up.  Partial tiles: from byte
-// kSplitPartOffset, kSplitPartBytes per workgroup (4 waves x at most 256 fp32
-// accumulators x 64 lanes).
-constexpr int kSplitMaxGrid = 1024;
-constexpr int kSplitTimeoutWord = 4 * kSplitMaxGrid;
-constexpr size_t kSplitPartOffset = 32 * 1024;
-constexpr size_t kSplitPartBytes = 256 * 1024;
-inline size_t split_workspace_bytes(int cus) { return kSplitPartOffset + (size_t)cus * kSplitPartBytes; }
+                       uint8_t* q_codes, uint8_t* q_scales, float* out_f32, hipStream_t stream);
 
 // measurement kernels (measure.hip)
 hipError_t launch_gated_silu(const uint16_t* c, int M, int N, int ldc, uint16_t* out, int ldo,

@@ -54,7 +54,6 @@
 //   memory fence (the kernel orders its LDS accesses itself).
 // * Raw buffer loads return zeros past the end of a tensor, which clips ragged M
 //   and padded rows without branches; stores are predicated per row and column.
-#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -88,15 +87,11 @@ constexpr int kGroupM = 8;
 // F32: the debug form of the kernel, whose store writes the fp32 value the bf16 store
 // would round (a separate instantiation, so that the production kernels carry no
 // trace of it).
-// SPLIT: the form whose last round may split tiles along K (the _ws entry points; also a
-// separate instantiation: the schedule's extra state costs registers).
-template <int FMT_, int EPI_, int TM_, int RING_, int WLDS_, int HD_ = 0, int WL_ = 2, bool F32_ = false,
-          bool SPLIT_ = false>
+template <int FMT_, int EPI_, int TM_, int RING_, int WLDS_, int HD_ = 0, int WL_ = 2, bool F32_ = false>
 struct Tile {
   static constexpr int FMT = FMT_, EPI = EPI_, TM = TM_, RING = RING_, WLDS = WLDS_, HD = HD_;
-  static constexpr bool F32 = F32_, SPLIT = SPLIT_;
-  using Debug = Tile<FMT_, EPI_, TM_, RING_, WLDS_, HD_, WL_, true, false>;
-  using Split = Tile<FMT_, EPI_, TM_, RING_, WLDS_, HD_, WL_, false, true>;
+  static constexpr bool F32 = F32_;
+  using Debug = Tile<FMT_, EPI_, TM_, RING_, WLDS_, HD_, WL_, true>;
   static constexpr int WAVES_N = WL_, WAVES_M = 4 / WL_, TN = 8 / WL_, NW = 4, NT = 256;
   static constexpr int WN = 32 * TN, WM = 32 * TM;
   static constexpr int BN = WN * WAVES_N, BM = WM * WAVES_M;
@@ -199,11 +194,6 @@ struct Params {
   int n_heads;
   const float* a_tscale;      // NVFP4 tensor scales (device)
   const float* w_tscale;
-  // Split last round (null: every tile whole): ready flags and partial tiles, laid out as
-  // split_workspace_bytes describes; split_max bounds the parts of one tile.
-  uint32_t* ws_flag;
-  float* ws_part;
-  int split_max;
 };
 
 // Activation LDS rows are 64 bytes = 4 chunks of 16 bytes; chunk c of row r is
@@ -845,104 +835,6 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
-// ---------------------------------------------------------------- split last round
-// A part's accumulators in the work space: workgroup b's slot, wave w's quarter, then
-// per result tile (tn, tm) and lane 16 consecutive floats (each lane stores and loads
-// 64 contiguous bytes; a wave 4 KB per result tile).
-template <class T>
-__device__ __forceinline__ float* split_slot(const Params& p, int b, int wave, int lane) {
-  constexpr int kWave = T::TN * T::TM * 16 * 64;
-  static_assert(4 * kWave * 4 <= (int)kSplitPartBytes, "a partial tile fits its slot");
-  return p.ws_part + (size_t)b * (kSplitPartBytes / 4) + wave * kWave + lane * 16;
-}
-
-// Bound on the polls of one flag (each sleeps ~0.5 us and reads through to the device
-// scope): the wait ends within about a second even if the flag never rises, and the
-// give-up is counted in the work space.
-constexpr int kSplitSpinLimit = 1 << 19;
-
-// Every part of a split tile stores the wave's accumulators in its slot.  The parts
-// other than the owner then raise the wave's flag: the release fence makes the stores
-// visible at device scope before the flag (each XCD has its own L2).  The owner reads
-// its own slot back after the acquire fence in split_gather, whose wait for the
-// wave's outstanding memory operations covers these stores.
-template <class T>
-__device__ __forceinline__ void split_publish(const Params& p, v16f (&acc)[T::TN][T::TM], int wave, int lane,
-                                              bool raise_flag) {
-  float* dst = split_slot<T>(p, blockIdx.x, wave, lane);
-#pragma unroll
-  for (int tn = 0; tn < T::TN; ++tn)
-#pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm) {
-      __builtin_amdgcn_sched_barrier(0);     // one result tile at a time keeps register use low
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<v4f*>(dst + (tn * T::TM + tm) * 64 * 16 + 4 * g) =
-            v4f{acc[tn][tm][4 * g], acc[tn][tm][4 * g + 1], acc[tn][tm][4 * g + 2], acc[tn][tm][4 * g + 3]};
-    }
-  __builtin_amdgcn_sched_barrier(0);
-  if (raise_flag) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    if (lane == 0) __hip_atomic_store(p.ws_flag + 4 * blockIdx.x + wave, 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// dst = v, with the value placed in AGPRs, where the MFMAs leave the accumulators: the
-// epilogue then reads every accumulator from one register class (sums produced by
-// vector adds would otherwise stay in VGPRs, and the two classes together spill).
-// Device pass only, like pin_accumulators.
-__device__ __forceinline__ void acc_in_agprs(v16f& dst, const v16f& v) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("" : "=a"(dst) : "0"(v));
-#else
-  dst = v;
-#endif
-}
-
-// The tile's last part (its owner), after storing its own slot: wait for the flags
-// of parts 0 .. s-2 (workgroup x + 8 (j + q L) for part q), lower them again (so the
-// work space is ready for the next call), and set the accumulators to the sum of the
-// s partial tiles in part order.  The accumulators are rebuilt from memory rather than
-// added to, so that the publishing and the owning paths leave them in the same state.
-template <class T>
-__device__ __forceinline__ void split_gather(const Params& p, v16f (&acc)[T::TN][T::TM], int wave, int lane, int x,
-                                             int j, int L, int s) {
-  for (int q = 0; q < s - 1; ++q) {
-    uint32_t* flag = p.ws_flag + 4 * (x + 8 * (j + q * L)) + wave;
-    for (int n = 0;; ++n) {
-      const uint32_t f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__builtin_amdgcn_readfirstlane(f) != 0u) break;
-      if (n == kSplitSpinLimit) {
-        if (lane == 0) __hip_atomic_fetch_add(p.ws_flag + kSplitTimeoutWord, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(16);
-    }
-    if (lane == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#pragma unroll
-  for (int tn = 0; tn < T::TN; ++tn)
-#pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm) {
-      __builtin_amdgcn_sched_barrier(0);   // one result tile at a time
-      v16f sum;
-      for (int q = 0; q < s; ++q) {
-        const float* src = split_slot<T>(p, x + 8 * (j + q * L), wave, lane) + (tn * T::TM + tm) * 64 * 16;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const v4f v = *reinterpret_cast<const v4f*>(src + 4 * g);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sum[4 * g + e] = q == 0 ? v[e] : sum[4 * g + e] + v[e];
-        }
-      }
-      acc_in_agprs(acc[tn][tm], sum);
-    }
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 template <class T>
 __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[T::LDS_BYTES];
@@ -961,52 +853,22 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
   const int gx = (G - x + 7) >> 3;                 // workgroups on this XCD
   const int q = p.tiles / X, r = p.tiles % X;
   const int x0 = x * q + min(x, r), len = q + (x < r ? 1 : 0);
+  const int n_mine = jx < len ? (len - jx + gx - 1) / gx : 0;
+  if (n_mine == 0) return;                         // uniform over the workgroup
+  auto tile_of = [&](int i, int& n0, int& m0) __attribute__((always_inline)) {
+    int tmi, tni;
+    tile_coords(x0 + jx + (i < n_mine ? i : n_mine - 1) * gx, p.tiles_m, p.tiles_n, tmi, tni);
+    n0 = tni * T::BN;
+    m0 = tmi * T::BM;
+  };
+
   // k-steps per tile, rounded up to whole unrolled groups of the weight ring.  The
   // steps past K add exact zeros: their activation code and scale offsets lie past
   // the end of those buffers, where raw buffer loads return zeros (the range check
   // covers voffset + soffset), and E2M1 / E4M3 zeros times any finite weight code
   // (the rows that follow in the blob, or zeros past its end) are zero.
-  constexpr int SPG = T::STEPS_PER_GROUP;
-  const int nks = (p.K / T::KSTEP + SPG - 1) / SPG * SPG;
-  // Units of work.  The XCD's gx workgroups take R = len / gx full rounds of whole
-  // tiles.  The L = len % gx tiles of its last round would leave gx - L workgroups idle
-  // for a whole tile; with a work space each of them is split along K into s parts
-  // (whole unrolled groups of k-steps), part q of leftover tile j going to workgroup
-  // j + q*L.  Part s - 1 sits on the highest workgroup id of the tile: it owns the
-  // tile.  Every part stores its fp32 partial sums and raises a flag; the owner sums
-  // the parts in part order and runs the epilogue.  A workgroup waits only for
-  // workgroups of lower id, which the in-order dispatcher has already started, so the
-  // waits end even when the grid is not resident all at once.
-  const int R = len / gx, L = len - R * gx;
-  int s = 1;
-  if constexpr (T::SPLIT)
-    if (p.split_max > 1 && L > 0) s = min(min(gx / L, p.split_max), nks / SPG);
-  const int nk_part = s > 1 ? (nks / SPG + s - 1) / s * SPG : nks;
-  if (s > 1) s = (nks + nk_part - 1) / nk_part;                   // every part non-empty
-  const bool has_part = T::SPLIT && s > 1 && jx < L * s;   // this workgroup's last unit is a part
-  const int n_mine = R + (has_part || (s == 1 && jx < L) ? 1 : 0);
-  if (n_mine == 0) return;                         // uniform over the workgroup
-  // The part: its tile (leftover tile j = jx mod L), k-steps [part_k0, part_k1) of part
-  // q = jx / L, and unit index part_at (no unit has it when this workgroup has no part).
-  // What only the end of the kernel needs (L, s, j, q) is packed into one word.
-  const int tail_j = L > 0 ? jx % L : 0, tail_q = L > 0 ? jx / L : 0;
-  const int part_at = has_part ? R : -1;
-  const int part_tile = x0 + R * gx + tail_j;
-  const int part_k0 = tail_q * nk_part, part_k1 = min(nks, part_k0 + nk_part);
-  const uint32_t part_info = (uint32_t)L | ((uint32_t)s << 8) | ((uint32_t)tail_j << 16) | ((uint32_t)tail_q << 24);
-  const int full_base = x0 + jx;
-  // Unit i (clamped to the last one, which the loads that run ahead past it repeat):
-  // its tile's origin and k-steps [k0, k1).
-  auto unit_of = [&](int i, int& n0, int& m0, int& k0, int& k1) __attribute__((always_inline)) {
-    i = i < n_mine ? i : n_mine - 1;
-    const bool part = T::SPLIT && i == part_at;
-    int tmi, tni;
-    tile_coords(part ? part_tile : full_base + i * gx, p.tiles_m, p.tiles_n, tmi, tni);
-    n0 = tni * T::BN;
-    m0 = tmi * T::BM;
-    k0 = part ? part_k0 : 0;
-    k1 = part ? part_k1 : nks;
-  };
+  const int nks = (p.K / T::KSTEP + T::STEPS_PER_GROUP - 1) / T::STEPS_PER_GROUP * T::STEPS_PER_GROUP;
+  const int units = nks * T::CH;                                  // units per tile
   const uint32_t wgroup = (uint32_t)(p.K / 64) * T::FRAG;         // blob bytes of one 32-row group
   const uint32_t a_panel = (uint32_t)p.M * kRowBytes;            // bytes of one K panel of activation codes
   const auto a_rsrc = make_rsrc(p.a_codes, p.a_bytes);
@@ -1019,17 +881,18 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
 
   // Weight cursor: tile and unit that the next weight loads fetch.  Lane L of
   // fragment (group g, unit u) sits at g * wgroup + u * FRAG + L * FRAG/64.
-  int wc_i = 0, wc_u = 0, wc_end = 0;
+  int wc_i = 0, wc_u = 0;
   uint32_t wbase = 0;
   auto set_w_tile = [&](int i) __attribute__((always_inline)) {
-    int n0, m0, k0, k1;
-    unit_of(i, n0, m0, k0, k1);
+    int n0, m0;
+    tile_of(i, n0, m0);
     wbase = (uint32_t)(n0 / 32 + wn * T::TN + T::WLDS) * wgroup + (uint32_t)(T::FRAG / 64) * lane;
-    wc_u = k0 * T::CH;
-    wc_end = k1 * T::CH;
   };
   auto advance_w = [&]() __attribute__((always_inline)) {
-    if (++wc_u == wc_end) set_w_tile(++wc_i);
+    if (++wc_u == units) {
+      wc_u = 0;
+      set_w_tile(++wc_i);
+    }
   };
   // Activation cursor: tile and k-step of the next stage.  Activation copy c of
   // wave w = 16 token rows of a K panel (contiguous in the panel-major layout),
@@ -1043,7 +906,7 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
   // of weight scale records, waves 2 and 3 repeating waves 0 and 1 so that every wave
   // issues the same operations.  Rows past M read other data; their results are
   // never stored.
-  int ac_i = 0, ac_ks = 0, ac_end = 0;
+  int ac_i = 0, ac_ks = 0;
   uint32_t a_off = 0;
   [[maybe_unused]] uint32_t w_off[T::WCK > 0 ? T::WCK : 1];
   [[maybe_unused]] uint32_t as_off = 0, ws_off = 0;
@@ -1052,10 +915,8 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
   [[maybe_unused]] const uint32_t sc_step = ws_wave ? ws_step : as_step;
   [[maybe_unused]] const int sc_dst = ws_wave ? T::WS_OFF : T::AS_OFF;
   auto set_a_tile = [&](int i) __attribute__((always_inline)) {
-    int n0, m0, k0, k1;
-    unit_of(i, n0, m0, k0, k1);
-    ac_ks = k0;
-    ac_end = k1;
+    int n0, m0;
+    tile_of(i, n0, m0);
     // the swizzle of row 16k + L/4 depends on L only, so copy c of the wave is copy 0
     // moved by c * 1 KB
     const int rr = 16 * (wave * T::ACKP) + (lane >> 2);
@@ -1103,7 +964,10 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
     }
   };
   auto advance_a = [&]() __attribute__((always_inline)) {
-    if (++ac_ks == ac_end) set_a_tile(++ac_i);
+    if (++ac_ks == nks) {
+      ac_ks = 0;
+      set_a_tile(++ac_i);
+    }
   };
   // Copies that only keep the operation count of a prologue half-step uniform.
   auto pad = [&](auto n_c) __attribute__((always_inline)) {
@@ -1229,54 +1093,30 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
     cur = nxt;
   };
 
-  // The k-steps of unit i, from zero accumulators.
-  auto run_unit = [&](int i, int k0, int k1) __attribute__((always_inline)) {
+  constexpr int SPG = T::STEPS_PER_GROUP;
+  for (int i = 0; i < n_mine; ++i) {
     static_for<0, SPG>([&](auto si_c) __attribute__((always_inline)) {
       step(si_c, std::integral_constant<bool, decltype(si_c)::value == 0>{});
     });
-    for (int gi = k0 + SPG; gi < k1; gi += SPG)
+    for (int gi = SPG; gi < nks; gi += SPG)
       static_for<0, SPG>([&](auto si_c) __attribute__((always_inline)) { step(si_c, std::false_type{}); });
-  };
-  // Whole tiles.  A split unit is always a workgroup's last, and it runs after this
-  // loop, in code of its own: its partial sums reach the accumulators through vector
-  // adds, and inside the loop those values would have to share registers with the
-  // ones the MFMAs write.
-  for (int i = 0; i < (has_part ? R : n_mine); ++i) {
-    int n0, m0, k0, k1;
-    unit_of(i, n0, m0, k0, k1);
-    run_unit(i, k0, k1);
+    int n0, m0;
+    tile_of(i, n0, m0);
     epilogue<T>(p, acc, n0 + wn * T::WN, m0 + wm * T::WM, lane, wn, wm, lds);
-  }
-  if constexpr (T::SPLIT) {
-    if (has_part) {
-      int n0, m0, k0, k1;
-      unit_of(R, n0, m0, k0, k1);
-      run_unit(R, k0, k1);
-      const int pl = part_info & 0xFF, ps = (part_info >> 8) & 0xFF, pj = (part_info >> 16) & 0xFF;
-      const bool owner = (int)(part_info >> 24) == ps - 1;
-      split_publish<T>(p, acc, wave, lane, !owner);
-      if (owner) {
-        split_gather<T>(p, acc, wave, lane, blockIdx.x & 7, pj, pl, ps);
-        epilogue<T>(p, acc, n0 + wn * T::WN, m0 + wm * T::WM, lane, wn, wm, lds);
-      }
-    }
   }
   wait_vmcnt<0>();     // no copy into this workgroup's LDS may outlive it
 }
 
 // Tiles are dealt to one persistent workgroup per CU.
-int query_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-    return n;
-  return 0;
-}
 int cu_count() {
   static int count = 0;
   if (count == 0) {
-    const int n = query_cus();
-    count = n > 0 ? n : 256;
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      count = n;
+    else
+      count = 256;
   }
   return count;
 }
@@ -1302,41 +1142,10 @@ const EnvFlags& env_flags() {
   return flags;
 }
 
-// Rounds of the persistent schedule, counting a split last round as 1/s of a round:
-// per XCD (the fullest, ceil(tiles / 8) tiles on cus / 8 workgroups), R full rounds and L
-// leftover tiles split into s = min(gx / L, 8, k-step groups) parts.
-double schedule_rounds(long tiles, int cus, int groups, bool split, int* s_out = nullptr) {
-  const long len = (tiles + 7) / 8, gx = cus / 8 > 0 ? cus / 8 : 1;
-  const long R = len / gx, L = len % gx;
-  long s = 1;
-  if (split && L > 0) {
-    s = std::min(std::min(gx / L, 8L), (long)groups);
-    if (s > 1) {
-      const long per = (groups + s - 1) / s;
-      s = (groups + per - 1) / per;
-    }
-    if (s < 1) s = 1;
-  }
-  if (s_out) *s_out = (int)s;
-  return L == 0 ? (double)R : s > 1 ? R + 1.0 / s : R + 1.0;
-}
-
 const char* fmt_name(int f) { return f == FMT_FP4 ? "FP4" : f == FMT_FP8 ? "FP8" : f == FMT_MX8 ? "MXFP8" : "NVFP4"; }
 const char* epi_name(int e) {
   return e == EPI_IDENTITY ? "identity" : e == EPI_GATED_SILU ? "gated-SiLU" : e == EPI_QK_RMSNORM ? "QK-RMSNorm"
          : e == EPI_GELU_TANH ? "GELU-tanh" : "gated residual";
-}
-
-// Whether the schedule of sched_of splits any tile: some XCD's last round is partly
-// empty and its idle workgroups can take at least a second part per leftover tile.
-bool any_split(long tiles, int G, int nks, int spg) {
-  const int X = G < 8 ? G : 8;
-  for (int x = 0; x < X; ++x) {
-    const long len = tiles / X + (x < tiles % X ? 1 : 0), gx = (G - x + 7) / 8;
-    const long L = len % gx;
-    if (L > 0 && std::min(std::min(gx / L, 8L), (long)(nks / spg)) > 1) return true;
-  }
-  return false;
 }
 
 template <class T>
@@ -1344,28 +1153,16 @@ hipError_t launch(Params& p, hipStream_t stream) {
   p.tiles_m = (p.M + T::BM - 1) / T::BM;
   p.tiles_n = padded_rows(p.N) / T::BN;
   p.tiles = p.tiles_m * p.tiles_n;
-  // with a work space, every CU takes part however few the tiles, and the split form
-  // of the kernel runs when its schedule splits anything (else the plain one)
-  const bool ws = p.ws_flag != nullptr;
-  const int nks = (p.K / T::KSTEP + T::STEPS_PER_GROUP - 1) / T::STEPS_PER_GROUP * T::STEPS_PER_GROUP;
-  const int grid = ws || p.tiles >= cu_count() ? cu_count() : p.tiles;
-  const bool split = ws && p.out_f32 == nullptr && any_split(p.tiles, grid, nks, T::STEPS_PER_GROUP);
-  p.split_max = split ? 8 : 1;
-  if (env_flags().log) {
-    const int groups = (p.K / T::KSTEP + T::STEPS_PER_GROUP - 1) / T::STEPS_PER_GROUP;
-    int sp = 1;
-    const double rounds = schedule_rounds(p.tiles, grid, groups, split, &sp);
+  const int grid = p.tiles < cu_count() ? p.tiles : cu_count();
+  if (env_flags().log)
     std::fprintf(stderr,
                  "ditq gemm: %s %s M=%d N=%d K=%d | tile 256x%d, %s grid, TM=%d, ring %d, LDS weight groups %d, "
-                 "%d LDS stages of %d B | %d tiles on %d workgroups, %.3f rounds, last round split %d-way%s\n",
+                 "%d LDS stages of %d B | %d tiles on %d workgroups, %.3f rounds%s\n",
                  fmt_name(T::FMT), epi_name(T::EPI), p.M, p.N, p.K, T::BM, T::WAVES_N == 4 ? "4 x 1" : "2 x 2",
-                 T::TM, T::RING, T::WLDS, T::STAGES, T::STAGE, p.tiles, grid, rounds, sp,
+                 T::TM, T::RING, T::WLDS, T::STAGES, T::STAGE, p.tiles, grid, (double)p.tiles / grid,
                  p.out_f32 ? ", fp32 debug store" : "");
-  }
   if (p.out_f32 != nullptr)
     hipLaunchKernelGGL(gemm_kernel<typename T::Debug>, dim3(grid), dim3(T::NT), 0, stream, p);
-  else if (split)
-    hipLaunchKernelGGL(gemm_kernel<typename T::Split>, dim3(grid), dim3(T::NT), 0, stream, p);
   else
     hipLaunchKernelGGL(gemm_kernel<T>, dim3(grid), dim3(T::NT), 0, stream, p);
   return hipGetLastError();
@@ -1375,13 +1172,13 @@ hipError_t launch(Params& p, hipStream_t stream) {
 // accumulators leave too few registers, and the spilling kernel measured 5-8 %
 // slower even where it saves a round of tiles: M = 2048 and 4096 with N = 16384).
 // On the 2 x 2 grid 192 or 256 (TM = 3 or 4 per wave), whichever takes less time:
-// rounds of tiles over the CUs (a split last round counting 1/s) times the time of one
-// tile, a 256-token tile taking 1.35x a 192-token one (measured 1.34-1.37x:
-// QK-RMSNorm head_dim 128, 4 against 3 rounds, 100.1 against 102.9 us; head_dim 256, 5
-// against 3 rounds, 154.5 against 125.7 us; the gated residual, 3 against 2 rounds,
-// 232.9 against 207.8 us).  FP8 and MXFP8 always take 192: with 256 their operand
-// registers spill.  Weight ring: 8 units on the FP4 4 x 1 grid when the k-steps come
-// in groups of 4, else 4 (every 2 x 2 grid, FP8 and MXFP8).
+// rounds of tiles over the CUs times the time of one tile, a 256-token tile taking
+// 1.35x a 192-token one (measured 1.34-1.37x: QK-RMSNorm head_dim 128, 4 against 3
+// rounds, 100.1 against 102.9 us; head_dim 256, 5 against 3 rounds, 154.5 against
+// 125.7 us; the gated residual, 3 against 2 rounds, 232.9 against 207.8 us).  FP8
+// and MXFP8 always take 192: with 256 their operand registers spill.  Weight ring: 8
+// units on the FP4 4 x 1 grid when the k-steps come in groups of 4, else 4 (every 2 x 2
+// grid, FP8 and MXFP8).
 template <int FMT, int EPI, int HD = 0, int WLDS = wlds_for(FMT)>
 hipError_t launch_cfg(Params& p, hipStream_t stream) {
   // 4 x 1 wave grid: 64 features x BM tokens per wave, every weight through registers.
@@ -1407,11 +1204,8 @@ hipError_t launch_cfg(Params& p, hipStream_t stream) {
     } else {
       const int cus = cu_count();
       const long tn = padded_rows(p.N) / 256;
-      const bool split = p.ws_flag != nullptr;
-      const int groups = (nks + 1) / 2;              // ring 4: k-steps in groups of 2
-      const double r3 = schedule_rounds((p.M + 191) / 192 * tn, cus, groups, split);
-      const double r4 = schedule_rounds((p.M + 255) / 256 * tn, cus, groups, split);
-      bool tm3 = r3 * 1.0 < r4 * 1.35;
+      const long r3 = ((p.M + 191) / 192 * tn + cus - 1) / cus, r4 = ((p.M + 255) / 256 * tn + cus - 1) / cus;
+      bool tm3 = r3 * 20 < r4 * 27;
       if (env_flags().force_bm) tm3 = env_flags().force_bm == 192;
       // 2 x 2 grid: a 4-unit weight ring (2 of the 4 groups come through LDS, so a
       // deeper ring only adds registers: with 8 units the QK-RMSNorm kernels spill
@@ -1447,11 +1241,9 @@ hipError_t launch_epi(Params& p, int epi, const RmsArgs* rms, hipStream_t stream
 
 }  // namespace
 
-int gemm_cus() { return query_cus(); }
-
 hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, const uint8_t* blob, int M, int N,
                        int K, int epi, const RmsArgs* rms, const ResidualArgs* gr, uint16_t* out, int ldo,
-                       uint8_t* q_codes, uint8_t* q_scales, float* out_f32, void* workspace, hipStream_t stream) {
+                       uint8_t* q_codes, uint8_t* q_scales, float* out_f32, hipStream_t stream) {
   const int Np = padded_rows(N);
   Params p{};
   p.a_codes = a_codes;
@@ -1474,10 +1266,6 @@ hipError_t launch_gemm(int fmt, const uint8_t* a_codes, const void* a_scales, co
     p.w_tscale = reinterpret_cast<const float*>(blob + kNvTensorScaleOff);
   }
   p.ws_bytes = (uint32_t)blob_scale_bytes(fmt, Np, K);
-  if (workspace) {
-    p.ws_flag = static_cast<uint32_t*>(workspace);
-    p.ws_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSplitPartOffset);
-  }
   if (gr) {
     p.residual = gr->residual;
     p.ldr = gr->ldr;

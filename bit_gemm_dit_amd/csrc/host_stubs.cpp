@@ -30,10 +30,9 @@ hipError_t launch_amax_bf16(const uint16_t*, int, int, int, uint32_t*, uint32_t*
 }
 hipError_t launch_pack(int, int, const uint16_t*, int, int, int, uint8_t*, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_gemm(int, const uint8_t*, const void*, const uint8_t*, int, int, int, int, const RmsArgs*,
-                       const ResidualArgs*, uint16_t*, int, uint8_t*, uint8_t*, float*, void*, hipStream_t) {
+                       const ResidualArgs*, uint16_t*, int, uint8_t*, uint8_t*, float*, hipStream_t) {
   return hipErrorNoDevice;
 }
-int gemm_cus() { return 0; }
 hipError_t launch_gated_silu(const uint16_t*, int, int, int, uint16_t*, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_mfma_probe(int, int, unsigned long long*, hipStream_t) { return hipErrorNoDevice; }
 

@@ -325,32 +325,6 @@ dit_status dit_gemm_gate_residual(dit_fmt fmt, const void* a_codes, const void* 
                                   int M, int N, int K, const dit_gate_residual_params* gr,
                                   void* out_bf16, int ldo, void* stream);
 
-/* ---------------------------------------------------------------- the same with a split last round
- * The operation of dit_gemm_epilogue / dit_gemm_gate_residual (the big GEMM with its
- * small op fused before the one store: page "How fal made Ideogram V4 6x faster",
- * paragraphs 3-4), scheduled differently.  The kernel deals output tiles to one
- * workgroup per compute unit in rounds; when the tiles do not fill the last round,
- * the tiles of that round are split along K over the idle compute units, and each
- * tile's parts are summed (fp32, in a fixed order) before its epilogue.  The result
- * is deterministic, but its fp32 rounding differs from the unsplit call's: the
- * split tiles sum the same products in another grouping.
- * workspace: device memory of dit_gemm_workspace_bytes() bytes for the current
- * device, 256-byte aligned, owned by the caller, that must be all zero before its
- * first use (each completed call leaves it ready for the next one).  Calls that
- * share one workspace must not run at the same time (use one per stream).
- * workspace NULL runs the call exactly as the entry point without _ws.
- * Errors: as the entry point without _ws; a workspace that is not 256-byte
- * aligned: DIT_EALIGN; workspace_bytes below dit_gemm_workspace_bytes(), or a
- * workspace that overlaps the output: DIT_EINVAL. */
-size_t dit_gemm_workspace_bytes(void);   /* 0 if the device cannot be queried */
-dit_status dit_gemm_epilogue_ws(dit_fmt fmt, const void* a_codes, const void* a_scales, const void* w_packed,
-                                int M, int N, int K, dit_epi epi, const dit_rmsnorm_params* rms,
-                                void* out_bf16, int ldo, void* workspace, size_t workspace_bytes, void* stream);
-dit_status dit_gemm_gate_residual_ws(dit_fmt fmt, const void* a_codes, const void* a_scales,
-                                     const void* w_packed, int M, int N, int K,
-                                     const dit_gate_residual_params* gr, void* out_bf16, int ldo,
-                                     void* workspace, size_t workspace_bytes, void* stream);
-
 /* Static, NUL-terminated description of a status code. */
 const char* dit_status_str(dit_status status);
 

@@ -332,46 +332,3 @@ def test_quantize_noalloc_validation():
     if not _has_gpu():
         for fmt in (1, 2, 3, 4):
             assert lib.dit_quantize_act_noalloc(fmt, A, 4, 256, 256, B, C, None) == EDEVICE
-
-
-WS = 0x1000000           # a fake 256-byte aligned work space address
-
-
-def _ws(fmt=1, a=A, s=B, w=C, M=64, N=512, K=256, epi=1, rms=None, out=D, ldo=256, ws=WS, ws_bytes=1 << 28):
-    return ditq._lib.dit_gemm_epilogue_ws(fmt, a, s, w, M, N, K, epi, ctypes.byref(rms) if rms else None, out, ldo,
-                                          ws, ws_bytes, None)
-
-
-def _gr_ws(fmt=1, M=64, N=512, K=256, gr="default", out=D, ldo=512, ws=WS, ws_bytes=1 << 28):
-    if gr == "default":
-        gr = ditq.GateResidualParams(E, 512, F, 32)
-    return ditq._lib.dit_gemm_gate_residual_ws(fmt, A, B, C, M, N, K, ctypes.byref(gr) if gr else None, out, ldo,
-                                               ws, ws_bytes, None)
-
-
-def test_split_workspace_entry_points_validation():
-    # every check of the entry point without _ws comes first
-    assert _ws(out=None) == EINVAL
-    assert _ws(fmt=5) == EINVAL
-    assert _ws(epi=2) == EINVAL                                      # RMSNorm without params
-    assert _ws(K=320) == EUNSUP
-    assert _ws(ldo=255) == EALIGN
-    assert _gr_ws(gr=None) == EINVAL
-    assert _gr_ws(out=None) == EINVAL
-    # the work space: 256-byte aligned
-    assert _ws(ws=WS + 128) == EALIGN
-    assert _gr_ws(ws=WS + 16) == EALIGN
-    if not _has_gpu():
-        # no device: the size query says 0, and a work space cannot be sized
-        assert ditq._lib.dit_gemm_workspace_bytes() == 0
-        assert _ws() == EDEVICE
-        assert _gr_ws() == EDEVICE
-        # a NULL work space is the entry point without _ws
-        assert _ws(ws=None, ws_bytes=0) == EDEVICE
-        assert _gr_ws(ws=None, ws_bytes=0) == EDEVICE
-    else:
-        need = ditq._lib.dit_gemm_workspace_bytes()
-        assert need > 0
-        assert _ws(ws_bytes=need - 1) == EINVAL                     # too small
-        assert _gr_ws(ws_bytes=need - 1) == EINVAL
-        assert _ws(ws=D - 0x100, ws_bytes=need) == EINVAL           # overlaps the output
