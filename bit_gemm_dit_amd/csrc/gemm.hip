@@ -49,6 +49,9 @@
 // * Persistent: one workgroup per CU walks its share of the tiles, and the loads
 //   run ahead across tile boundaries, so the next tile's first steps are in flight
 //   while the current tile's epilogue runs.
+// * Activation fragments are read from LDS into registers ahead of their MFMAs: one
+//   half-step ahead (two buffers), or, for FP4 on the 4 x 1 grid, two half-steps
+//   ahead (three buffers), so that no MFMA waits for LDS data.
 // * Every half-step issues the same number of memory operations, so each wait is a
 //   constant count of outstanding operations, and the workgroup barrier carries no
 //   memory fence (the kernel orders its LDS accesses itself).
@@ -87,11 +90,15 @@ constexpr int kGroupM = 8;
 // F32: the debug form of the kernel, whose store writes the fp32 value the bf16 store
 // would round (a separate instantiation, so that the production kernels carry no
 // trace of it).
-template <int FMT_, int EPI_, int TM_, int RING_, int WLDS_, int HD_ = 0, int WL_ = 2, bool F32_ = false>
+// FB: activation fragment buffers in registers.  2: each half-step reads the fragments
+// the next half-step consumes.  3 (the block-scaled formats): each half-step reads the
+// fragments consumed two half-steps later, so no MFMA waits for LDS data.
+template <int FMT_, int EPI_, int TM_, int RING_, int WLDS_, int HD_ = 0, int WL_ = 2, bool F32_ = false,
+          int FB_ = 2>
 struct Tile {
-  static constexpr int FMT = FMT_, EPI = EPI_, TM = TM_, RING = RING_, WLDS = WLDS_, HD = HD_;
+  static constexpr int FMT = FMT_, EPI = EPI_, TM = TM_, RING = RING_, WLDS = WLDS_, HD = HD_, FB = FB_;
   static constexpr bool F32 = F32_;
-  using Debug = Tile<FMT_, EPI_, TM_, RING_, WLDS_, HD_, WL_, true>;
+  using Debug = Tile<FMT_, EPI_, TM_, RING_, WLDS_, HD_, WL_, true, FB_>;
   static constexpr int WAVES_N = WL_, WAVES_M = 4 / WL_, TN = 8 / WL_, NW = 4, NT = 256;
   static constexpr int WN = 32 * TN, WM = 32 * TM;
   static constexpr int BN = WN * WAVES_N, BM = WM * WAVES_M;
@@ -109,7 +116,9 @@ struct Tile {
   static constexpr bool SC1 = MX && !NV && WL_ == 4;
   static constexpr int TND = TN - WLDS;                        // weight groups loaded into registers
   static constexpr int UNIT_LOADS = TND * FRAG_LOADS;
-  static constexpr int STEPS_PER_GROUP = RING / CH;            // k-steps per unrolled group
+  // k-steps per unrolled group: whole turns of the weight ring (and, with three fragment
+  // buffers, of those too: lcm(RING, 3) units)
+  static constexpr int STEPS_PER_GROUP = FB == 3 ? (RING % 3 == 0 ? RING : 3 * RING) / CH : RING / CH;
   static constexpr int GROUP_BYTES = FRAG * CH;                // one 32-row group per k-step (2 KB)
   // LDS stage: weight codes of the LDS groups | activation codes | activation scale
   // words | weight scale records
@@ -140,8 +149,9 @@ struct Tile {
   // Ring depth: at most 5 stages, as many as fit in LDS, and few enough that the
   // wait for a stage stays within vmcnt's range (63 operations in flight).
   static constexpr int STAGES_VM = (63 - OPS_H0) / OPS_STEP + 2;
-  static constexpr int STAGES = STAGES_FIT < 5 ? (STAGES_FIT < STAGES_VM ? STAGES_FIT : STAGES_VM)
-                                               : (5 < STAGES_VM ? 5 : STAGES_VM);
+  static constexpr int STAGES_CAP = FB == 3 ? 6 : 5;          // three buffers read a stage one step earlier
+  static constexpr int STAGES = STAGES_FIT < STAGES_CAP ? (STAGES_FIT < STAGES_VM ? STAGES_FIT : STAGES_VM)
+                                                        : (STAGES_CAP < STAGES_VM ? STAGES_CAP : STAGES_VM);
   static constexpr int JUNK_OFF = STAGES * STAGE;            // target of the prologue's padding copies
   static constexpr int RED_OFF = JUNK_OFF + 1024;            // per-token partial sums of squares
   static constexpr int LDS_BYTES = RED_OFF + RED_BYTES;
@@ -153,7 +163,8 @@ struct Tile {
   static constexpr int WAIT_UNIT = MX ? (RING - 2) / 2 * OPS_STEP : (RING - 2) * OPS_H1;
   //   stage g+1 (needed at the barrier of step g): issued in the second half of
   //   step g + 1 - STAGES; steps g+2-STAGES .. g-1 and the first half of g follow.
-  static constexpr int WAIT_STAGE = (STAGES - 2) * OPS_STEP + OPS_H0;
+  //   With three fragment buffers stage g+2 (read from the next step on): one step less.
+  static constexpr int WAIT_STAGE = (STAGES - (FB == 3 ? 3 : 2)) * OPS_STEP + OPS_H0;
   static constexpr int WAIT_BARRIER = MX ? (WAIT_UNIT < WAIT_STAGE ? WAIT_UNIT : WAIT_STAGE) : WAIT_STAGE;
   // prologue: the half-steps before step 0 that issue stage 0 .. STAGES-1 and unit 0 .. RING-2
   static constexpr int PRO_HALVES = MX ? (2 * STAGES - 1 > RING - 1 ? 2 * STAGES - 1 : RING - 1)
@@ -166,6 +177,7 @@ struct Tile {
   static_assert(ACK % APANELS == 0, "whole activation copies per panel");
   static_assert(WLDS == 0 || GROUP_BYTES == 2048, "LDS weight groups are copied as two 1 KB halves");
   static_assert(RING % CH == 0 && RING >= 4, "ring holds whole k-steps");
+  static_assert(FB == 2 || (FB == 3 && MX), "three fragment buffers: the two-unit k-step of the block-scaled path");
   static_assert(WAIT_UNIT < 64 && WAIT_STAGE < 64, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024 && STAGES >= 3, "LDS");
   static_assert(TN * TM * 16 <= 256, "accumulators fit in the AGPRs");
@@ -977,7 +989,9 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
   };
 
   WUnit<T> ring[T::RING];
-  AFrag<T> fa, fb;
+  AFrag<T> fr[T::FB];
+  AFrag<T>& fa = fr[0];
+  AFrag<T>& fb = fr[1];
   Scales<T> sc, sn;
   v16f acc[T::TN][T::TM];
 
@@ -1008,11 +1022,13 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
       }
     }
   });
-  // Stage 0 went out in the second half of step -S; everything issued after that
-  // half may still be in flight.
+  // Stage 0 went out in the second half of step -S, stage 1 in that of step 1 - S;
+  // everything issued after the half of the last stage needed (stage 1 with three
+  // fragment buffers, which read both stages before step 0's MFMAs) may still be in
+  // flight.
   constexpr int PRO_WAIT = []() {
     int n = 0;
-    for (int h = -2 * S + 2; h < 0; ++h) {
+    for (int h = -2 * S + (T::FB == 3 ? 4 : 2); h < 0; ++h) {
       const bool second = (h & 1) != 0;
       n += T::MX ? (second ? T::OPS_H1 : T::OPS_H0) : (second ? T::OPS_H1 : 0);
     }
@@ -1023,6 +1039,7 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
   barrier();
   load_scales<T>(sc, lds, wn, wm, lane);
   load_act<T, 0>(fa, lds, wn, wm, lane);
+  if constexpr (T::FB == 3) load_act<T, 1>(fb, lds, wn, wm, lane);
   select_scales<T>(sc, lane);
 
   // One k-step.  Step g computes from LDS slot g mod S (byte offset `cur`) and
@@ -1039,7 +1056,37 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_kernel(Params p) {
     constexpr int SI = decltype(si_c)::value;
     constexpr bool ZERO = decltype(zero_c)::value;
     const int nxt = cur + T::STAGE == S * T::STAGE ? 0 : cur + T::STAGE;
-    if constexpr (T::MX) {
+    if constexpr (T::FB == 3) {
+      // unit U = 2 step + J uses fragment buffer U mod 3 and reads unit U + 2's (stage
+      // g+1) into buffer (U + 2) mod 3, the one the previous half-step consumed
+      constexpr int u0 = (2 * SI) % T::RING, u1 = u0 + 1;
+      constexpr int l0 = (u0 + T::RING - 1) % T::RING, l1 = u0;
+      constexpr int f0 = (2 * SI) % 3, f1 = (2 * SI + 1) % 3, f2 = (2 * SI + 2) % 3;
+      wait_vmcnt<T::WAIT_UNIT>();                  // unit u0 has landed
+      __builtin_amdgcn_sched_barrier(0);
+      load_scales<T>(sn, lds + nxt, wn, wm, lane);
+      load_act<T, 0>(fr[f2], lds + nxt, wn, wm, lane);
+      load_unit<T>(ring[l0], w_rsrc, wbase, wc_u, (int)wgroup);
+      mfma_part<T, 0, 0, T::TM, ZERO>(acc, ring[u0], fr[f0], sc);
+      spread_vmem<T::TN * T::TM * T::MFMA_PER_UNIT, T::UNIT_LOADS>();
+      pin_accumulators<T>(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      advance_w();
+      wait_vmcnt<T::WAIT_BARRIER, true>();         // stage g+2 and unit u1 have landed; reads of `cur` done
+      barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      load_act<T, 1>(fr[f0], lds + nxt, wn, wm, lane);   // reads before the copies (see below)
+      copy_stage(cur);
+      load_unit<T>(ring[l1], w_rsrc, wbase, wc_u, (int)wgroup);
+      mfma_part<T, 1, 0, T::TM, false>(acc, ring[u1], fr[f1], sc);
+      spread_vmem<T::TN * T::TM * T::MFMA_PER_UNIT, T::NCOPY + T::UNIT_LOADS>();
+      pin_accumulators<T>(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      advance_w();
+      advance_a();
+      sc = sn;
+      select_scales<T>(sc, lane);
+    } else if constexpr (T::MX) {
       constexpr int u0 = (2 * SI) % T::RING, u1 = u0 + 1;
       constexpr int l0 = (u0 + T::RING - 1) % T::RING, l1 = u0;
       wait_vmcnt<T::WAIT_UNIT>();                  // unit u0 has landed
@@ -1199,6 +1246,15 @@ hipError_t launch_cfg(Params& p, hipStream_t stream) {
   } else {
     const int nks = p.K / 128;
     if constexpr (grid41) {
+      // three fragment buffers with a 4-unit ring when the k-steps fill its 6-step
+      // groups (K = 768, 1536, 3072, 12288, ...): same-box A/B against the two-buffer
+      // 8-unit ring, 10 alternations, outputs identical: gated-SiLU 119.7 -> 117.0 and
+      // 119.1 -> 116.6 us, GELU 113.2 -> 111.9 us, identity 126.6 -> 123.7 us.  With an
+      // 8-unit ring the three buffers spill 22-51 VGPRs; with 6 units they measured
+      // slower (121.5 us).  On the 2 x 2 grid they spill (FP4, MXFP8) or measured
+      // slower (NVFP4 gated-SiLU 374.7 vs 354.2 us), so they stay on this grid.
+      using T3 = Tile<FMT, EPI, 6, 4, 0, HD, 4, false, 3>;
+      if (nks % T3::STEPS_PER_GROUP == 0) return launch<T3>(p, stream);
       if (nks % 4 != 0) return launch<Tile<FMT, EPI, 6, 4, 0, HD, 4>>(p, stream);
       return launch<Tile<FMT, EPI, 6, 8, 0, HD, 4>>(p, stream);
     } else {
