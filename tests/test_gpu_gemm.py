@@ -155,6 +155,12 @@ SMALL = [
     ("qkv_rmsnorm_hd128", "nv4", "qk_rmsnorm", 257, None, 512, 2),
     ("qkv_rmsnorm_hd256", "nv4", "qk_rmsnorm", 65, None, 512, 1),
     ("mlp_gelu_tanh", "nv4", "gelu_tanh", 70, 512, 256, None),
+    # FP4 on the 4 x 1 grid with three fragment buffers (K / 128 a multiple of 6): one to
+    # three 6-step groups per tile, a ragged M tail, N not a multiple of 256
+    ("mlp_gated_silu", "fp4", "gated_silu", 257, 1408, 768, None),
+    ("mlp_gated_silu", "fp4", "identity", 385, 832, 1536, None),
+    ("mlp_gelu_tanh", "fp4", "gelu_tanh", 200, 576, 2304, None),
+    ("mlp_gated_silu", "fp4", "gated_silu", 63, 512, 3072, None),
 ]
 
 
