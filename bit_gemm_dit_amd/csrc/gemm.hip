@@ -550,99 +550,6 @@ __device__ __forceinline__ void spread_vmem() {
 __device__ __forceinline__ void barrier();
 __device__ __forceinline__ void wait_lds();
 
-// The epilogue of token tile tm (32 token rows of the wave) for the element-wise small ops
-// (identity, gated-SiLU, GELU, the gated residual): reads only acc[.][tm].
-template <class T>
-__device__ __forceinline__ void epilogue_rows(const Params& p, v16f (&acc)[T::TN][T::TM], int n0w, int m0w,
-                                              int lane, int tm) {
-  const int h = lane >> 5, l32 = lane & 31;
-  __builtin_amdgcn_sched_barrier(0);     // one token tile at a time keeps register use low
-  const int row = m0w + 32 * tm + l32;
-  const bool ok = row < p.M;
-  float sa = 1.0f;
-  if constexpr (T::FMT == FMT_FP8) sa = reinterpret_cast<const float*>(p.a_scales)[ok ? row : p.M - 1];
-  if constexpr (T::EPI != EPI_GATED_SILU) {
-#pragma unroll
-    for (int tn = 0; tn < T::TN; ++tn) {
-      __builtin_amdgcn_sched_barrier(0);   // one result tile at a time
-      float v[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = acc[tn][tm][r];
-      if constexpr (T::FMT == FMT_FP8) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const v4f sw = *reinterpret_cast<const v4f*>(
-              reinterpret_cast<const float*>(p.w_scales) + n0w + 32 * tn + 8 * g + 4 * h);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[4 * g + i] *= sa * sw[i];
-        }
-      }
-      if constexpr (T::EPI == EPI_GELU_TANH) {
-        gelu_tanh16(v);
-      }
-      if constexpr (T::EPI == EPI_GATE_RESIDUAL) {
-        // this lane's 16 columns are 4 runs of 4 (n0 + 8g + 4h + i): the residual
-        // as four 8-byte reads, the gate row of the token's sample as four 16-byte
-        // reads.  Rows past M read row M - 1, and a 32-column result tile at or past
-        // N (the padding of the last tile; N is a multiple of 64, so a tile is
-        // wholly in or out) reads nothing: every read stays inside residual[M][ldr]
-        // and gate[ceil(M / rows_per_gate)][N], and neither kind of result is
-        // stored.  The test is uniform over the wave: a per-lane test measured dozens
-        // of register spills more.  The 4-bit formats skip the reads of such a tile,
-        // the 8-bit ones read the last 32 columns instead (each form is the one that
-        // spills fewer registers in that format's kernels).
-        const int rr = ok ? row : p.M - 1;
-        constexpr bool kSkip = is_fp4_codes(T::FMT);
-        const bool live = kSkip ? n0w + 32 * tn < p.N : true;
-        const int col = (kSkip ? n0w + 32 * tn : __builtin_amdgcn_readfirstlane(min(n0w + 32 * tn, p.N - 32))) +
-                        4 * h;
-        const uint16_t* rp = p.residual + (size_t)rr * p.ldr + col;
-        const float* gp = p.gate + (size_t)(rr / p.rows_per_gate) * p.N + col;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 rv = {0u, 0u};
-          v4f gv = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (live) {
-            rv = *reinterpret_cast<const uint2*>(rp + 8 * g);
-            gv = *reinterpret_cast<const v4f*>(gp + 8 * g);
-          }
-          v[4 * g + 0] = __builtin_fmaf(gv[0], v[4 * g + 0], bf16_lo(rv.x));
-          v[4 * g + 1] = __builtin_fmaf(gv[1], v[4 * g + 1], bf16_hi(rv.x));
-          v[4 * g + 2] = __builtin_fmaf(gv[2], v[4 * g + 2], bf16_lo(rv.y));
-          v[4 * g + 3] = __builtin_fmaf(gv[3], v[4 * g + 3], bf16_hi(rv.y));
-        }
-      }
-      store_tile<T>(p, row, ok, n0w + 32 * tn, p.N, h, v);
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < T::TN / 2; ++q) {
-      __builtin_amdgcn_sched_barrier(0);   // one gate/up pair at a time
-      float gate[16], up[16], v[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        gate[r] = acc[2 * q][tm][r];
-        up[r] = acc[2 * q + 1][tm][r];
-      }
-      if constexpr (T::FMT == FMT_FP8) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float* ws = reinterpret_cast<const float*>(p.w_scales) + n0w + 64 * q + 8 * g + 4 * h;
-          const v4f sg = *reinterpret_cast<const v4f*>(ws);
-          const v4f su = *reinterpret_cast<const v4f*>(ws + 32);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            gate[4 * g + i] *= sa * sg[i];
-            up[4 * g + i] *= sa * su[i];
-          }
-        }
-      }
-      silu_mul16(gate, up, v);
-      store_tile<T>(p, row, ok, n0w / 2 + 32 * q, p.N / 2, h, v);
-    }
-  }
-}
-
 template <class T>
 __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::TM], int n0w, int m0w, int lane,
                                          int wn, int wm, uint8_t* lds) {
@@ -659,7 +566,93 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
   }
   if constexpr (T::EPI != EPI_QK_RMSNORM) {
 #pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm) epilogue_rows<T>(p, acc, n0w, m0w, lane, tm);
+    for (int tm = 0; tm < T::TM; ++tm) {
+      __builtin_amdgcn_sched_barrier(0);     // one token tile at a time keeps register use low
+      const int row = m0w + 32 * tm + l32;
+      const bool ok = row < p.M;
+      float sa = 1.0f;
+      if constexpr (T::FMT == FMT_FP8) sa = reinterpret_cast<const float*>(p.a_scales)[ok ? row : p.M - 1];
+      if constexpr (T::EPI != EPI_GATED_SILU) {
+#pragma unroll
+        for (int tn = 0; tn < T::TN; ++tn) {
+          __builtin_amdgcn_sched_barrier(0);   // one result tile at a time
+          float v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = acc[tn][tm][r];
+          if constexpr (T::FMT == FMT_FP8) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const v4f sw = *reinterpret_cast<const v4f*>(
+                  reinterpret_cast<const float*>(p.w_scales) + n0w + 32 * tn + 8 * g + 4 * h);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[4 * g + i] *= sa * sw[i];
+            }
+          }
+          if constexpr (T::EPI == EPI_GELU_TANH) {
+            gelu_tanh16(v);
+          }
+          if constexpr (T::EPI == EPI_GATE_RESIDUAL) {
+            // this lane's 16 columns are 4 runs of 4 (n0 + 8g + 4h + i): the residual
+            // as four 8-byte reads, the gate row of the token's sample as four 16-byte
+            // reads.  Rows past M read row M - 1, and a 32-column result tile at or past
+            // N (the padding of the last tile; N is a multiple of 64, so a tile is
+            // wholly in or out) reads nothing: every read stays inside residual[M][ldr]
+            // and gate[ceil(M / rows_per_gate)][N], and neither kind of result is
+            // stored.  The test is uniform over the wave: a per-lane test measured dozens
+            // of register spills more.  The 4-bit formats skip the reads of such a tile,
+            // the 8-bit ones read the last 32 columns instead (each form is the one that
+            // spills fewer registers in that format's kernels).
+            const int rr = ok ? row : p.M - 1;
+            constexpr bool kSkip = is_fp4_codes(T::FMT);
+            const bool live = kSkip ? n0w + 32 * tn < p.N : true;
+            const int col = (kSkip ? n0w + 32 * tn : __builtin_amdgcn_readfirstlane(min(n0w + 32 * tn, p.N - 32))) +
+                            4 * h;
+            const uint16_t* rp = p.residual + (size_t)rr * p.ldr + col;
+            const float* gp = p.gate + (size_t)(rr / p.rows_per_gate) * p.N + col;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              uint2 rv = {0u, 0u};
+              v4f gv = {0.0f, 0.0f, 0.0f, 0.0f};
+              if (live) {
+                rv = *reinterpret_cast<const uint2*>(rp + 8 * g);
+                gv = *reinterpret_cast<const v4f*>(gp + 8 * g);
+              }
+              v[4 * g + 0] = __builtin_fmaf(gv[0], v[4 * g + 0], bf16_lo(rv.x));
+              v[4 * g + 1] = __builtin_fmaf(gv[1], v[4 * g + 1], bf16_hi(rv.x));
+              v[4 * g + 2] = __builtin_fmaf(gv[2], v[4 * g + 2], bf16_lo(rv.y));
+              v[4 * g + 3] = __builtin_fmaf(gv[3], v[4 * g + 3], bf16_hi(rv.y));
+            }
+          }
+          store_tile<T>(p, row, ok, n0w + 32 * tn, p.N, h, v);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < T::TN / 2; ++q) {
+          __builtin_amdgcn_sched_barrier(0);   // one gate/up pair at a time
+          float gate[16], up[16], v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            gate[r] = acc[2 * q][tm][r];
+            up[r] = acc[2 * q + 1][tm][r];
+          }
+          if constexpr (T::FMT == FMT_FP8) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const float* ws = reinterpret_cast<const float*>(p.w_scales) + n0w + 64 * q + 8 * g + 4 * h;
+              const v4f sg = *reinterpret_cast<const v4f*>(ws);
+              const v4f su = *reinterpret_cast<const v4f*>(ws + 32);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                gate[4 * g + i] *= sa * sg[i];
+                up[4 * g + i] *= sa * su[i];
+              }
+            }
+          }
+          silu_mul16(gate, up, v);
+          store_tile<T>(p, row, ok, n0w / 2 + 32 * q, p.N / 2, h, v);
+        }
+      }
+    }
   } else {
     // Per-head QK-RMSNorm.  A head is HW = head_dim / (the wave's columns) waves
     // wide: one wave (2 x 2 grid, head_dim 128), two (2 x 2 grid with head_dim 256,
