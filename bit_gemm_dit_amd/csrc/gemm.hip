@@ -1268,6 +1268,16 @@ hipError_t launch_cfg(Params& p, hipStream_t stream) {
       // 3-24 VGPRs, and same-box A/B measured 4 units faster or level: QK-RMSNorm
       // head_dim 128 93.7 vs 96.9 us, 256 118.7 vs 119.9 us, the gated residual
       // 179.1 vs 179.9 us)
+      // The gated residual (K = 12288 in the DiT MLP down projection) with every weight
+      // group in registers and three fragment buffers when the k-steps fill 6-step
+      // groups: same-box A/B 176.1 vs 181.7 us, outputs identical (the same layout
+      // measured slower for QK-RMSNorm head_dim 128: 95.1 vs 91.9 us).
+      if constexpr (EPI == EPI_GATE_RESIDUAL) {
+        if (nks % 6 == 0) {
+          if (tm3) return launch<Tile<FMT, EPI, 3, 4, 0, HD, 2, false, 3>>(p, stream);
+          return launch<Tile<FMT, EPI, 4, 4, 0, HD, 2, false, 3>>(p, stream);
+        }
+      }
       if (tm3) return launch<Tile<FMT, EPI, 3, 4, WLDS, HD>>(p, stream);
       return launch<Tile<FMT, EPI, 4, 4, WLDS, HD>>(p, stream);
     }

@@ -287,6 +287,10 @@ GR = [  # fmt, M, N, K, rows_per_gate, in_place
     ("mx8", 200, 768, 512, 64, False),
     ("mx8", 70, 256, 1024, 1000, True),
     ("nv4", 130, 512, 512, 50, False),
+    # FP4 with every weight group in registers and three fragment buffers (K / 128 a
+    # multiple of 6)
+    ("fp4", 300, 576, 768, 100, False),
+    ("fp4", 129, 1024, 1536, 7, True),
 ]
 
 
