@@ -181,6 +181,7 @@ def run_gpu(args):
         },
     }
     if not args.no_fusion_compare:
+        res["kernels"].update(time_quantizer_back_to_back(ditq, torch, wl, sets, quant_bytes, args))
         res["kernels"].update(time_quantized_output(ditq, torch, wl, sets, epi, args))
         res["kernels"].update(time_unfused_epilogue(ditq, torch, wl, d, sets, epi, args))
     if not args.no_power:
@@ -191,6 +192,50 @@ def run_gpu(args):
     if args.all_configs:
         res["other_configs"] = time_other_configs(ditq, torch, args)
     return res, d
+
+
+def time_quantizer_back_to_back(ditq, torch, wl, sets, quant_bytes, args):
+    """The FP4 quantizer launched n times back to back between one event pair (no
+    per-launch event gap, no GEMM write-back in flight), beside a plain device copy
+    that moves the same bytes (half read, half written) under the same rotation over
+    the input sets: the copy is the rate HBM gives a streaming kernel of this size."""
+    M, K = wl.M, wl.K
+    sptr = torch.cuda.current_stream().cuda_stream
+    n = max(40, args.steps // 2)
+    half = quant_bytes // 2 // 16 * 16
+    srcs = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in sets]
+    dsts = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in sets]
+    for t in srcs:
+        t.fill_(1)
+
+    def quantize(i):
+        x, _, codes, scales, _ = sets[i % len(sets)]
+        ditq.dit_quantize_act(ditq.FMT_FP4, x.data_ptr(), M, K, K, codes.data_ptr(), scales.data_ptr(), sptr)
+
+    def copy(i):
+        dsts[i % len(sets)].copy_(srcs[i % len(sets)])
+
+    out = {}
+    for name, fn in (("quant", quantize), ("copy", copy)):
+        for i in range(n // 2):
+            fn(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = a.elapsed_time(b) / n * 1e3
+    del srcs, dsts
+    q_gbps = quant_bytes / (out["quant"] * 1e-6) / 1e9
+    c_gbps = 2 * half / (out["copy"] * 1e-6) / 1e9
+    return {
+        "quant_fp4_back_to_back_us": round(out["quant"], 2),
+        "quant_fp4_back_to_back_hbm_frac": round(q_gbps / HBM_GBPS, 4),
+        "copy_same_bytes_us": round(out["copy"], 2),
+        "copy_same_bytes_hbm_frac": round(c_gbps / HBM_GBPS, 4),
+        "quant_fp4_rate_vs_copy": round(q_gbps / c_gbps, 4),
+    }
 
 
 def time_quantized_output(ditq, torch, wl, sets, epi, args):
