@@ -1229,9 +1229,10 @@ hipError_t launch(Params& p, hipStream_t stream) {
 template <int FMT, int EPI, int HD = 0, int WLDS = wlds_for(FMT)>
 hipError_t launch_cfg(Params& p, hipStream_t stream) {
   // 4 x 1 wave grid: 64 features x BM tokens per wave, every weight through registers.
-  // Measured faster than the 2 x 2 grid for FP4 (headline 122 vs 129 us) and FP8
-  // (CFG-pair identity 316 vs 325 us): no weight row is loaded by two waves, so the
-  // vector memory path carries less per k-step and CU.  MXFP8 and NVFP4 measured no
+  // Measured faster than the 2 x 2 grid with half its weight groups through LDS, for
+  // FP4 (headline 122 vs 129 us) and FP8 (CFG-pair identity 316 vs 325 us): no weight
+  // row is loaded by two waves, so the vector memory path carries less per k-step and
+  // CU.  (FP4 with three fragment buffers takes the 2 x 2 grid again, below.)  MXFP8 and NVFP4 measured no
   // faster and keep the 2 x 2 grid.  So does the gated residual, whose epilogue
   // spills on the 4 x 1 grid, and so does QK-RMSNorm: on the 4 x 1 grid a head spans
   // two or four waves (the epilogue handles it), but FP4 measured slower there
@@ -1246,15 +1247,18 @@ hipError_t launch_cfg(Params& p, hipStream_t stream) {
   } else {
     const int nks = p.K / 128;
     if constexpr (grid41) {
-      // three fragment buffers with a 4-unit ring when the k-steps fill its 6-step
-      // groups (K = 768, 1536, 3072, 12288, ...): same-box A/B against the two-buffer
-      // 8-unit ring, 10 alternations, outputs identical: gated-SiLU 119.7 -> 117.0 and
-      // 119.1 -> 116.6 us, GELU 113.2 -> 111.9 us, identity 126.6 -> 123.7 us.  With an
-      // 8-unit ring the three buffers spill 22-51 VGPRs; with 6 units they measured
-      // slower (121.5 us).  On the 2 x 2 grid they spill (FP4, MXFP8) or measured
-      // slower (NVFP4 gated-SiLU 374.7 vs 354.2 us), so they stay on this grid.
-      using T3 = Tile<FMT, EPI, 6, 4, 0, HD, 4, false, 3>;
-      if (nks % T3::STEPS_PER_GROUP == 0) return launch<T3>(p, stream);
+      // When the k-steps fill 6-step groups (K = 768, 1536, 3072, 12288, ...): the
+      // 2 x 2 grid with every weight group in registers, a 4-unit ring and three
+      // fragment buffers (192-token tiles, the gated residual's layout).  Each wave
+      // reads half the tile's token rows from LDS (24 KB per k-step and CU against
+      // the 4 x 1 grid's 48 KB), while the two waves of a row band both load its
+      // weights (16 KB more per k-step and CU through the vector memory path).
+      // Same-box A/B against the 4 x 1 grid's three-buffer kernel (itself 2-3 %
+      // faster than that grid's two-buffer kernel), outputs identical, two boxes, 10
+      // and 14 alternations: gated-SiLU 117.3 -> 115.3 and 118.1 -> 115.7 us, GELU
+      // 112.1 -> 109.3 and 111.6 -> 108.7 us, identity 124.8 -> 122.6 us (identity
+      // and GELU spill 4 VGPRs there).  Other K: the 4 x 1 grid, two buffers.
+      if (nks % 6 == 0) return launch<Tile<FMT, EPI, 3, 4, 0, HD, 2, false, 3>>(p, stream);
       if (nks % 4 != 0) return launch<Tile<FMT, EPI, 6, 4, 0, HD, 4>>(p, stream);
       return launch<Tile<FMT, EPI, 6, 8, 0, HD, 4>>(p, stream);
     } else {

@@ -155,12 +155,15 @@ SMALL = [
     ("qkv_rmsnorm_hd128", "nv4", "qk_rmsnorm", 257, None, 512, 2),
     ("qkv_rmsnorm_hd256", "nv4", "qk_rmsnorm", 65, None, 512, 1),
     ("mlp_gelu_tanh", "nv4", "gelu_tanh", 70, 512, 256, None),
-    # FP4 on the 4 x 1 grid with three fragment buffers (K / 128 a multiple of 6): one to
-    # three 6-step groups per tile, a ragged M tail, N not a multiple of 256
+    # FP4 identity / gated-SiLU / GELU with K / 128 a multiple of 6: the 2 x 2 grid with
+    # every weight group in registers and three fragment buffers; one to four 6-step
+    # groups per tile, a ragged M tail, M = 1, N not a multiple of 256, N = 64
     ("mlp_gated_silu", "fp4", "gated_silu", 257, 1408, 768, None),
     ("mlp_gated_silu", "fp4", "identity", 385, 832, 1536, None),
     ("mlp_gelu_tanh", "fp4", "gelu_tanh", 200, 576, 2304, None),
     ("mlp_gated_silu", "fp4", "gated_silu", 63, 512, 3072, None),
+    ("mlp_gated_silu", "fp4", "gated_silu", 1, 256, 768, None),
+    ("mlp_gated_silu", "fp4", "identity", 33, 64, 768, None),
 ]
 
 
