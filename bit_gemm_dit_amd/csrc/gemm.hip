@@ -31,17 +31,20 @@
 //   FP4, at the f16 MFMA rate.
 // * A workgroup of 4 waves (one per SIMD) computes a 256 (features) x BM (tokens)
 //   tile, on one of two wave grids:
-//   - 4 x 1 (FP4 and FP8 with the identity, gated-SiLU and GELU epilogues): wave wn
-//     owns 64 features x all BM tokens (2 x 6 result tiles of 32 x 32, BM = 192).
-//     No weight row is needed by two waves, so every weight fragment is loaded
-//     straight into a ring of registers several 64-K steps ahead, and only the
-//     activation tile is shared.
+//   - 4 x 1 (FP8 with the identity, gated-SiLU and GELU epilogues; FP4 with those
+//     where K / 128 is not a multiple of 6): wave wn owns 64 features x all BM
+//     tokens (2 x 6 result tiles of 32 x 32, BM = 192).  No weight row is needed by
+//     two waves, so every weight fragment is loaded straight into a ring of
+//     registers several 64-K steps ahead, and only the activation tile is shared.
 //   - 2 x 2 (the other formats and epilogues): wave (wn, wm) owns 128 features x
 //     BM/2 tokens (4 x TM result tiles, TM = 3 or 4).  A head of QK-RMSNorm is then
 //     one or two waves wide.  Of each wave's 4 weight row groups, FP4, NVFP4 and
 //     FP8 stage 2 through LDS (one copy per workgroup, read by the two waves of a
 //     row band) and load 2 into the register ring; MXFP8 loads all 4 into
-//     registers.
+//     registers, and so do FP4 identity, gated-SiLU, GELU and the gated residual
+//     where K / 128 is a multiple of 6 (each wave then reads half the tile's token
+//     rows from LDS, at the price of the two waves of a row band both loading its
+//     weights).
 //   The blob holds every fragment in the lane order of the MFMA operand, so no
 //   reshuffle is needed on either path.  The activation tile goes through LDS, in
 //   a ring of stages filled by direct-to-LDS buffer loads together with the step's
@@ -50,8 +53,9 @@
 //   run ahead across tile boundaries, so the next tile's first steps are in flight
 //   while the current tile's epilogue runs.
 // * Activation fragments are read from LDS into registers ahead of their MFMAs: one
-//   half-step ahead (two buffers), or, for FP4 on the 4 x 1 grid, two half-steps
-//   ahead (three buffers), so that no MFMA waits for LDS data.
+//   half-step ahead (two buffers), or, for the FP4 kernels with every weight group
+//   in registers, two half-steps ahead (three buffers), so that no MFMA waits for
+//   LDS data.
 // * Every half-step issues the same number of memory operations, so each wait is a
 //   constant count of outstanding operations, and the workgroup barrier carries no
 //   memory fence (the kernel orders its LDS accesses itself).
@@ -1222,8 +1226,9 @@ hipError_t launch(Params& p, hipStream_t stream) {
 // rounds of tiles over the CUs times the time of one tile, a 256-token tile taking
 // 1.35x a 192-token one (measured 1.34-1.37x: QK-RMSNorm head_dim 128, 4 against 3
 // rounds, 100.1 against 102.9 us; head_dim 256, 5 against 3 rounds, 154.5 against
-// 125.7 us; the gated residual, 3 against 2 rounds, 232.9 against 207.8 us).  FP8
-// and MXFP8 always take 192: with 256 their operand registers spill.  Weight ring: 8
+// 125.7 us; the gated residual, 3 against 2 rounds, 232.9 against 207.8 us).  FP8,
+// MXFP8 and FP4 identity / gated-SiLU / GELU always take 192: with 256 their operand
+// registers spill.  Weight ring: 8
 // units on the FP4 4 x 1 grid when the k-steps come in groups of 4, else 4 (every 2 x 2
 // grid, FP8 and MXFP8).
 template <int FMT, int EPI, int HD = 0, int WLDS = wlds_for(FMT)>
