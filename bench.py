@@ -38,6 +38,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import threading
 import time
@@ -54,11 +55,23 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_fp4_mlp_gated_silu.t
 GEMM_SRC = os.path.join(ROOT, "bit_gemm_dit_amd", "csrc", "gemm.hip")
 
 
+def code_only(text: str) -> str:
+    """C++ source without its comments, trailing blanks and empty lines, so that an
+    edit of the comments alone leaves the hash of the kernel source unchanged (the
+    sources hold no string literal with a comment marker in it)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash() -> str:
+    """Hash of the GEMM kernel's code (gemm.hip + common.hpp, comments excluded): the
+    counter summaries record it, and the traffic they give is used only while it
+    still matches."""
     h = hashlib.sha256()
     for f in (GEMM_SRC, os.path.join(ROOT, "bit_gemm_dit_amd", "csrc", "common.hpp")):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -42,8 +42,9 @@
 //     FP8 stage 2 through LDS (one copy per workgroup, read by the two waves of a
 //     row band) and load 2 into the register ring; MXFP8 loads all 4 into
 //     registers, and so do FP4 identity, gated-SiLU, GELU and the gated residual
-//     where K / 128 is a multiple of 6 (each wave then reads half the tile's token
-//     rows from LDS, at the price of the two waves of a row band both loading its
+//     where K / 128 is a multiple of 6, and FP4 QK-RMSNorm head_dim 128 in
+//     192-token tiles (each wave then reads only its half of the tile's token rows
+//     from LDS, at the price of the two waves of a row band both loading its
 //     weights).
 //   The blob holds every fragment in the lane order of the MFMA operand, so no
 //   reshuffle is needed on either path.  The activation tile goes through LDS, in
@@ -1279,8 +1280,14 @@ hipError_t launch_cfg(Params& p, hipStream_t stream) {
       // 179.1 vs 179.9 us)
       // The gated residual (K = 12288 in the DiT MLP down projection) with every weight
       // group in registers and three fragment buffers when the k-steps fill 6-step
-      // groups: same-box A/B 176.1 vs 181.7 us, outputs identical (the same layout
-      // measured slower for QK-RMSNorm head_dim 128: 95.1 vs 91.9 us).
+      // groups: same-box A/B 176.1 vs 181.7 us, outputs identical.  QK-RMSNorm
+      // head_dim 128 with 192-token tiles: every weight group in registers with two
+      // fragment buffers (three spill 8 VGPRs and measured slower, 97.9 us): each wave
+      // reads only its half of the token rows from LDS; same-box A/B on two boxes,
+      // outputs identical: 94.5 -> 91.9 and 85.8 -> 83.6 us.
+      if constexpr (EPI == EPI_QK_RMSNORM && HD == 128) {
+        if (tm3) return launch<Tile<FMT, EPI, 3, 4, 0, HD>>(p, stream);
+      }
       if constexpr (EPI == EPI_GATE_RESIDUAL) {
         if (nks % 6 == 0) {
           if (tm3) return launch<Tile<FMT, EPI, 3, 4, 0, HD, 2, false, 3>>(p, stream);

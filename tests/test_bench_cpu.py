@@ -40,7 +40,9 @@ def test_source_hash_covers_the_gemm_sources(tmp_path, monkeypatch):
     src.write_text(open(bench.GEMM_SRC).read())
     monkeypatch.setattr(bench, "GEMM_SRC", str(src))
     h0 = bench.kernel_source_hash()
-    src.write_text(src.read_text() + "\n// changed\n")
+    src.write_text(src.read_text() + "\n// a comment only\n")
+    assert bench.kernel_source_hash() == h0
+    src.write_text(src.read_text() + "\nconstexpr int kChanged = 1;\n")
     assert bench.kernel_source_hash() != h0
 
 
@@ -56,3 +58,12 @@ def test_oracle_rate_runs_for_every_format_and_epilogue():
         d = make_inputs(name, seed=1, **kw)
         r = bench.oracle_rate(d, fmt, epi, 0.05)
         assert r["value"] > 0 and r["kind"] == "oracle" and r["unit"] == "TFLOP/s", (name, fmt, epi, r)
+
+
+def test_kernel_hash_ignores_comments_only():
+    """The counter summaries stay valid across comment edits, not across code edits."""
+    import bench
+    src = "int a = 1;  // one\n/* block\n comment */\nint b = 2;\n\n// trailing\n"
+    assert bench.code_only(src) == "int a = 1;\nint b = 2;"
+    assert bench.code_only(src.replace("// one", "// first")) == bench.code_only(src)
+    assert bench.code_only(src.replace("b = 2", "b = 3")) != bench.code_only(src)

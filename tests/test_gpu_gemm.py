@@ -131,6 +131,7 @@ SMALL = [
     ("mlp_gated_silu", "fp4", "identity", 63, 256, 256, None),
     ("qkv_rmsnorm_hd128", "fp4", "qk_rmsnorm", 300, None, 512, 2),
     ("qkv_rmsnorm_hd128", "fp4", "qk_rmsnorm", 5, None, 256, 1),
+    ("qkv_rmsnorm_hd128", "fp4", "qk_rmsnorm", 257, None, 1536, 3),
     ("qkv_rmsnorm_hd256", "fp4", "qk_rmsnorm", 130, None, 512, 1),
     ("qkv_rmsnorm_hd256", "fp4", "qk_rmsnorm", 70, None, 768, 3),
     ("fp8_cfg_pair", "fp8", "identity", 300, 768, 512, None),
