@@ -1238,8 +1238,8 @@ hipError_t launch_cfg(Params& p, hipStream_t stream) {
   // Measured faster than the 2 x 2 grid with half its weight groups through LDS, for
   // FP4 (headline 122 vs 129 us) and FP8 (CFG-pair identity 316 vs 325 us): no weight
   // row is loaded by two waves, so the vector memory path carries less per k-step and
-  // CU.  (FP4 with three fragment buffers takes the 2 x 2 grid again, below.)  MXFP8 and NVFP4 measured no
-  // faster and keep the 2 x 2 grid.  So does the gated residual, whose epilogue
+  // CU.  (FP4 with three fragment buffers takes the 2 x 2 grid again, below.)  MXFP8
+  // and NVFP4 measured no faster and keep the 2 x 2 grid.  So does the gated residual, whose epilogue
   // spills on the 4 x 1 grid, and so does QK-RMSNorm: on the 4 x 1 grid a head spans
   // two or four waves (the epilogue handles it), but FP4 measured slower there
   // (head_dim 128: 109.6 vs 102 us; head_dim 256: 156 vs 127 us, where the 2 x 2
