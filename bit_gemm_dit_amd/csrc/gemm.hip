@@ -124,9 +124,10 @@ struct Tile {
   // as cold code, so that the k-loop runs straight through without taken branches.
   // Same-box A/B on three boxes, outputs identical: the FP4 gated-SiLU kernel with
   // three fragment buffers 1.2 % faster (117.2 -> 115.8, 114.6 -> 113.7, 121.8 ->
-  // 120.4 us); the identity and GELU kernels of that family 1-2 % slower, and in the
-  // other kernels the changed layout moves register allocation (QK-RMSNorm with
-  // 256-token tiles: 0 -> 14-16 spilled VGPRs), so they keep the default layout.
+  // 120.4 us); the identity and GELU kernels of that family 1-2 % slower, FP4
+  // QK-RMSNorm head_dim 128 0.4 % slower (93.4 -> 93.8 us), and in the other kernels
+  // the changed layout moves register allocation (QK-RMSNorm with 256-token tiles:
+  // 0 -> 14-16 spilled VGPRs), so they keep the default layout.
   static constexpr bool COLD_WRAP = FB_ == 3 && EPI == EPI_GATED_SILU;
   static constexpr int UNIT_LOADS = TND * FRAG_LOADS;
   // k-steps per unrolled group: whole turns of the weight ring (and, with three fragment
