@@ -28,15 +28,17 @@ def ditq():
     return bit_gemm_dit_amd
 
 
-@pytest.mark.parametrize("fmt,epi,M", [("fp4", "gated_silu", 300), ("nv4", "gated_silu", 200),
-                                       ("mx8", "gelu_tanh", 129), ("fp8", "identity", 257)])
-def test_captured_step_replays_equal_eager(ditq, fmt, epi, M):
+# K = 768 (6 k-steps) selects the FP4 kernels with three fragment buffers, K = 512 the others
+@pytest.mark.parametrize("fmt,epi,M,K", [("fp4", "gated_silu", 300, 512), ("fp4", "gated_silu", 300, 768),
+                                         ("nv4", "gated_silu", 200, 512), ("mx8", "gelu_tanh", 129, 512),
+                                         ("fp8", "identity", 257, 512)])
+def test_captured_step_replays_equal_eager(ditq, fmt, epi, M, K):
     import torch
     from tests.gpu_util import to_dev_bf16
     f, e = FMT[fmt], EPI[epi]
-    d0 = make_inputs("mlp_gated_silu", seed=1, M=M, N=1024, K=512)
-    d1 = make_inputs("mlp_gated_silu", seed=2, M=M, N=1024, K=512)
-    N, K = 1024, 512
+    N = 1024
+    d0 = make_inputs("mlp_gated_silu", seed=1, M=M, N=N, K=K)
+    d1 = make_inputs("mlp_gated_silu", seed=2, M=M, N=N, K=K)
     blob = ditq.pack_weights(to_dev_bf16(d0["w"]), f, e)
     x_static = to_dev_bf16(d0["x"]).clone()
     x_new = to_dev_bf16(d1["x"])
@@ -52,7 +54,7 @@ def test_captured_step_replays_equal_eager(ditq, fmt, epi, M):
     x_static.copy_(to_dev_bf16(d0["x"]))
     torch.cuda.synchronize()
 
-    print(f"graph capture {fmt} {epi} M={M}", flush=True)
+    print(f"graph capture {fmt} {epi} M={M} K={K}", flush=True)
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
