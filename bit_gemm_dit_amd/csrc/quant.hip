@@ -20,11 +20,42 @@
 // (include/ditq.h): the GEMM then copies each 64-byte-per-token panel slice of a
 // token tile as one contiguous run.
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 
 namespace ditq {
 namespace {
+
+// FP8 row quantizer, rows whose largest magnitude is at least 2^-60 (bf16 bits
+// 0x2180): x / s from one reciprocal per row and one correction, q0 = fl32(|x| * r)
+// with r = fl32(1 / s), then q0 + (|x| - q0 s) r with the residual exact in an FMA,
+// the sign restored from x.  An exhaustive check over every bf16 amax >= 2^-60 and
+// every bf16 x with |x| <= amax (tests/csrc/fp8_row_division_check.c) finds it equal to
+// the IEEE quotient fl32(x / s) bit for bit wherever |x / s| >= 2^-10, and below that
+// of magnitude <= 2^-10 with the sign of x, so both round to the same signed E4M3 zero:
+// the codes are those of the IEEE division.  Rows with a smaller maximum keep the IEEE
+// division (the residual could fall below fp32's normal range).  Four VALU operations
+// per element instead of the division's sequence.
+constexpr uint32_t kFp8RcpAmaxMin = 0x2180u;
+__device__ inline float fp8_quotient_rcp(float x, float s, float r) {
+  const float ax = __builtin_fabsf(x);
+  const float q0 = ax * r;
+  return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, ax), r, q0), x);
+}
+// fp8_encode4 with the quotient above: four bf16 values -> four E4M3 codes (byte i =
+// element i), the same clamp and conversion.
+__device__ inline uint32_t fp8_encode4_rcp(uint32_t w0, uint32_t w1, float s, float r) {
+  float a = fp8_quotient_rcp(bf16_lo(w0), s, r), b = fp8_quotient_rcp(bf16_hi(w0), s, r);
+  float c = fp8_quotient_rcp(bf16_lo(w1), s, r), d = fp8_quotient_rcp(bf16_hi(w1), s, r);
+  a = fmaxf(fminf(a, 448.0f), -448.0f);
+  b = fmaxf(fminf(b, 448.0f), -448.0f);
+  c = fmaxf(fminf(c, 448.0f), -448.0f);
+  d = fmaxf(fminf(d, 448.0f), -448.0f);
+  int q = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  q = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, q, true);
+  return (uint32_t)q;
+}
 
 // DPP quad permutations: xor 1 = [1,0,3,2], xor 2 = [2,3,0,1].
 constexpr int kQuadXor1 = 0xB1;
@@ -192,30 +223,36 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
   for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
   const float s = fp8_row_scale(m);
   if (lane == 0) scales[row] = s;
-  if (CACHED) {
+  const float r = 1.0f / s;
+  auto encode_row = [&](auto rcp_c) __attribute__((always_inline)) {
+    constexpr bool RCP = decltype(rcp_c)::value;
+    auto enc = [&](const v4i& v) __attribute__((always_inline)) {
+      uint2 q;
+      if constexpr (RCP) {
+        q.x = fp8_encode4_rcp((uint32_t)v.x, (uint32_t)v.y, s, r);
+        q.y = fp8_encode4_rcp((uint32_t)v.z, (uint32_t)v.w, s, r);
+      } else {
+        q.x = fp8_encode4((uint32_t)v.x, (uint32_t)v.y, s);
+        q.y = fp8_encode4((uint32_t)v.z, (uint32_t)v.w, s);
+      }
+      return q;
+    };
+    if (CACHED) {
 #pragma unroll
-    for (int i = 0; i < kMaxCached; ++i) {
-      const int k = i * 512 + lane * 8;
-      if (i < nch && k < K) {
-        const v4i v = cache[i];
-        uint2 q;
-        q.x = fp8_encode4((uint32_t)v.x, (uint32_t)v.y, s);
-        q.y = fp8_encode4((uint32_t)v.z, (uint32_t)v.w, s);
-        *reinterpret_cast<uint2*>(dst(k)) = q;
+      for (int i = 0; i < kMaxCached; ++i) {
+        const int k = i * 512 + lane * 8;
+        if (i < nch && k < K) *reinterpret_cast<uint2*>(dst(k)) = enc(cache[i]);
+      }
+    } else {
+      for (int i = 0; i < nch; ++i) {
+        const int k = i * 512 + lane * 8;
+        if (k < K) *reinterpret_cast<uint2*>(dst(k)) = enc(*reinterpret_cast<const v4i*>(xr + k));
       }
     }
-  } else {
-    for (int i = 0; i < nch; ++i) {
-      const int k = i * 512 + lane * 8;
-      if (k < K) {
-        const v4i v = *reinterpret_cast<const v4i*>(xr + k);
-        uint2 q;
-        q.x = fp8_encode4((uint32_t)v.x, (uint32_t)v.y, s);
-        q.y = fp8_encode4((uint32_t)v.z, (uint32_t)v.w, s);
-        *reinterpret_cast<uint2*>(dst(k)) = q;
-      }
-    }
-  }
+  };
+  // m is the row's maximum in every lane, so the choice is uniform over the wave
+  if (m >= kFp8RcpAmaxMin) encode_row(std::true_type{});
+  else encode_row(std::false_type{});
 }
 
 }  // namespace
