@@ -152,9 +152,25 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
   __shared__ uint32_t wave_max[4];
   uint32_t m = 0;
   const uint32_t stride = gridDim.x * 256u;
-  for (uint32_t c = blockIdx.x * 256u + threadIdx.x; c < total; c += stride) {
-    const uint32_t row = c / per_row, col = c - row * per_row;
-    m = max(m, absmax8(*reinterpret_cast<const v4i*>(x + (size_t)row * ld + (size_t)col * 8)));
+  // eight loads in flight per thread and pass: same-box A/B of the whole NVFP4
+  // quantizer (this pass, the reduction, the quantizer) at 4608 x 3072, outputs
+  // identical: 19.77 us with one load per pass, 18.85 with four, 18.66 with eight.
+  // (Moving the quantizer itself to 128-thread workgroups of 8 tokens, as for FP4 and
+  // MXFP8, measured no faster: its per-element division dominates.)
+  constexpr int kU = 8;
+  for (uint32_t c = blockIdx.x * 256u + threadIdx.x; c < total; c += kU * stride) {
+    v4i v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t cc = c + u * stride;
+      v[u] = v4i{0, 0, 0, 0};
+      if (cc < total) {
+        const uint32_t row = cc / per_row, col = cc - row * per_row;
+        v[u] = *reinterpret_cast<const v4i*>(x + (size_t)row * ld + (size_t)col * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) m = max(m, absmax8(v[u]));
   }
   m = block_max256(m, wave_max);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
