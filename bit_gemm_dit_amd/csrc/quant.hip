@@ -185,7 +185,8 @@ __global__ __launch_bounds__(256) void amax_final_kernel(const uint32_t* __restr
   if (threadIdx.x == 0) slot[0] = m;
 }
 
-// NVFP4: the FP4 kernel's structure; a block of 16 is one lane pair (DPP xor 1).
+// NVFP4: one lane per 8 elements as in the FP4 kernel, in a grid-stride loop over
+// 256-thread workgroups; a block of 16 is one lane pair (DPP xor 1).
 // Chunk `col` (8 elements) goes to the FP4 code position; its block (col/2) scale to
 // byte (col/2) % 8 of the token's 8-byte row of 128-element panel col/16.
 __global__ __launch_bounds__(256) void quant_nv4_kernel(const uint16_t* __restrict__ x, int M, int ldx,
