@@ -625,6 +625,41 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
         finish_tile<T>(p, v, tn, row, row < p.M, n0w, h);
       }
     }
+  } else if constexpr (T::FMT == FMT_FP8 && T::EPI == EPI_GATED_SILU) {
+    // gate/up result tile pair outer, like the identity / GELU path above.  Same-box
+    // A/B, outputs identical: CFG pair 305.4 -> 286.0 us, 4608 x 16384 x 3072
+    // 204.9 -> 193.3 us.
+    float sa[T::TM];
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm) {
+      const int row = m0w + 32 * tm + l32;
+      sa[tm] = reinterpret_cast<const float*>(p.a_scales)[row < p.M ? row : p.M - 1];
+    }
+#pragma unroll
+    for (int q = 0; q < T::TN / 2; ++q) {
+      __builtin_amdgcn_sched_barrier(0);
+      v4f sg[4], su[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float* ws = reinterpret_cast<const float*>(p.w_scales) + n0w + 64 * q + 8 * g + 4 * h;
+        sg[g] = *reinterpret_cast<const v4f*>(ws);
+        su[g] = *reinterpret_cast<const v4f*>(ws + 32);
+      }
+#pragma unroll
+      for (int tm = 0; tm < T::TM; ++tm) {
+        const int row = m0w + 32 * tm + l32;
+        float gate[16], up[16], v[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            gate[4 * g + i] = acc[2 * q][tm][4 * g + i] * (sa[tm] * sg[g][i]);
+            up[4 * g + i] = acc[2 * q + 1][tm][4 * g + i] * (sa[tm] * su[g][i]);
+          }
+        silu_mul16(gate, up, v);
+        store_tile<T>(p, row, row < p.M, n0w / 2 + 32 * q, p.N / 2, h, v);
+      }
+    }
   } else if constexpr (T::EPI != EPI_QK_RMSNORM) {
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) {
@@ -695,19 +730,6 @@ __device__ __forceinline__ void epilogue(const Params& p, v16f (&acc)[T::TN][T::
           for (int r = 0; r < 16; ++r) {
             gate[r] = acc[2 * q][tm][r];
             up[r] = acc[2 * q + 1][tm][r];
-          }
-          if constexpr (T::FMT == FMT_FP8) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const float* ws = reinterpret_cast<const float*>(p.w_scales) + n0w + 64 * q + 8 * g + 4 * h;
-              const v4f sg = *reinterpret_cast<const v4f*>(ws);
-              const v4f su = *reinterpret_cast<const v4f*>(ws + 32);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                gate[4 * g + i] *= sa * sg[i];
-                up[4 * g + i] *= sa * su[i];
-              }
-            }
           }
           silu_mul16(gate, up, v);
           store_tile<T>(p, row, ok, n0w / 2 + 32 * q, p.N / 2, h, v);
